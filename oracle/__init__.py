@@ -1,0 +1,210 @@
+"""CPU oracle for MoE routing, dispatch and combine (ctypes over plain C).
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU
+baseline leg of the benchmark may import this package.  The product path
+(the HIP library and its Python binding) never imports, loads or calls it,
+and the two share no code.
+
+Every function here only marshals numpy arrays into ``moe_oracle.c``, where
+the definitions live (each cites the page passage it follows).  The arrays
+use the same layouts as the HIP path:
+
+* logits float32 [T, E]; idx int32 [T, k]; w float32 [T, k]
+* counts int32 [E]; token_slot int32 [T, k] (e*C + r or -1); recv_src int32 [E*C]
+* x, y bf16 carried as uint16 bit patterns
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libmoe_oracle.so")
+_CFLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-fPIC", "-shared", "-std=c11"]
+
+_lib = None
+
+BF16 = 0
+FP8_E4M3 = 1
+
+
+def build(force: bool = True) -> str:
+    """Compile moe_oracle.c with gcc into libmoe_oracle.so next to it."""
+    global _lib
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.run(["gcc", *_CFLAGS, "-o", tmp, _SRC, "-lm"], check=True)
+        os.replace(tmp, _LIB_PATH)
+        _lib = None
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build(force=True)
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    i32, i64 = ctypes.c_int32, ctypes.c_int64
+    lib.oracle_route_topk.argtypes = [P, i64, i32, i32, P, P]
+    lib.oracle_route_topk.restype = ctypes.c_int
+    lib.oracle_assign_slots.argtypes = [P, i64, i32, i32, i32, P, P, P]
+    lib.oracle_assign_slots.restype = ctypes.c_int
+    lib.oracle_quantize_row_fp8.argtypes = [P, i32, P, P]
+    lib.oracle_quantize_row_fp8.restype = ctypes.c_int
+    lib.oracle_filled_rows.argtypes = [P, i32, i32]
+    lib.oracle_filled_rows.restype = i64
+    lib.oracle_pack.argtypes = [P, i64, i32, i32, P, P, i32, i32, P, P, P]
+    lib.oracle_pack.restype = ctypes.c_int
+    lib.oracle_combine.argtypes = [P, P, P, i64, i32, i32, P, P]
+    lib.oracle_combine.restype = ctypes.c_int
+    lib.oracle_bf16_round.argtypes = [ctypes.c_float]
+    lib.oracle_bf16_round.restype = ctypes.c_uint16
+    lib.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+    lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+    lib.oracle_row_bytes.argtypes = [i32, i32]
+    lib.oracle_row_bytes.restype = i64
+    lib.oracle_fixed_slot_bytes.argtypes = [i64, i64, i32, i32, i32]
+    lib.oracle_fixed_slot_bytes.restype = i64
+    lib.oracle_bf16_round_n.argtypes = [P, i64, P]
+    lib.oracle_bf16_round_n.restype = None
+    lib.oracle_e4m3_encode_n.argtypes = [P, i64, P]
+    lib.oracle_e4m3_encode_n.restype = None
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray | None):
+    return None if a is None else a.ctypes.data
+
+
+def _c(a, dtype) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise ValueError(f"oracle {what} rejected its arguments (rc={rc})")
+
+
+def route_topk(logits: np.ndarray, k: int):
+    """Top-k experts per token (descending logit, ties to lower index) and
+    their full-softmax weights.  Returns (idx int32 [T,k], w float32 [T,k])."""
+    logits = _c(logits, np.float32)
+    T, E = logits.shape
+    idx = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float32)
+    _check(_load().oracle_route_topk(_ptr(logits), T, E, k, _ptr(idx), _ptr(w)), "route_topk")
+    return idx, w
+
+
+def assign_slots(idx: np.ndarray, E: int, capacity: int):
+    """Per-expert counts and fixed slots in ascending token order.
+    Returns (counts int32 [E], token_slot int32 [T,k], recv_src int32 [E*C])."""
+    idx = _c(idx, np.int32)
+    T, k = idx.shape
+    counts = np.empty(E, np.int32)
+    token_slot = np.empty((T, k), np.int32)
+    recv_src = np.empty(E * capacity, np.int32)
+    _check(_load().oracle_assign_slots(_ptr(idx), T, E, k, capacity, _ptr(counts),
+                                       _ptr(token_slot), _ptr(recv_src)), "assign_slots")
+    return counts, token_slot, recv_src
+
+
+def quantize_row_fp8(x_row_bits: np.ndarray):
+    """E4M3 codes (uint8 [H]) and per-128 scales (float32 [H/128]) of one bf16 row."""
+    x = _c(x_row_bits, np.uint16).reshape(-1)
+    H = x.shape[0]
+    codes = np.empty(H, np.uint8)
+    scales = np.empty(max(H // 128, 1), np.float32)
+    _check(_load().oracle_quantize_row_fp8(_ptr(x), H, _ptr(codes), _ptr(scales)), "quantize_row_fp8")
+    return codes, scales
+
+
+def pack(x_bits: np.ndarray, dtype: int, recv_src: np.ndarray, counts: np.ndarray, capacity: int):
+    """Contents of every filled slot in ascending slot order.
+    Returns (rows, scales or None, slot_of_row int32 [R]); rows are uint16 [R,H]
+    (bf16) or uint8 [R,H] (fp8 codes) and scales float32 [R, H/128]."""
+    x = _c(x_bits, np.uint16)
+    T, H = x.shape
+    counts = _c(counts, np.int32)
+    recv_src = _c(recv_src, np.int32)
+    E = counts.shape[0]
+    lib = _load()
+    R = int(lib.oracle_filled_rows(_ptr(counts), E, capacity))
+    slot_of_row = np.empty(R, np.int32)
+    if dtype == BF16:
+        rows = np.empty((R, H), np.uint16)
+        scales = None
+    else:
+        rows = np.empty((R, H), np.uint8)
+        scales = np.empty((R, H // 128), np.float32)
+    _check(lib.oracle_pack(_ptr(x), T, H, dtype, _ptr(recv_src), _ptr(counts), E, capacity,
+                           _ptr(rows), _ptr(scales), _ptr(slot_of_row)), "pack")
+    return rows, scales, slot_of_row
+
+
+def combine(y_pairs_bits: np.ndarray, token_slot: np.ndarray, w: np.ndarray, want_acc: bool = False):
+    """out[t] = bf16(sum_j w[t,j] * y_pairs[t*k+j]) with fp32 FMA in top-k
+    order, skipping j with token_slot < 0.  Returns out uint16 [T,H] (and the
+    float32 accumulators if want_acc)."""
+    token_slot = _c(token_slot, np.int32)
+    T, k = token_slot.shape
+    y = _c(y_pairs_bits, np.uint16).reshape(T * k, -1)
+    H = y.shape[1]
+    w = _c(w, np.float32).reshape(T, k)
+    out = np.empty((T, H), np.uint16)
+    acc = np.empty((T, H), np.float32) if want_acc else None
+    _check(_load().oracle_combine(_ptr(y), _ptr(token_slot), _ptr(w), T, k, H, _ptr(out), _ptr(acc)),
+           "combine")
+    return (out, acc) if want_acc else out
+
+
+def bf16_round(f: float) -> int:
+    return int(_load().oracle_bf16_round(float(f)))
+
+
+def bf16_round_array(a: np.ndarray) -> np.ndarray:
+    flat = _c(a, np.float32).reshape(-1)
+    out = np.empty(flat.size, np.uint16)
+    _load().oracle_bf16_round_n(_ptr(flat), flat.size, _ptr(out))
+    return out.reshape(np.shape(a))
+
+
+def e4m3_encode(f: float) -> int:
+    return int(_load().oracle_e4m3_encode(float(f)))
+
+
+def e4m3_encode_array(a: np.ndarray) -> np.ndarray:
+    flat = _c(a, np.float32).reshape(-1)
+    out = np.empty(flat.size, np.uint8)
+    _load().oracle_e4m3_encode_n(_ptr(flat), flat.size, _ptr(out))
+    return out.reshape(np.shape(a))
+
+
+def row_bytes(H: int, dtype: int) -> int:
+    return int(_load().oracle_row_bytes(H, dtype))
+
+
+def fixed_slot_bytes(experts: int, slots_per_expert: int, H: int, dtype: int, header_bytes: int = 0) -> int:
+    return int(_load().oracle_fixed_slot_bytes(experts, slots_per_expert, H, dtype, header_bytes))
+
+
+def run_pipeline(logits: np.ndarray, x_bits: np.ndarray, k: int, capacity: int, dtype: int,
+                 y_pairs_bits: np.ndarray | None = None):
+    """Route, assign slots, pack and (if y_pairs given) combine, all on the CPU."""
+    E = logits.shape[1]
+    idx, w = route_topk(logits, k)
+    counts, token_slot, recv_src = assign_slots(idx, E, capacity)
+    rows, scales, slot_of_row = pack(x_bits, dtype, recv_src, counts, capacity)
+    res = dict(idx=idx, w=w, counts=counts, token_slot=token_slot, recv_src=recv_src,
+               rows=rows, scales=scales, slot_of_row=slot_of_row)
+    if y_pairs_bits is not None:
+        res["out"] = combine(y_pairs_bits, token_slot, w)
+    return res
