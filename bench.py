@@ -1,0 +1,247 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE token routing/dispatch/combine path on one MI355X.
+
+One step = moe_route_topk + moe_dispatch + moe_combine, back to back on one
+stream, over one batch of seeded synthetic input already resident in HBM.
+W untimed warm-up steps, then exactly K timed steps between device
+synchronisations.  Prints one JSON line (stdout):
+
+  value     tokens/s of the whole job (one GPU)
+  config    the workload plus effective HBM GB/s and fraction of the 8 TB/s
+            peak, from the algorithmic byte model (each row read once and
+            written k times, unfilled slots not counted)
+  roofline  the dominant kernel (combine): algorithmic bytes per launch over
+            its mean launch time from HIP events recorded around each launch
+            in the timed region, against the 8 TB/s HBM peak
+  cpu_baseline  the CPU oracle (single-threaded, plain C) on a bounded
+            sample of the same workload
+
+Consecutive steps cycle through several copies of every buffer (inputs,
+outputs and the fixed-slot buffers) so that each step's data was last touched
+many steps earlier: the 256 MB last-level cache in front of HBM cannot serve
+a small workload's working set from a previous step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+METRIC = "dispatch+combine tokens/s and effective HBM GB/s (% of peak), 1 MI355X"
+HBM_PEAK_GBPS = 8000.0
+LLC_BYTES = 256 * 2 ** 20
+
+
+def algorithmic_bytes(w: W.Workload) -> dict:
+    """Bytes each step must move: every row read once and written k times."""
+    T, H, E, k = w.T, w.H, w.E, w.k
+    row = (H + H // 32) if w.fp8 else 2 * H
+    b = {
+        "route": T * E * 4 + T * k * 8,
+        "count_scan_slot": T * k * 12 + E * 4,
+        "pack": T * H * 2 + T * k * 4 + T * k * row,
+        "combine": T * k * 2 * H + T * k * 8 + T * H * 2,
+    }
+    b["total"] = sum(b.values())
+    return b
+
+
+def host_cpu() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w: W.Workload, seconds: float) -> dict:
+    """Time the CPU oracle (route, slots, pack, combine) on the first
+    min(T, 2048) tokens of the workload, repeated for ~`seconds`."""
+    import numpy as np
+    import oracle
+
+    ts = min(w.T, 2048)
+    ws = w.with_(T=ts, C=min(w.C, ts))
+    logits = W.make_logits(w)[:ts].numpy()
+    x = W.bits(W.make_x(w)[:ts])
+    y_pairs = W.bits(W.make_y_pairs(w, rows=ts * w.k))
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        idx, wt = oracle.route_topk(logits, ws.k)
+        counts, token_slot, recv_src = oracle.assign_slots(idx, ws.E, ws.C)
+        oracle.pack(x, oracle.FP8_E4M3 if w.fp8 else oracle.BF16, recv_src, counts, ws.C)
+        oracle.combine(y_pairs, token_slot, wt)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    tok_s = passes * ts / el
+    return {
+        "value": tok_s, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+        "sample": f"{passes} passes of route+slots+pack+combine over the first {ts} of {w.T} tokens "
+                  f"({w.name}), {el:.1f} s",
+        "gbps": algorithmic_bytes(ws)["total"] * passes / el / 1e9,
+        "host": f"{host_cpu()}, {os.cpu_count()} threads visible",
+    }
+
+
+class BufferSet:
+    """One complete copy of a step's inputs, outputs and fixed-slot buffers."""
+
+    def __init__(self, w: W.Workload, logits_cpu, x_cpu, dev, moe, torch):
+        self.logits = logits_cpu.to(dev)
+        self.x = x_cpu.to(dev)
+        self.idx = torch.empty(w.T, w.k, dtype=torch.int32, device=dev)
+        self.wt = torch.empty(w.T, w.k, dtype=torch.float32, device=dev)
+        self.bufs = moe.DispatchBuffers.allocate(w.T, w.H, w.E, w.k, w.C, w.fp8, dev)
+        self.y = torch.empty(w.E, w.C, w.H, dtype=torch.bfloat16, device=dev)
+        self.out = torch.empty(w.T, w.H, dtype=torch.bfloat16, device=dev)
+        self.step = moe.PreparedStep(self.logits, w.k, self.x, w.C, w.fp8, self.bufs, self.y, self.out,
+                                     self.idx, self.wt)
+
+    def fill_expert_outputs(self, w: W.Workload, torch, gen):
+        """Seeded N(0,1) bf16 expert outputs in the slots the dispatch filled."""
+        slots = self.bufs.token_slot.reshape(-1)
+        slots = slots[slots >= 0].to(torch.int64)
+        rows = torch.randn(slots.numel(), w.H, device=self.y.device, generator=gen, dtype=torch.float32)
+        self.y.view(-1, w.H).index_copy_(0, slots, rows.to(torch.bfloat16))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mixtral_prefill", choices=W.ORDER)
+    ap.add_argument("--rotate", type=int, default=0,
+                    help="buffer copies cycled through (0: enough that 2 GiB of step traffic separates reuses)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this path has no multi-GPU (sharded) mode; run with --gpus 1",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import combine_moe_route_amd as moe
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP device", file=sys.stderr)
+        return 1
+    moe.load()
+    dev = torch.device("cuda:0")
+    w = W.WORKLOADS[args.workload]
+    nbytes = algorithmic_bytes(w)
+    R = args.rotate or max(1, min(32, math.ceil(2 * 2 ** 30 / nbytes["total"])))
+
+    logits_cpu = W.make_logits(w)
+    x_cpu = W.make_x(w)
+    sets = [BufferSet(w, logits_cpu, x_cpu, dev, moe, torch) for _ in range(R)]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed * 16 + 3)
+    for s in sets:
+        s.step.route()
+        s.step.dispatch()
+        s.fill_expert_outputs(w, torch, gen)
+    torch.cuda.synchronize()
+
+    K, Wm = args.steps, args.warmup
+    for i in range(Wm):
+        st = sets[i % R].step
+        st.route()
+        st.dispatch()
+        st.combine()
+    c0 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    c1 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(K):
+        st = sets[(Wm + i) % R].step
+        st.route()
+        st.dispatch()
+        c0[i].record()
+        st.combine()
+        c1[i].record()
+    e1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    wall_ms = (t1 - t0) * 1e3 / K
+    event_ms = e0.elapsed_time(e1) / K
+    ms = max(wall_ms, event_ms)
+    combine_ms = sum(a.elapsed_time(b) for a, b in zip(c0, c1)) / K
+    gbps = nbytes["total"] / (ms * 1e-3) / 1e9
+    comb_gbps = nbytes["combine"] / (combine_ms * 1e-3) / 1e9
+
+    if args.copy_mib:
+        n = args.copy_mib * 2 ** 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty(n, dtype=torch.uint8, device=dev)
+        a.fill_(1)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    result = {
+        "metric": METRIC,
+        "value": w.T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "tokens": w.T, "hidden": w.H, "experts": w.E, "top_k": w.k, "capacity": w.C,
+            "row_dtype": "fp8-e4m3+fp32/128" if w.fp8 else "bf16", "routing": w.routing,
+            "parallelism": "none (1 GPU)",
+            "algorithmic_bytes_per_step": nbytes["total"],
+            "effective_hbm_gbps": gbps,
+            "hbm_frac": gbps / HBM_PEAK_GBPS,
+            "buffer_copies_cycled": R,
+            "ms_per_step_wall": wall_ms, "ms_per_step_events": event_ms,
+        },
+        "roofline": {
+            "kernel": f"combine_kernel<{w.k}>",
+            "bound": "hbm",
+            "achieved": comb_gbps,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": comb_gbps / HBM_PEAK_GBPS,
+            "traffic": None,
+            "algorithmic_bytes_per_launch": nbytes["combine"],
+            "mean_launch_us": combine_ms * 1e3,
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

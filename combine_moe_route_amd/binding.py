@@ -1,0 +1,226 @@
+"""Thin ctypes binding of libmoe_route.so.
+
+Argument marshalling only: every function checks tensor dtypes, shapes and
+devices, allocates outputs with ``torch.empty`` when none are given, and
+calls the C entry point of the same name on the caller's current HIP stream.
+All computation happens in the library's HIP kernels; there is no fallback.
+The C contracts (layouts, tie rules, error codes) are documented in
+include/moe_route.h.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+from .build import LIB_PATH
+
+MOE_OK = 0
+MOE_ERR_INVALID = -1
+MOE_ERR_UNSUPPORTED = -2
+MOE_ERR_WORKSPACE = -3
+MOE_ERR_HIP = -4
+MOE_DTYPE_BF16 = 0
+MOE_DTYPE_FP8_E4M3 = 1
+MOE_MAX_EXPERTS = 1024
+MOE_MAX_TOPK = 16
+
+_lib = None
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {moe_status_string(status)} ({status})")
+        self.status = status
+
+
+def load() -> ctypes.CDLL:
+    """Load the in-tree HIP library; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with combine_moe_route_amd.build.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.moe_status_string.argtypes = [ctypes.c_int]
+    lib.moe_status_string.restype = ctypes.c_char_p
+    lib.moe_route_topk.argtypes = [P, i64, i32, i32, P, P, P]
+    lib.moe_route_topk.restype = ctypes.c_int
+    lib.moe_dispatch_workspace_bytes.argtypes = [i64, i32, i32]
+    lib.moe_dispatch_workspace_bytes.restype = ctypes.c_size_t
+    lib.moe_dispatch.argtypes = [P, i64, i32, P, i32, i32, i32, i32, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.moe_dispatch.restype = ctypes.c_int
+    lib.moe_combine.argtypes = [P, i32, i32, i32, P, P, i64, i32, P, P]
+    lib.moe_combine.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def moe_status_string(status: int) -> str:
+    return load().moe_status_string(int(status)).decode()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, dtype, shape, name: str):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a device tensor")
+
+
+def moe_route_topk(logits: torch.Tensor, k: int, topk_idx: torch.Tensor | None = None,
+                   topk_w: torch.Tensor | None = None, stream=None):
+    """Top-k experts (int32 [T,k]) and softmax weights (float32 [T,k])."""
+    T, E = logits.shape
+    _need(logits, torch.float32, (T, E), "logits")
+    if topk_idx is None:
+        topk_idx = torch.empty(T, k, dtype=torch.int32, device=logits.device)
+    if topk_w is None:
+        topk_w = torch.empty(T, k, dtype=torch.float32, device=logits.device)
+    _need(topk_idx, torch.int32, (T, k), "topk_idx")
+    _need(topk_w, torch.float32, (T, k), "topk_w")
+    rc = load().moe_route_topk(_ptr(logits), T, E, k, _ptr(topk_idx), _ptr(topk_w), _stream(stream))
+    if rc != MOE_OK:
+        raise MoeError("moe_route_topk", rc)
+    return topk_idx, topk_w
+
+
+def moe_dispatch_workspace_bytes(T: int, E: int, k: int) -> int:
+    return int(load().moe_dispatch_workspace_bytes(T, E, k))
+
+
+@dataclass
+class DispatchBuffers:
+    """Outputs of moe_dispatch (all device tensors)."""
+    recv_x: torch.Tensor          # bf16 [E, C, H] or uint8 [E, C, H] (E4M3 codes)
+    recv_scales: torch.Tensor | None  # float32 [E, C, H/128] for fp8
+    recv_src: torch.Tensor        # int32 [E, C]
+    expert_counts: torch.Tensor   # int32 [E]
+    token_slot: torch.Tensor      # int32 [T, k]
+    workspace: torch.Tensor       # uint8 scratch
+
+    @staticmethod
+    def allocate(T: int, H: int, E: int, k: int, capacity: int, fp8: bool, device) -> "DispatchBuffers":
+        if fp8:
+            recv_x = torch.empty(E, capacity, H, dtype=torch.uint8, device=device)
+            recv_scales = torch.empty(E, capacity, H // 128, dtype=torch.float32, device=device)
+        else:
+            recv_x = torch.empty(E, capacity, H, dtype=torch.bfloat16, device=device)
+            recv_scales = None
+        ws = moe_dispatch_workspace_bytes(T, E, k)
+        return DispatchBuffers(
+            recv_x=recv_x, recv_scales=recv_scales,
+            recv_src=torch.empty(E, capacity, dtype=torch.int32, device=device),
+            expert_counts=torch.empty(E, dtype=torch.int32, device=device),
+            token_slot=torch.empty(T, k, dtype=torch.int32, device=device),
+            workspace=torch.empty(max(ws, 256), dtype=torch.uint8, device=device),
+        )
+
+
+def moe_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: int, capacity: int, fp8: bool = False,
+                 bufs: DispatchBuffers | None = None, stream=None) -> DispatchBuffers:
+    """Counts, fixed slots (ascending token order) and packed rows."""
+    T, H = x.shape
+    k = topk_idx.shape[1]
+    E = num_experts
+    _need(x, torch.bfloat16, (T, H), "x")
+    _need(topk_idx, torch.int32, (T, k), "topk_idx")
+    if bufs is None:
+        bufs = DispatchBuffers.allocate(T, H, E, k, capacity, fp8, x.device)
+    _need(bufs.recv_x, torch.uint8 if fp8 else torch.bfloat16, (E, capacity, H), "recv_x")
+    if fp8:
+        _need(bufs.recv_scales, torch.float32, (E, capacity, H // 128), "recv_scales")
+    _need(bufs.recv_src, torch.int32, (E, capacity), "recv_src")
+    _need(bufs.expert_counts, torch.int32, (E,), "expert_counts")
+    _need(bufs.token_slot, torch.int32, (T, k), "token_slot")
+    rc = load().moe_dispatch(
+        _ptr(x), T, H, _ptr(topk_idx), E, k, capacity, MOE_DTYPE_FP8_E4M3 if fp8 else MOE_DTYPE_BF16,
+        _ptr(bufs.recv_x), _ptr(bufs.recv_scales) if fp8 else None, _ptr(bufs.recv_src),
+        _ptr(bufs.expert_counts), _ptr(bufs.token_slot), _ptr(bufs.workspace), bufs.workspace.numel(),
+        _stream(stream))
+    if rc != MOE_OK:
+        raise MoeError("moe_dispatch", rc)
+    return bufs
+
+
+def moe_combine(y: torch.Tensor, token_slot: torch.Tensor, topk_w: torch.Tensor, out: torch.Tensor | None = None,
+                stream=None) -> torch.Tensor:
+    """out[t] = bf16(sum_j w[t,j] * y[token_slot[t,j]]), fp32 FMA in top-k order."""
+    E, C, H = y.shape
+    T, k = token_slot.shape
+    _need(y, torch.bfloat16, (E, C, H), "y")
+    _need(token_slot, torch.int32, (T, k), "token_slot")
+    _need(topk_w, torch.float32, (T, k), "topk_w")
+    if out is None:
+        out = torch.empty(T, H, dtype=torch.bfloat16, device=y.device)
+    _need(out, torch.bfloat16, (T, H), "out")
+    rc = load().moe_combine(_ptr(y), E, C, H, _ptr(token_slot), _ptr(topk_w), T, k, _ptr(out), _stream(stream))
+    if rc != MOE_OK:
+        raise MoeError("moe_combine", rc)
+    return out
+
+
+class PreparedStep:
+    """Route, dispatch and combine with their arguments marshalled once.
+
+    For callers that repeat the same three calls on the same buffers (a
+    layer's fixed, reused buffers, or a benchmark loop): each call is then a
+    bare C ABI call with pre-computed pointers, so host overhead stays far
+    below the kernels' run time.  The tensors must stay alive and keep their
+    shapes while the object is used."""
+
+    def __init__(self, logits: torch.Tensor, k: int, x: torch.Tensor, capacity: int, fp8: bool,
+                 bufs: DispatchBuffers, y: torch.Tensor, out: torch.Tensor, topk_idx: torch.Tensor,
+                 topk_w: torch.Tensor, stream=None):
+        T, E = logits.shape
+        H = x.shape[1]
+        _need(logits, torch.float32, (T, E), "logits")
+        _need(x, torch.bfloat16, (T, H), "x")
+        _need(topk_idx, torch.int32, (T, k), "topk_idx")
+        _need(topk_w, torch.float32, (T, k), "topk_w")
+        _need(bufs.recv_x, torch.uint8 if fp8 else torch.bfloat16, (E, capacity, H), "recv_x")
+        _need(bufs.token_slot, torch.int32, (T, k), "token_slot")
+        _need(y, torch.bfloat16, (E, capacity, H), "y")
+        _need(out, torch.bfloat16, (T, H), "out")
+        self._lib = load()
+        s = _stream(stream)
+        self.route_args = (_ptr(logits), T, E, k, _ptr(topk_idx), _ptr(topk_w), s)
+        self.dispatch_args = (
+            _ptr(x), T, H, _ptr(topk_idx), E, k, capacity, MOE_DTYPE_FP8_E4M3 if fp8 else MOE_DTYPE_BF16,
+            _ptr(bufs.recv_x), _ptr(bufs.recv_scales) if fp8 else None, _ptr(bufs.recv_src),
+            _ptr(bufs.expert_counts), _ptr(bufs.token_slot), _ptr(bufs.workspace), bufs.workspace.numel(), s)
+        self.combine_args = (_ptr(y), E, capacity, H, _ptr(bufs.token_slot), _ptr(topk_w), T, k, _ptr(out), s)
+        self._keep = (logits, x, bufs, y, out, topk_idx, topk_w)
+
+    def route(self):
+        rc = self._lib.moe_route_topk(*self.route_args)
+        if rc != MOE_OK:
+            raise MoeError("moe_route_topk", rc)
+
+    def dispatch(self):
+        rc = self._lib.moe_dispatch(*self.dispatch_args)
+        if rc != MOE_OK:
+            raise MoeError("moe_dispatch", rc)
+
+    def combine(self):
+        rc = self._lib.moe_combine(*self.combine_args)
+        if rc != MOE_OK:
+            raise MoeError("moe_combine", rc)

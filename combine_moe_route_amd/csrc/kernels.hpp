@@ -1,0 +1,23 @@
+// kernels.hpp -- host launchers of the library's kernels (internal).
+// Arguments are validated by the C ABI layer before these are called.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+hipError_t launch_route_topk(const float *logits, int64_t T, int E, int k, int32_t *idx, float *w,
+                             hipStream_t s);
+
+size_t dispatch_workspace_bytes(int64_t T, int E, int k);
+
+hipError_t launch_dispatch(const uint16_t *x, int64_t T, int H, const int32_t *topk_idx, int E, int k, int C,
+                           int dtype, void *recv_x, float *recv_scales, int32_t *recv_src,
+                           int32_t *expert_counts, int32_t *token_slot, void *workspace, hipStream_t s);
+
+hipError_t launch_combine(const uint16_t *y, int64_t nrows, int H, const int32_t *token_slot, const float *w,
+                          int64_t T, int k, uint16_t *out, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,125 @@
+// moe_api.cpp -- the C ABI of libmoe_route.so: argument checks, then the
+// kernel launches.  The operations and their contracts are documented in
+// include/moe_route.h.
+#include "moe_route.h"
+
+#include <limits.h>
+
+#include "kernels.hpp"
+
+namespace {
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+int from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// Shared checks of E and k.
+int check_ek(int32_t E, int32_t k)
+{
+    if (E < 1 || k < 1 || k > E)
+        return MOE_ERR_INVALID;
+    if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK)
+        return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+MOE_API const char *moe_status_string(int status)
+{
+    switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported size";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+    }
+}
+
+MOE_API int moe_route_topk(const float *logits, int64_t T, int32_t E, int32_t k, int32_t *topk_idx,
+                           float *topk_w, hipStream_t stream)
+{
+    if (T < 0)
+        return MOE_ERR_INVALID;
+    int rc = check_ek(E, k);
+    if (rc != MOE_OK)
+        return rc;
+    if (T == 0)
+        return MOE_OK;
+    if (!logits || !topk_idx || !topk_w)
+        return MOE_ERR_INVALID;
+    if (!aligned(logits, 4) || !aligned(topk_idx, 4) || !aligned(topk_w, 4))
+        return MOE_ERR_INVALID;
+    if (T > MOE_MAX_TOKENS)
+        return MOE_ERR_UNSUPPORTED;
+    (void)hipGetLastError();
+    return from_hip(moe::launch_route_topk(logits, T, E, k, topk_idx, topk_w, stream));
+}
+
+MOE_API size_t moe_dispatch_workspace_bytes(int64_t T, int32_t E, int32_t k)
+{
+    if (T < 0 || E < 1 || k < 1 || E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK)
+        return 0;
+    return moe::dispatch_workspace_bytes(T, E, k);
+}
+
+MOE_API int moe_dispatch(const uint16_t *x, int64_t T, int32_t H, const int32_t *topk_idx, int32_t E, int32_t k,
+                         int32_t capacity, int32_t out_dtype, void *recv_x, float *recv_scales,
+                         int32_t *recv_src, int32_t *expert_counts, int32_t *token_slot, void *workspace,
+                         size_t workspace_bytes, hipStream_t stream)
+{
+    if (T < 0 || H < 1 || capacity < 1)
+        return MOE_ERR_INVALID;
+    int rc = check_ek(E, k);
+    if (rc != MOE_OK)
+        return rc;
+    if (out_dtype != MOE_DTYPE_BF16 && out_dtype != MOE_DTYPE_FP8_E4M3)
+        return MOE_ERR_INVALID;
+    if (H % 8 != 0 || (out_dtype == MOE_DTYPE_FP8_E4M3 && H % 128 != 0))
+        return MOE_ERR_UNSUPPORTED;
+    if ((int64_t)E * capacity > INT32_MAX || T > MOE_MAX_TOKENS)
+        return MOE_ERR_UNSUPPORTED;
+    if (!expert_counts || !aligned(expert_counts, 4))
+        return MOE_ERR_INVALID;
+    if (T > 0) {
+        if (!x || !topk_idx || !recv_x || !recv_src || !token_slot)
+            return MOE_ERR_INVALID;
+        if (!aligned(x, 16) || !aligned(recv_x, 16) || !aligned(topk_idx, 4) || !aligned(recv_src, 4) ||
+            !aligned(token_slot, 4))
+            return MOE_ERR_INVALID;
+        if (out_dtype == MOE_DTYPE_FP8_E4M3 && (!recv_scales || !aligned(recv_scales, 4)))
+            return MOE_ERR_INVALID;
+    }
+    if (out_dtype == MOE_DTYPE_BF16 && recv_scales)
+        return MOE_ERR_INVALID;
+    const size_t need = moe::dispatch_workspace_bytes(T, E, k);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+        return MOE_ERR_WORKSPACE;
+    (void)hipGetLastError();
+    return from_hip(moe::launch_dispatch(x, T, H, topk_idx, E, k, capacity, out_dtype, recv_x, recv_scales,
+                                         recv_src, expert_counts, token_slot, workspace, stream));
+}
+
+MOE_API int moe_combine(const uint16_t *y, int32_t E, int32_t capacity, int32_t H, const int32_t *token_slot,
+                        const float *topk_w, int64_t T, int32_t k, uint16_t *out, hipStream_t stream)
+{
+    if (T < 0 || H < 1 || capacity < 1 || E < 1 || k < 1)
+        return MOE_ERR_INVALID;
+    if (k > MOE_MAX_TOPK || H % 8 != 0)
+        return MOE_ERR_UNSUPPORTED;
+    if ((int64_t)E * capacity > INT32_MAX || T > MOE_MAX_TOKENS)
+        return MOE_ERR_UNSUPPORTED;
+    if (T == 0)
+        return MOE_OK;
+    if (!y || !token_slot || !topk_w || !out)
+        return MOE_ERR_INVALID;
+    if (!aligned(y, 16) || !aligned(out, 16) || !aligned(token_slot, 4) || !aligned(topk_w, 4))
+        return MOE_ERR_INVALID;
+    (void)hipGetLastError();
+    return from_hip(moe::launch_combine(y, (int64_t)E * capacity, H, token_slot, topk_w, T, k, out, stream));
+}
+
+}  // extern "C"

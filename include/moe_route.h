@@ -1,0 +1,182 @@
+/*
+ * moe_route.h -- C ABI of libmoe_route.so: Mixture-of-Experts token routing,
+ * dispatch and combine on one AMD Instinct MI355X (gfx950).
+ *
+ * The three operations are those of an expert-parallel MoE layer, as the
+ * following pages describe them:
+ *   - Perplexity, "Efficient and portable mixture-of-experts communication"
+ *     (pplx-kernels blog): Introduction (router, top-K, weighted sum),
+ *     Portable kernels (fixed per-source buffers, reused across layers),
+ *     Dispatch (pack tokens into contiguous per-expert buffers for the
+ *     grouped GEMM, keep each token's source index), Combine (weighted sum
+ *     of 16-bit expert outputs into a caller-allocated tensor).
+ *   - "How GPUs Talk to Each Other During LLM Inference", section 7 (Expert
+ *     Parallelism): dispatch groups tokens by expert; combine weights each
+ *     expert output by the router's score and adds the k outputs.
+ *   - AI-infra handbook, "NVSHMEM and DeepEP": "Why MoE's all-to-all is
+ *     hard" (route, sort by destination, count, dispatch, combine),
+ *     "High-throughput mode" (FP8 dispatch with one scale per 128 elements,
+ *     BF16 combine), "Low-latency mode" (fixed slots per expert, no host
+ *     synchronisation, graph-capturable; too few slots is an error).
+ *
+ * Conventions for every entry point
+ *   - Pointers marked (device) are HIP device pointers; the caller allocates
+ *     and owns every buffer.  The library allocates nothing on these paths
+ *     and keeps no state between calls.
+ *   - All work is enqueued on `stream` (NULL = the default stream) and the
+ *     call returns without waiting: no device synchronisation and no
+ *     device-to-host copy, so calls can be captured in a HIP graph.
+ *   - Arguments are checked on the host before anything is enqueued.  The
+ *     return value is MOE_OK or a negative MOE_ERR_* code; on error nothing
+ *     was enqueued.  MOE_ERR_HIP reports a failed kernel launch.
+ *   - Arrays are dense and row-major.  bf16 values are passed as their
+ *     16-bit patterns (uint16_t).  Buffers read or written in 16-byte
+ *     vectors (x, recv_x, y, out) must be 16-byte aligned.
+ *   - Results are deterministic: the same inputs give the same bits on
+ *     every call, whatever the launch order of the work-groups.
+ */
+#ifndef MOE_ROUTE_H
+#define MOE_ROUTE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_API __attribute__((visibility("default")))
+
+/* Status codes. */
+#define MOE_OK 0
+#define MOE_ERR_INVALID (-1)      /* null pointer, negative size, k outside [1, E], misalignment */
+#define MOE_ERR_UNSUPPORTED (-2)  /* a size this library does not handle (limits below) */
+#define MOE_ERR_WORKSPACE (-3)    /* workspace missing or smaller than moe_dispatch_workspace_bytes() */
+#define MOE_ERR_HIP (-4)          /* a HIP launch failed */
+
+/* Dispatch row formats. */
+#define MOE_DTYPE_BF16 0          /* rows copied bit for bit, 2*H bytes */
+#define MOE_DTYPE_FP8_E4M3 1      /* OCP E4M3 codes (H bytes) + one fp32 scale per 128 elements */
+
+/* Limits. */
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_TOPK 16
+#define MOE_MAX_TOKENS (1 << 24)  /* T above this is MOE_ERR_UNSUPPORTED */
+
+/* Text for a status code (static storage, never NULL). */
+MOE_API const char *moe_status_string(int status);
+
+/*
+ * moe_route_topk -- router top-k selection and weights.
+ *
+ * pplx blog, Introduction: the router produces a probability distribution
+ * over experts, the top-K experts are chosen and their outputs are weighted
+ * by that distribution.  "How GPUs Talk", section 7: each output is weighted
+ * by the score the router gave its expert.
+ *
+ *   logits   (device, in)  float [T][E] router logits
+ *   T        tokens, 0 <= T <= MOE_MAX_TOKENS (T = 0 enqueues nothing)
+ *   E        experts, 1 <= E <= MOE_MAX_EXPERTS
+ *   k        experts per token, 1 <= k <= min(E, MOE_MAX_TOPK)
+ *   topk_idx (device, out) int32 [T][k]: the k experts with the largest
+ *            logits in descending order; equal logits are ordered by
+ *            ascending expert index, and -0.0 equals +0.0.  NaN logits are
+ *            outside the domain.
+ *   topk_w   (device, out) float [T][k]: softmax over all E logits of the
+ *            token, evaluated at topk_idx (not renormalised over the k):
+ *            exp(L[e] - max) / sum exp(L - max), computed in fp32.
+ *   stream   HIP stream
+ */
+MOE_API int moe_route_topk(const float *logits, int64_t T, int32_t E, int32_t k,
+                           int32_t *topk_idx, float *topk_w, hipStream_t stream);
+
+/*
+ * Bytes of device workspace moe_dispatch needs for T tokens and E experts
+ * (per-chunk expert histograms).  Host function; returns 0 for bad sizes.
+ */
+MOE_API size_t moe_dispatch_workspace_bytes(int64_t T, int32_t E, int32_t k);
+
+/*
+ * moe_dispatch -- per-expert counts, fixed-slot assignment and row packing.
+ *
+ * Handbook "Why MoE's all-to-all is hard": after routing, tokens are sorted
+ * by destination and counted per destination.  Handbook "Low-latency mode":
+ * every expert owns a fixed number of slots (`capacity`) so a token's write
+ * address is known without a host round trip.  pplx blog, Dispatch: tokens
+ * are laid out contiguously per expert for the grouped GEMM, and each
+ * token's source index is kept for combine.  Handbook "High-throughput
+ * mode": FP8 dispatch uses one scale per 128 elements.
+ *
+ *   x             (device, in)  bf16 [T][H] token activations, 16 B aligned
+ *   T             tokens, 0 <= T <= MOE_MAX_TOKENS (T = 0 still zeroes
+ *                 expert_counts)
+ *   H             hidden size; multiple of 8 (bf16) or of 128 (fp8)
+ *   topk_idx      (device, in)  int32 [T][k]; each row holds k distinct
+ *                 experts in [0, E).  An id outside [0, E) is dropped
+ *                 (token_slot -1, not counted).  Repeated ids in one row
+ *                 are outside the domain (memory-safe, result unspecified).
+ *   E, k          as for moe_route_topk
+ *   capacity      C, slots per expert, >= 1, with E*C <= INT32_MAX
+ *   out_dtype     MOE_DTYPE_BF16 or MOE_DTYPE_FP8_E4M3
+ *   recv_x        (device, out) [E][C][H] rows: bf16 (2H bytes each) or
+ *                 E4M3 codes (H bytes each); 16 B aligned.  Slot r of expert
+ *                 e holds the r-th token (in ascending token order) routed
+ *                 to e.  Unfilled slots are not written.
+ *   recv_scales   (device, out) float [E][C][H/128] for fp8 (amax/448 of
+ *                 each 128-element block, 1.0 for an all-zero block; codes
+ *                 are RNE(x / scale) saturated to +-448); NULL for bf16.
+ *   recv_src      (device, out) int32 [E][C]: source token of each filled
+ *                 slot; unfilled slots are not written.
+ *   expert_counts (device, out) int32 [E]: true number of tokens routed to
+ *                 each expert.  A value above C means overflow: the later
+ *                 tokens of that expert were dropped.  The handbook treats
+ *                 too few slots as a failure of the batch; here it is
+ *                 reported on the device, so no host synchronisation is
+ *                 needed, and the caller decides (fail, or split the batch).
+ *   token_slot    (device, out) int32 [T][k]: e*C + r, the recv_x row of
+ *                 (t, j), or -1 if dropped.  Combine reads it.
+ *   workspace     (device, scratch) at least moe_dispatch_workspace_bytes()
+ *                 bytes, 256 B aligned; contents need no initialisation and
+ *                 are undefined afterwards.
+ *   stream        HIP stream
+ * Buffers must not overlap.
+ */
+MOE_API int moe_dispatch(const uint16_t *x, int64_t T, int32_t H, const int32_t *topk_idx,
+                         int32_t E, int32_t k, int32_t capacity, int32_t out_dtype,
+                         void *recv_x, float *recv_scales, int32_t *recv_src,
+                         int32_t *expert_counts, int32_t *token_slot, void *workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_combine -- gather each token's k expert outputs and return their
+ * router-weighted sum in the original token order.
+ *
+ * pplx blog, Combine: the routing table gives, per expert, which buffer to
+ * read and which weight to apply; the weighted sum of the 16-bit expert
+ * outputs is written to a caller-allocated tensor.  "How GPUs Talk",
+ * section 7: the k weighted outputs are added at the token's origin.
+ *
+ *   y          (device, in)  bf16 [E][C][H] expert outputs, same row layout
+ *              as moe_dispatch's recv_x; 16 B aligned
+ *   E, capacity, H   as for moe_dispatch (H multiple of 8)
+ *   token_slot (device, in)  int32 [T][k] from moe_dispatch; entries < 0
+ *              or >= E*C are skipped
+ *   topk_w     (device, in)  float [T][k] router weights
+ *   T, k       tokens (0..MOE_MAX_TOKENS) and experts per token
+ *              (1..MOE_MAX_TOPK)
+ *   out        (device, out) bf16 [T][H]; out[t][h] = bf16 RNE of
+ *              acc, acc = +0 then acc = fma(w[t][j], y[slot(t,j)][h], acc)
+ *              for j = 0..k-1 in order.  Must not overlap y.
+ *   stream     HIP stream
+ */
+MOE_API int moe_combine(const uint16_t *y, int32_t E, int32_t capacity, int32_t H,
+                        const int32_t *token_slot, const float *topk_w, int64_t T, int32_t k,
+                        uint16_t *out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_ROUTE_H */

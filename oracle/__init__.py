@@ -72,6 +72,8 @@ def _load():
     lib.oracle_row_bytes.restype = i64
     lib.oracle_fixed_slot_bytes.argtypes = [i64, i64, i32, i32, i32]
     lib.oracle_fixed_slot_bytes.restype = i64
+    lib.oracle_quantize_rows_fp8.argtypes = [P, i64, i32, P, P]
+    lib.oracle_quantize_rows_fp8.restype = ctypes.c_int
     lib.oracle_bf16_round_n.argtypes = [P, i64, P]
     lib.oracle_bf16_round_n.restype = None
     lib.oracle_e4m3_encode_n.argtypes = [P, i64, P]
@@ -124,6 +126,17 @@ def quantize_row_fp8(x_row_bits: np.ndarray):
     codes = np.empty(H, np.uint8)
     scales = np.empty(max(H // 128, 1), np.float32)
     _check(_load().oracle_quantize_row_fp8(_ptr(x), H, _ptr(codes), _ptr(scales)), "quantize_row_fp8")
+    return codes, scales
+
+
+def quantize_rows_fp8(x_bits: np.ndarray):
+    """Row-wise quantize_row_fp8 of a bf16 matrix [n, H]: codes uint8 [n, H]
+    and scales float32 [n, H/128]."""
+    x = _c(x_bits, np.uint16)
+    n, H = x.shape
+    codes = np.empty((n, H), np.uint8)
+    scales = np.empty((n, max(H // 128, 1)), np.float32)
+    _check(_load().oracle_quantize_rows_fp8(_ptr(x), n, H, _ptr(codes), _ptr(scales)), "quantize_rows_fp8")
     return codes, scales
 
 

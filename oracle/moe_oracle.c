@@ -366,3 +366,14 @@ void oracle_e4m3_encode_n(const float *in, int64_t n, uint8_t *out)
     for (int64_t i = 0; i < n; ++i)
         out[i] = oracle_e4m3_encode(in[i]);
 }
+
+/* Quantise n rows of H elements, one oracle_quantize_row_fp8() per row. */
+int oracle_quantize_rows_fp8(const uint16_t *x, int64_t n, int32_t H, uint8_t *codes, float *scales)
+{
+    for (int64_t r = 0; r < n; ++r) {
+        int rc = oracle_quantize_row_fp8(x + r * H, H, codes + r * H, scales + r * (H / 128));
+        if (rc)
+            return rc;
+    }
+    return 0;
+}

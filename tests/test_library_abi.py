@@ -1,0 +1,92 @@
+"""The HIP library loads on any host, exports every entry point its header
+declares, rejects bad arguments on the host before touching a device, and
+links nothing from the oracle.  No kernel runs here (no GPU needed)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import combine_moe_route_amd as moe
+from combine_moe_route_amd.build import LIB_PATH
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = [os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h")]
+
+
+def _declared():
+    names = []
+    for h in HEADERS:
+        text = open(h).read()
+        names += re.findall(r"MOE_API\s+[\w\s\*]+?\b(moe_\w+)\s*\(", text)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB_PATH):
+        moe.build()
+    return moe.load()
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ("moe_route_topk", "moe_dispatch", "moe_combine", "moe_dispatch_workspace_bytes",
+              "moe_status_string"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\s[TW]\s+(\w+)$", out, re.M))
+    for n in _declared():
+        assert n in exported, n
+        assert hasattr(lib, n)
+    # nothing but the declared C ABI is exported under the moe_ prefix
+    assert {s for s in exported if s.startswith("moe_")} == set(_declared())
+
+
+def test_library_does_not_link_the_oracle():
+    out = subprocess.run(["ldd", LIB_PATH], capture_output=True, text=True).stdout
+    assert "oracle" not in out
+    syms = subprocess.run(["nm", "-D", LIB_PATH], capture_output=True, text=True).stdout
+    assert "oracle_" not in syms
+
+
+def test_status_strings(lib):
+    assert moe.moe_status_string(0) == "ok"
+    assert "workspace" in moe.moe_status_string(-3)
+    assert moe.moe_status_string(99) == "unknown status"
+
+
+def test_workspace_size(lib):
+    assert moe.moe_dispatch_workspace_bytes(32768, 128, 8) == 128 * 128 * 4 + 32768 * 8 * 4
+    assert moe.moe_dispatch_workspace_bytes(-1, 8, 2) == 0
+    assert moe.moe_dispatch_workspace_bytes(10, 2000, 2) == 0
+    assert moe.moe_dispatch_workspace_bytes(0, 8, 2) == 0
+
+
+def test_host_validation_without_device(lib):
+    # every call below fails its argument checks before any HIP call
+    P = None
+    assert lib.moe_route_topk(P, -1, 8, 2, P, P, P) == -1
+    assert lib.moe_route_topk(P, 4, 8, 0, P, P, P) == -1
+    assert lib.moe_route_topk(P, 4, 8, 9, P, P, P) == -1
+    assert lib.moe_route_topk(P, 4, 4096, 2, P, P, P) == -2
+    assert lib.moe_route_topk(P, 4, 64, 17, P, P, P) == -2
+    assert lib.moe_route_topk(P, 4, 8, 2, P, P, P) == -1          # null pointers
+    assert lib.moe_route_topk(P, 0, 8, 2, P, P, P) == 0           # empty: nothing to do
+    assert lib.moe_combine(P, 8, 4, 64, P, P, -1, 2, P, P) == -1
+    assert lib.moe_combine(P, 8, 4, 60, P, P, 4, 2, P, P) == -2
+    assert lib.moe_combine(P, 8, 4, 64, P, P, 4, 17, P, P) == -2
+    assert lib.moe_combine(P, 8, 4, 64, P, P, 0, 2, P, P) == 0
+    assert lib.moe_combine(P, 8, 4, 64, P, P, 4, 2, P, P) == -1
+    assert lib.moe_combine(P, 65536, 65536, 64, P, P, 4, 2, P, P) == -2   # E*C beyond int32
+    d = lib.moe_dispatch
+    assert d(P, 4, 64, P, 8, 2, 4, 0, P, P, P, P, P, P, 0, P) == -1     # null pointers
+    assert d(P, 4, 64, P, 8, 2, 4, 2, P, P, P, P, P, P, 0, P) == -1     # bad dtype
+    assert d(P, 4, 64, P, 8, 2, 0, 0, P, P, P, P, P, P, 0, P) == -1     # capacity 0
+    assert d(P, 4, 100, P, 8, 2, 4, 0, P, P, P, P, P, P, 0, P) == -2    # H % 8
+    assert d(P, 4, 192, P, 8, 2, 4, 1, P, P, P, P, P, P, 0, P) == -2    # fp8 needs H % 128
+    assert d(P, 4, 64, P, 8, 9, 4, 0, P, P, P, P, P, P, 0, P) == -1     # k > E
