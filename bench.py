@@ -55,6 +55,37 @@ def algorithmic_bytes(w: W.Workload) -> dict:
     return b
 
 
+def combine_source_hash() -> str:
+    """Hash of the combine kernel's sources, to tell whether a committed
+    counter measurement still describes the kernel that runs."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("combine.hip", "device_common.hpp"):
+        with open(os.path.join(ROOT, "combine_moe_route_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(w: W.Workload):
+    """HBM bytes per combine launch from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when there is
+    none for this workload or the kernel changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{w.name}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and line.startswith("combine-"):
+            key, val = line.split(":", 1)
+            fields[key.strip()] = val.strip()
+    if fields.get("combine-source-sha256-16") != combine_source_hash():
+        return None
+    try:
+        return int(fields["combine-traffic-bytes-per-launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def host_cpu() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -128,6 +159,12 @@ def main() -> int:
                     help="buffer copies cycled through (0: enough that 2 GiB of step traffic separates reuses)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--streams", type=int, default=1,
+                    help="HIP streams the timed steps alternate over (2: two independent batches in flight)")
+    ap.add_argument("--timing", choices=["ext", "marker"], default="ext",
+                    help="combine launch timing: events attached to the launch (ext) or recorded around it")
+    ap.add_argument("--no-overlap", action="store_true",
+                    help="skip the extra two-batches-in-flight measurement")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -163,33 +200,85 @@ def main() -> int:
     torch.cuda.synchronize()
 
     K, Wm = args.steps, args.warmup
-    for i in range(Wm):
-        st = sets[i % R].step
-        st.route()
-        st.dispatch()
-        st.combine()
-    c0 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    c1 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    S = max(1, args.streams)
+    main = torch.cuda.current_stream()
+    streams = [main] + [torch.cuda.Stream() for _ in range(max(S, 2) - 1)]
+    hip_events = moe.HipEvents()
+
+    def bind(nstreams):
+        """Bind buffer set i to stream i % nstreams (a set never changes stream
+        while steps are queued)."""
+        torch.cuda.synchronize()
+        for si, st in enumerate(sets):
+            st.step = moe.PreparedStep(st.logits, w.k, st.x, w.C, w.fp8, st.bufs, st.y, st.out, st.idx, st.wt,
+                                       stream=streams[si % nstreams])
+
+    def run_steps(first, n, nstreams, ev=None):
+        """n steps over buffer sets first, first+1, ...; when `ev` maps step
+        index -> (start, stop) raw events, those steps' combine launches are
+        timed."""
+        for i in range(n):
+            si = (first + i) % R
+            st = sets[si].step
+            st.route()
+            st.dispatch()
+            pair = ev.get(i) if ev else None
+            if pair is None:
+                st.combine()
+            elif args.timing == "ext":
+                st.combine_timed(*pair)
+            else:
+                hip_events.record(pair[0], streams[si % nstreams])
+                st.combine()
+                hip_events.record(pair[1], streams[si % nstreams])
+
+    def timed(first, n, nstreams, ev=None):
+        torch.cuda.synchronize()
+        for strm in streams[1:nstreams]:
+            strm.wait_stream(main)
+        t0 = time.perf_counter()
+        run_steps(first, n, nstreams, ev)
+        for strm in streams[1:nstreams]:
+            main.wait_stream(strm)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / n
+
+    # headline: S stream(s), combine timed per launch by its own kernel timestamps
+    if R % S:
+        R -= R % S
+    bind(S)
+    run_steps(0, Wm, S)
+    # every event pair is a pair of barrier packets in the stream (~3.5 us of
+    # lost pipelining each on this runtime), so only ~8 launches spread over
+    # the K timed steps carry them
+    every = max(1, K // 8)
+    ev = {i: (hip_events.create(), hip_events.create()) for i in range(every // 2, K, every)}
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record()
-    for i in range(K):
-        st = sets[(Wm + i) % R].step
-        st.route()
-        st.dispatch()
-        c0[i].record()
-        st.combine()
-        c1[i].record()
-    e1.record()
+    e0.record(main)
+    wall_ms = timed(Wm, K, S, ev)
+    e1.record(main)
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    event_ms = e0.elapsed_time(e1) / K     # includes the trailing sync gap; reported only
+    ms = wall_ms
+    combine_times = [hip_events.elapsed_ms(a, b) for a, b in ev.values()]
+    combine_ms = sum(combine_times) / len(combine_times)
+    for a, b in ev.values():
+        hip_events.destroy(a)
+        hip_events.destroy(b)
 
-    wall_ms = (t1 - t0) * 1e3 / K
-    event_ms = e0.elapsed_time(e1) / K
-    ms = max(wall_ms, event_ms)
-    combine_ms = sum(a.elapsed_time(b) for a, b in zip(c0, c1)) / K
+    # the same steps without timing events, for comparison
+    plain_ms = timed(Wm + K, K, S)
+
+    # two independent batches in flight (steps alternate over two streams)
+    overlap = None
+    if not args.no_overlap and S == 1 and R >= 2:
+        bind(2)
+        run_steps(0, Wm, 2)
+        ov_ms = timed(Wm, K, 2)
+        overlap = {"streams": 2, "ms_per_step": ov_ms, "tokens_per_s": w.T / (ov_ms * 1e-3),
+                   "hbm_frac": nbytes["total"] / (ov_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
     gbps = nbytes["total"] / (ms * 1e-3) / 1e9
     comb_gbps = nbytes["combine"] / (combine_ms * 1e-3) / 1e9
 
@@ -223,7 +312,10 @@ def main() -> int:
             "effective_hbm_gbps": gbps,
             "hbm_frac": gbps / HBM_PEAK_GBPS,
             "buffer_copies_cycled": R,
-            "ms_per_step_wall": wall_ms, "ms_per_step_events": event_ms,
+            "streams": S,
+            "ms_per_step_events": event_ms,
+            "ms_per_step_without_timing_events": plain_ms,
+            "two_batches_in_flight": overlap,
         },
         "roofline": {
             "kernel": f"combine_kernel<{w.k}>",
@@ -232,9 +324,15 @@ def main() -> int:
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": comb_gbps / HBM_PEAK_GBPS,
-            "traffic": None,
+            "traffic": measured_traffic(w),
+            "traffic_source": f"profiles/{w.name}_hbm_traffic.md (bytes per launch)",
             "algorithmic_bytes_per_launch": nbytes["combine"],
             "mean_launch_us": combine_ms * 1e3,
+            "timed_launches": len(combine_times),
+            "min_launch_us": min(combine_times) * 1e3,
+            "max_launch_us": max(combine_times) * 1e3,
+            "timing": ("device-release HIP events attached to each timed combine launch (moe_combine_timed)"
+                       if args.timing == "ext" else "device-release HIP events recorded around each timed combine"),
         },
     }
     if not args.no_cpu_baseline:

@@ -10,6 +10,7 @@ from .binding import (  # noqa: F401
     MOE_MAX_EXPERTS,
     MOE_MAX_TOPK,
     DispatchBuffers,
+    HipEvents,
     MoeError,
     PreparedStep,
     load,

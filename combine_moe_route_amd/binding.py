@@ -55,12 +55,61 @@ def load() -> ctypes.CDLL:
     lib.moe_dispatch.restype = ctypes.c_int
     lib.moe_combine.argtypes = [P, i32, i32, i32, P, P, i64, i32, P, P]
     lib.moe_combine.restype = ctypes.c_int
+    lib.moe_combine_timed.argtypes = [P, i32, i32, i32, P, P, i64, i32, P, P, P, P]
+    lib.moe_combine_timed.restype = ctypes.c_int
     _lib = lib
     return lib
 
 
 def moe_status_string(status: int) -> str:
     return load().moe_status_string(int(status)).decode()
+
+
+class HipEvents:
+    """Raw hipEvent_t handles from the HIP runtime this process already uses
+    (the one torch loaded), for moe_combine_timed."""
+
+    def __init__(self):
+        lib = None
+        for path in (os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"), "libamdhip64.so.7"):
+            try:
+                lib = ctypes.CDLL(path)
+                break
+            except OSError:
+                continue
+        if lib is None:
+            raise ImportError("libamdhip64 not found")
+        lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self._hip = lib
+
+    # device-scope release on record: no system-wide cache writeback per
+    # event, so timing events barely perturb the work they bracket
+    RELEASE_TO_DEVICE = 0x40000000
+
+    def create(self, flags: int = RELEASE_TO_DEVICE) -> int:
+        ev = ctypes.c_void_p()
+        if self._hip.hipEventCreateWithFlags(ctypes.byref(ev), flags) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        return ev.value
+
+    def record(self, ev: int, stream=None):
+        if self._hip.hipEventRecord(ev, _stream(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, start: int, stop: int) -> float:
+        if self._hip.hipEventSynchronize(stop) != 0:
+            raise RuntimeError("hipEventSynchronize failed")
+        ms = ctypes.c_float()
+        if self._hip.hipEventElapsedTime(ctypes.byref(ms), start, stop) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, ev: int):
+        self._hip.hipEventDestroy(ev)
 
 
 def _stream(stream) -> int | None:
@@ -162,8 +211,9 @@ def moe_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: int, capa
 
 
 def moe_combine(y: torch.Tensor, token_slot: torch.Tensor, topk_w: torch.Tensor, out: torch.Tensor | None = None,
-                stream=None) -> torch.Tensor:
-    """out[t] = bf16(sum_j w[t,j] * y[token_slot[t,j]]), fp32 FMA in top-k order."""
+                stream=None, events: tuple[int, int] | None = None) -> torch.Tensor:
+    """out[t] = bf16(sum_j w[t,j] * y[token_slot[t,j]]), fp32 FMA in top-k order.
+    `events` = (start, stop) raw hipEvent_t handles selects moe_combine_timed."""
     E, C, H = y.shape
     T, k = token_slot.shape
     _need(y, torch.bfloat16, (E, C, H), "y")
@@ -172,9 +222,13 @@ def moe_combine(y: torch.Tensor, token_slot: torch.Tensor, topk_w: torch.Tensor,
     if out is None:
         out = torch.empty(T, H, dtype=torch.bfloat16, device=y.device)
     _need(out, torch.bfloat16, (T, H), "out")
-    rc = load().moe_combine(_ptr(y), E, C, H, _ptr(token_slot), _ptr(topk_w), T, k, _ptr(out), _stream(stream))
+    args = (_ptr(y), E, C, H, _ptr(token_slot), _ptr(topk_w), T, k, _ptr(out), _stream(stream))
+    if events is None:
+        rc = load().moe_combine(*args)
+    else:
+        rc = load().moe_combine_timed(*args, events[0], events[1])
     if rc != MOE_OK:
-        raise MoeError("moe_combine", rc)
+        raise MoeError("moe_combine" if events is None else "moe_combine_timed", rc)
     return out
 
 
@@ -224,3 +278,9 @@ class PreparedStep:
         rc = self._lib.moe_combine(*self.combine_args)
         if rc != MOE_OK:
             raise MoeError("moe_combine", rc)
+
+    def combine_timed(self, start_event: int, stop_event: int):
+        """combine, with raw hipEvent_t handles recording its kernel's start and end."""
+        rc = self._lib.moe_combine_timed(*self.combine_args, start_event, stop_event)
+        if rc != MOE_OK:
+            raise MoeError("moe_combine_timed", rc)

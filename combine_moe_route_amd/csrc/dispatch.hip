@@ -12,17 +12,20 @@
 // Slot order inside an expert is ascending source token.  The rank of
 // (t, j) among the tokens routed to e is computed without order-dependent
 // atomics, so the result is deterministic:
-//   K1 count:  one work-group per chunk of 256 tokens builds, in LDS, a
-//              256-bit membership mask per expert (atomic OR, which commutes),
-//              then writes the chunk's per-expert histogram and each pair's
-//              rank inside the chunk (popcount of the mask below its bit).
-//   K2 scan:   one wave per expert turns the chunk histograms into exclusive
-//              per-chunk offsets (wave prefix sums) and the true total count.
-//   K3 pack:   one wave per (token, column segment) finishes the slot
-//              (offset + rank, dropped when >= capacity), records token_slot
-//              and recv_src, loads the row once in 16-byte vectors and stores
-//              it to each of its k slots -- bf16 bit copies, or E4M3 codes
-//              with per-128 fp32 scales.
+//   count:  one work-group per chunk of 256 tokens builds, in LDS, a 256-bit
+//           membership mask per expert (atomic OR, which commutes), then
+//           writes the chunk's per-expert histogram and each pair's rank
+//           inside the chunk (popcount of the mask below its bit).
+//   pack:   one wave per (token, row segment) requests all of its row
+//           vectors, and while they are in flight finishes the k slots:
+//           offset = sum of the expert's counts in earlier chunks (an
+//           exclusive prefix over a few L2-resident histogram words),
+//           slot = e*C + offset + rank, dropped when >= C.  Segment 0
+//           records token_slot and recv_src; then the row is stored to
+//           each slot -- bf16 bit copies, or E4M3 codes with per-128 fp32
+//           scales.  The first E waves also write the true totals.
+// Slot rows are written with non-temporal stores: each byte is written once
+// per call.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -78,70 +81,106 @@ __global__ __launch_bounds__(kBlock) void dispatch_count_kernel(const int32_t *_
     }
 }
 
-// chunk_counts[e][c] -> exclusive prefix over c (in place); total -> counts[e].
-__global__ __launch_bounds__(kBlock) void dispatch_scan_kernel(int32_t *__restrict__ chunk_counts, int E,
-                                                               int nchunks, int32_t *__restrict__ expert_counts)
+// T = 0: nothing routed, every count is zero.
+__global__ __launch_bounds__(kBlock) void dispatch_zero_counts_kernel(int32_t *__restrict__ expert_counts, int E)
 {
-    const int lane = lane_id();
-    const int e = uniform(blockIdx.x * kWavesPerBlock + (int)(threadIdx.x / kWave));
-    if (e >= E)
-        return;
-    int32_t *row = chunk_counts + (int64_t)e * nchunks;
-    int carry = 0;
-    for (int base = 0; base < nchunks; base += kWave) {
-        const int i = base + lane;
-        const int v = i < nchunks ? row[i] : 0;
-        int x = v;
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-            const int y = __shfl_up(x, o);
-            if (lane >= o)
-                x += y;
-        }
-        if (i < nchunks)
-            row[i] = carry + x - v;
-        carry += __shfl(x, kWave - 1);
-    }
-    if (lane == 0)
-        expert_counts[e] = carry;
+    for (int e = blockIdx.x * kBlock + threadIdx.x; e < E; e += gridDim.x * kBlock)
+        expert_counts[e] = 0;
 }
 
-// Slot of pair (t, lane) for lanes < k, else -1.  Wave 0 of a token's
-// segments also records token_slot and recv_src.
-__device__ __forceinline__ int finish_slot(const int32_t *__restrict__ topk_idx,
-                                           const int32_t *__restrict__ local_rank,
-                                           const int32_t *__restrict__ chunk_base, int64_t t, int E, int k,
-                                           int C, int nchunks, bool record, int32_t *__restrict__ token_slot,
-                                           int32_t *__restrict__ recv_src)
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Streaming stores: every slot byte is written once per call and not read
+// back by this call, so stores are non-temporal.  (Measured on MI355X: the
+// row loads are faster as ordinary loads, the stores as non-temporal ones.)
+__device__ __forceinline__ void store_stream(u32x4 *p, u32x4 v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void store_stream(float *p, float v) { __builtin_nontemporal_store(v, p); }
+
+// Slot of pair (t, j) for the lanes that own it, -1 elsewhere.  L =
+// lanes_per_pair lanes serve pair j = lane / L: they load the expert id and
+// in-chunk rank, and sum the expert's counts over all earlier 256-token
+// chunks (the exclusive prefix, read from the L2-resident chunk histograms
+// with up to 8 independent loads per lane in flight), then a butterfly
+// within the L lanes.  slot = e*C + prefix + rank, or -1 when that is >= C
+// or the id is out of range.  The value is valid in lane j*L.
+__device__ __forceinline__ int wave_slot(const int32_t *__restrict__ topk_idx, const int32_t *__restrict__ local_rank,
+                                         const int32_t *__restrict__ chunk_counts, int64_t t, int E, int k, int C,
+                                         int nchunks, int lanes_per_pair)
 {
     const int lane = lane_id();
-    int slot = -1;
-    if (lane < k) {
-        const int e = topk_idx[t * k + lane];
-        const int r = local_rank[t * k + lane];
-        if ((unsigned)e < (unsigned)E && r >= 0) {
-            const int64_t rr = (int64_t)chunk_base[(int64_t)e * nchunks + t / kChunk] + r;
-            if (rr < C)
-                slot = (int)((int64_t)e * C + rr);
-        }
-        if (record) {
-            token_slot[t * k + lane] = slot;
-            if (slot >= 0)
-                recv_src[slot] = (int32_t)t;
+    const int j = lane / lanes_per_pair;
+    const int sub = lane - j * lanes_per_pair;
+    const int c = (int)(t / kChunk);
+    int e = -1, r = -1, sum = 0;
+    if (j < k) {
+        e = topk_idx[t * k + j];
+        r = local_rank[t * k + j];
+        if ((unsigned)e < (unsigned)E) {
+            const int32_t *row = chunk_counts + (int64_t)e * nchunks;
+            for (int base = sub; base < c; base += 8 * lanes_per_pair) {
+                int part[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int cc = base + u * lanes_per_pair;
+                    part[u] = cc < c ? row[cc] : 0;
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    sum += part[u];
+            }
         }
     }
+    for (int o = lanes_per_pair / 2; o > 0; o >>= 1)
+        sum += __shfl_xor(sum, o);
+    int slot = -1;
+    if (j < k && (unsigned)e < (unsigned)E && r >= 0 && (int64_t)sum + r < C)
+        slot = (int)((int64_t)e * C + sum + r);
     return slot;
 }
 
-constexpr int kBatch = 2;  // 16-byte vectors per lane in flight per store round
+// Segment 0 of each token records token_slot and recv_src.
+__device__ __forceinline__ void record_slot(int slot, int64_t t, int k, int lanes_per_pair,
+                                            int32_t *__restrict__ token_slot, int32_t *__restrict__ recv_src)
+{
+    const int lane = lane_id();
+    const int j = lane / lanes_per_pair;
+    if (j < k && lane == j * lanes_per_pair) {
+        token_slot[t * k + j] = slot;
+        if (slot >= 0)
+            recv_src[slot] = (int32_t)t;
+    }
+}
 
-// bf16 rows: one wave per (token, segment); lane owns 16-byte vectors
-// seg*vpl*64 + i*64 + lane, i < vpl.
+// The true per-expert totals, spread over the first waves of the grid.
+__device__ __forceinline__ void wave_totals(int64_t task, int64_t ntasks, const int32_t *__restrict__ chunk_counts,
+                                            int E, int nchunks, int32_t *__restrict__ expert_counts)
+{
+    const int lane = lane_id();
+    for (int64_t e = task; e < E; e += ntasks) {
+        const int32_t *row = chunk_counts + e * nchunks;
+        int sum = 0;
+        for (int cc = lane; cc < nchunks; cc += kWave)
+            sum += row[cc];
+        for (int o = kWave / 2; o > 0; o >>= 1)
+            sum += __shfl_xor(sum, o);
+        if (lane == 0)
+            expert_counts[e] = sum;
+    }
+}
+
+constexpr int kMaxV = 16;  // most 16-byte vectors per lane in flight (bf16 rows)
+
+// bf16 rows: one wave per (token, row segment).  The lane's vectors
+// seg*VPL*64 + i*64 + lane (i < VPL) are all requested first; the slot
+// arithmetic runs while they are in flight; then every vector is stored to
+// each of the k slots.  No work-group barrier: the waves' latency chains
+// overlap freely.
+template <int VPL>
 __global__ __launch_bounds__(kBlock) void dispatch_pack_bf16_kernel(
-    const uint4 *__restrict__ x, int64_t T, int nvec, const int32_t *__restrict__ topk_idx,
-    const int32_t *__restrict__ local_rank, const int32_t *__restrict__ chunk_base, int E, int k, int C,
-    int nchunks, int vpl, int segs, int32_t *__restrict__ token_slot, int32_t *__restrict__ recv_src,
-    uint4 *__restrict__ recv_x)
+    const u32x4 *__restrict__ x, int64_t T, int nvec, const int32_t *__restrict__ topk_idx,
+    const int32_t *__restrict__ local_rank, const int32_t *__restrict__ chunk_counts, int E, int k, int C,
+    int nchunks, int lanes_per_pair, int segs, int32_t *__restrict__ token_slot,
+    int32_t *__restrict__ recv_src, int32_t *__restrict__ expert_counts, u32x4 *__restrict__ recv_x)
 {
     const int lane = lane_id();
     const int64_t task = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
@@ -149,30 +188,29 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_bf16_kernel(
     const int seg = (int)(task - t * segs);
     if (t >= T)
         return;
-    const int slot = finish_slot(topk_idx, local_rank, chunk_base, t, E, k, C, nchunks, seg == 0, token_slot,
-                                 recv_src);
-    const uint4 *src = x + t * nvec;
-    const int v0 = seg * vpl * kWave + lane;
-    for (int i0 = 0; i0 < vpl; i0 += kBatch) {
-        uint4 buf[kBatch];
+    const u32x4 *src = x + t * nvec;
+    const int v0 = seg * VPL * kWave + lane;
+    u32x4 buf[VPL];
 #pragma unroll
-        for (int b = 0; b < kBatch; ++b) {
-            const int v = v0 + (i0 + b) * kWave;
-            if (i0 + b < vpl && v < nvec)
-                buf[b] = src[v];
-        }
-        for (int j = 0; j < k; ++j) {
-            const int s = lane_value(slot, j);
-            if (s < 0)
-                continue;
-            uint4 *dst = recv_x + (int64_t)s * nvec;
+    for (int i = 0; i < VPL; ++i)
+        buf[i] = v0 + i * kWave < nvec ? src[v0 + i * kWave] : (u32x4){0, 0, 0, 0};
+
+    const int slot = wave_slot(topk_idx, local_rank, chunk_counts, t, E, k, C, nchunks, lanes_per_pair);
+    if (seg == 0)
+        record_slot(slot, t, k, lanes_per_pair, token_slot, recv_src);
+    if (task < E)
+        wave_totals(task, T * segs, chunk_counts, E, nchunks, expert_counts);
+
+#pragma unroll 1
+    for (int j = 0; j < k; ++j) {
+        const int s = lane_value(slot, j * lanes_per_pair);
+        if (s < 0)
+            continue;
+        u32x4 *dst = recv_x + (int64_t)s * nvec;
 #pragma unroll
-            for (int b = 0; b < kBatch; ++b) {
-                const int v = v0 + (i0 + b) * kWave;
-                if (i0 + b < vpl && v < nvec)
-                    dst[v] = buf[b];
-            }
-        }
+        for (int i = 0; i < VPL; ++i)
+            if (v0 + i * kWave < nvec)
+                store_stream(dst + v0 + i * kWave, buf[i]);
     }
 }
 
@@ -201,13 +239,32 @@ __device__ __forceinline__ uint32_t e4m3_from_float(float q)
     return sign | code;
 }
 
-// fp8 rows: lane owns 16 consecutive elements (two 16-byte bf16 loads, one
-// 16-byte code store); 8 lanes form one 128-element scale block.
+// 16 bf16 values -> 16 E4M3 codes scaled by 1/sc (IEEE division).
+__device__ __forceinline__ u32x4 quantize16(const float *f, float sc)
+{
+    uint32_t packed[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        packed[q] = e4m3_from_float(f[4 * q] / sc) | (e4m3_from_float(f[4 * q + 1] / sc) << 8) |
+                    (e4m3_from_float(f[4 * q + 2] / sc) << 16) | (e4m3_from_float(f[4 * q + 3] / sc) << 24);
+    return (u32x4){packed[0], packed[1], packed[2], packed[3]};
+}
+
+constexpr int kMaxG = 8;   // most 16-element groups per lane in flight (fp8 rows)
+
+// fp8 rows: one wave per (token, row segment); a lane owns groups of 16
+// consecutive elements (two 16-byte loads, one 16-byte code store), groups
+// seg*VPL*64 + i*64 + lane.  The 8 consecutive lanes holding one
+// 128-element block find its amax with a 3-step butterfly; the scale is
+// amax/448 (IEEE division; 1 for an all-zero block) and each code is the
+// E4M3 encoding of x / scale (IEEE division).
+template <int VPL>
 __global__ __launch_bounds__(kBlock) void dispatch_pack_fp8_kernel(
-    const uint4 *__restrict__ x, int64_t T, int nvec16, const int32_t *__restrict__ topk_idx,
-    const int32_t *__restrict__ local_rank, const int32_t *__restrict__ chunk_base, int E, int k, int C,
-    int nchunks, int vpl, int segs, int32_t *__restrict__ token_slot, int32_t *__restrict__ recv_src,
-    uint4 *__restrict__ recv_x, float *__restrict__ recv_scales)
+    const u32x4 *__restrict__ x, int64_t T, int ngrp, const int32_t *__restrict__ topk_idx,
+    const int32_t *__restrict__ local_rank, const int32_t *__restrict__ chunk_counts, int E, int k, int C,
+    int nchunks, int lanes_per_pair, int segs, int32_t *__restrict__ token_slot,
+    int32_t *__restrict__ recv_src, int32_t *__restrict__ expert_counts, u32x4 *__restrict__ recv_x,
+    float *__restrict__ recv_scales)
 {
     const int lane = lane_id();
     const int64_t task = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
@@ -215,21 +272,30 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_fp8_kernel(
     const int seg = (int)(task - t * segs);
     if (t >= T)
         return;
-    const int slot = finish_slot(topk_idx, local_rank, chunk_base, t, E, k, C, nchunks, seg == 0, token_slot,
-                                 recv_src);
-    const int nblk = nvec16 / 8;  // scale blocks per row
-    const uint4 *src = x + t * (int64_t)nvec16 * 2;
-    const int v0 = seg * vpl * kWave + lane;
-    for (int i = 0; i < vpl; ++i) {
-        const int v = v0 + i * kWave;      // 16-element group; the 8 lanes of a block share validity
-        const bool ok = v < nvec16;
-        uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
-        if (ok) {
-            lo = src[2 * v];
-            hi = src[2 * v + 1];
+    const u32x4 *src = x + t * (int64_t)ngrp * 2;
+    const int nblk = ngrp / 8;
+    const int g0 = seg * VPL * kWave + lane;
+    u32x4 lo[VPL], hi[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        lo[i] = hi[i] = (u32x4){0, 0, 0, 0};
+        if (g0 + i * kWave < ngrp) {
+            lo[i] = src[2 * (g0 + i * kWave)];
+            hi[i] = src[2 * (g0 + i * kWave) + 1];
         }
+    }
+
+    const int slot = wave_slot(topk_idx, local_rank, chunk_counts, t, E, k, C, nchunks, lanes_per_pair);
+    if (seg == 0)
+        record_slot(slot, t, k, lanes_per_pair, token_slot, recv_src);
+    if (task < E)
+        wave_totals(task, T * segs, chunk_counts, E, nchunks, expert_counts);
+
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        const int g = g0 + i * kWave;   // the 8 lanes of a scale block share validity (ngrp % 8 == 0)
         float f[16];
-        const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        const uint32_t w[8] = {lo[i][0], lo[i][1], lo[i][2], lo[i][3], hi[i][0], hi[i][1], hi[i][2], hi[i][3]};
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
             f[2 * q] = bf16_lo(w[q]);
@@ -242,38 +308,41 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_fp8_kernel(
 #pragma unroll
         for (int o = 1; o < 8; o <<= 1)
             amax = fmaxf(amax, __shfl_xor(amax, o));
-        const float sc = amax == 0.0f ? 1.0f : amax / 448.0f;
-        uint32_t packed[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            packed[q] = e4m3_from_float(f[4 * q] / sc) | (e4m3_from_float(f[4 * q + 1] / sc) << 8) |
-                        (e4m3_from_float(f[4 * q + 2] / sc) << 16) | (e4m3_from_float(f[4 * q + 3] / sc) << 24);
-        }
-        const uint4 codes = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-        if (!ok)
+        if (g >= ngrp)
             continue;
+        const float sc = amax == 0.0f ? 1.0f : amax / 448.0f;
+        const u32x4 codes = quantize16(f, sc);
+#pragma unroll 1
         for (int j = 0; j < k; ++j) {
-            const int s = lane_value(slot, j);
+            const int s = lane_value(slot, j * lanes_per_pair);
             if (s < 0)
                 continue;
-            recv_x[(int64_t)s * nvec16 + v] = codes;
+            store_stream(recv_x + (int64_t)s * ngrp + g, codes);
             if ((lane & 7) == 0)
-                recv_scales[(int64_t)s * nblk + v / 8] = sc;
+                store_stream(recv_scales + (int64_t)s * nblk + g / 8, sc);
         }
     }
 }
 
-// Split each row into `segs` segments of `vpl` vectors per lane so that at
-// least ~min_waves waves are in flight.
-void split_rows(int64_t T, int nvec, int64_t min_waves, int *vpl, int *segs)
+// Lanes per (t, j) pair in the slot computation: 64 / next_pow2(k).
+int pair_lanes(int k)
 {
-    const int max_segs = (nvec + kWave - 1) / kWave;
-    int64_t want = T > 0 ? (min_waves + T - 1) / T : 1;
-    int s = (int)(want < 1 ? 1 : (want > max_segs ? max_segs : want));
-    int v = (nvec + s * kWave - 1) / (s * kWave);
-    s = (nvec + v * kWave - 1) / (v * kWave);
+    int p = 1;
+    while (p < k)
+        p <<= 1;
+    return kWave / p;
+}
+
+// Units (vectors or groups) per lane and row segments per token: the
+// smallest power of two (>= 2) that keeps the grid at <= ~32768 waves, so
+// small batches get many short waves and large ones few long ones.
+void choose_split(int64_t T, int nunits, int max_per_lane, int *vpl, int *segs)
+{
+    int v = 2;
+    while (v < max_per_lane && T * ((nunits + v * kWave - 1) / (v * kWave)) > 32768)
+        v *= 2;
     *vpl = v;
-    *segs = s;
+    *segs = (nunits + v * kWave - 1) / (v * kWave);
 }
 
 }  // namespace
@@ -290,37 +359,50 @@ hipError_t launch_dispatch(const uint16_t *x, int64_t T, int H, const int32_t *t
                            int dtype, void *recv_x, float *recv_scales, int32_t *recv_src,
                            int32_t *expert_counts, int32_t *token_slot, void *workspace, hipStream_t s)
 {
+    if (T == 0) {
+        hipLaunchKernelGGL(dispatch_zero_counts_kernel, dim3((E + kBlock - 1) / kBlock), dim3(kBlock), 0, s,
+                           expert_counts, E);
+        return hipGetLastError();
+    }
     const int nchunks = (int)((T + kChunk - 1) / kChunk);
     int32_t *chunk_counts = (int32_t *)workspace;
     int32_t *local_rank =
         (int32_t *)((char *)workspace + ((int64_t)E * nchunks * 4 + 255) / 256 * 256);
 
-    if (nchunks > 0) {
-        hipLaunchKernelGGL(dispatch_count_kernel, dim3(nchunks), dim3(kBlock), (size_t)E * kMaskWords * 4, s,
-                           topk_idx, T, E, k, nchunks, chunk_counts, local_rank);
-    }
-    hipLaunchKernelGGL(dispatch_scan_kernel, dim3((E + kWavesPerBlock - 1) / kWavesPerBlock), dim3(kBlock), 0, s,
-                       chunk_counts, E, nchunks, expert_counts);
-    if (T == 0)
-        return hipGetLastError();
+    hipLaunchKernelGGL(dispatch_count_kernel, dim3(nchunks), dim3(kBlock), (size_t)E * kMaskWords * 4, s, topk_idx,
+                       T, E, k, nchunks, chunk_counts, local_rank);
 
+    const int lpp = pair_lanes(k);
     int vpl, segs;
     if (dtype == 0) {
         const int nvec = H / 8;
-        split_rows(T, nvec, 2048, &vpl, &segs);
-        const int64_t tasks = T * segs;
-        const int64_t blocks = (tasks + kWavesPerBlock - 1) / kWavesPerBlock;
-        hipLaunchKernelGGL(dispatch_pack_bf16_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, s,
-                           (const uint4 *)x, T, nvec, topk_idx, local_rank, chunk_counts, E, k, C, nchunks, vpl,
-                           segs, token_slot, recv_src, (uint4 *)recv_x);
+        choose_split(T, nvec, kMaxV, &vpl, &segs);
+        const dim3 grid((unsigned)((T * segs + kWavesPerBlock - 1) / kWavesPerBlock));
+#define MOE_PACK_BF16(V)                                                                                         \
+    hipLaunchKernelGGL(dispatch_pack_bf16_kernel<V>, grid, dim3(kBlock), 0, s, (const u32x4 *)x, T, nvec, topk_idx, \
+                       local_rank, chunk_counts, E, k, C, nchunks, lpp, segs, token_slot, recv_src, expert_counts,   \
+                       (u32x4 *)recv_x)
+        switch (vpl) {
+        case 2: MOE_PACK_BF16(2); break;
+        case 4: MOE_PACK_BF16(4); break;
+        case 8: MOE_PACK_BF16(8); break;
+        default: MOE_PACK_BF16(16); break;
+        }
+#undef MOE_PACK_BF16
     } else {
-        const int nvec16 = H / 16;
-        split_rows(T, nvec16, 2048, &vpl, &segs);
-        const int64_t tasks = T * segs;
-        const int64_t blocks = (tasks + kWavesPerBlock - 1) / kWavesPerBlock;
-        hipLaunchKernelGGL(dispatch_pack_fp8_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, s,
-                           (const uint4 *)x, T, nvec16, topk_idx, local_rank, chunk_counts, E, k, C, nchunks, vpl,
-                           segs, token_slot, recv_src, (uint4 *)recv_x, recv_scales);
+        const int ngrp = H / 16;
+        choose_split(T, ngrp, kMaxG, &vpl, &segs);
+        const dim3 grid((unsigned)((T * segs + kWavesPerBlock - 1) / kWavesPerBlock));
+#define MOE_PACK_FP8(V)                                                                                          \
+    hipLaunchKernelGGL(dispatch_pack_fp8_kernel<V>, grid, dim3(kBlock), 0, s, (const u32x4 *)x, T, ngrp, topk_idx,  \
+                       local_rank, chunk_counts, E, k, C, nchunks, lpp, segs, token_slot, recv_src, expert_counts,   \
+                       (u32x4 *)recv_x, recv_scales)
+        switch (vpl) {
+        case 2: MOE_PACK_FP8(2); break;
+        case 4: MOE_PACK_FP8(4); break;
+        default: MOE_PACK_FP8(8); break;
+        }
+#undef MOE_PACK_FP8
     }
     return hipGetLastError();
 }

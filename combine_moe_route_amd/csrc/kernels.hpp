@@ -17,7 +17,10 @@ hipError_t launch_dispatch(const uint16_t *x, int64_t T, int H, const int32_t *t
                            int dtype, void *recv_x, float *recv_scales, int32_t *recv_src,
                            int32_t *expert_counts, int32_t *token_slot, void *workspace, hipStream_t s);
 
+// start/stop: optional events recorded at the kernel's start and end
+// (hipExtLaunchKernel); both NULL for an ordinary launch.
 hipError_t launch_combine(const uint16_t *y, int64_t nrows, int H, const int32_t *token_slot, const float *w,
-                          int64_t T, int k, uint16_t *out, hipStream_t s);
+                          int64_t T, int k, uint16_t *out, hipStream_t s, hipEvent_t start = nullptr,
+                          hipEvent_t stop = nullptr);
 
 }  // namespace moe

@@ -103,8 +103,11 @@ MOE_API int moe_dispatch(const uint16_t *x, int64_t T, int32_t H, const int32_t 
                                          recv_src, expert_counts, token_slot, workspace, stream));
 }
 
-MOE_API int moe_combine(const uint16_t *y, int32_t E, int32_t capacity, int32_t H, const int32_t *token_slot,
-                        const float *topk_w, int64_t T, int32_t k, uint16_t *out, hipStream_t stream)
+namespace {
+
+int combine_checked(const uint16_t *y, int32_t E, int32_t capacity, int32_t H, const int32_t *token_slot,
+                    const float *topk_w, int64_t T, int32_t k, uint16_t *out, hipStream_t stream, hipEvent_t start,
+                    hipEvent_t stop)
 {
     if (T < 0 || H < 1 || capacity < 1 || E < 1 || k < 1)
         return MOE_ERR_INVALID;
@@ -118,8 +121,28 @@ MOE_API int moe_combine(const uint16_t *y, int32_t E, int32_t capacity, int32_t 
         return MOE_ERR_INVALID;
     if (!aligned(y, 16) || !aligned(out, 16) || !aligned(token_slot, 4) || !aligned(topk_w, 4))
         return MOE_ERR_INVALID;
+    const uintptr_t y0 = (uintptr_t)y, y1 = y0 + (uintptr_t)E * capacity * H * 2;
+    const uintptr_t o0 = (uintptr_t)out, o1 = o0 + (uintptr_t)T * H * 2;
+    if (o0 < y1 && y0 < o1)
+        return MOE_ERR_INVALID;  // out overlaps y
     (void)hipGetLastError();
-    return from_hip(moe::launch_combine(y, (int64_t)E * capacity, H, token_slot, topk_w, T, k, out, stream));
+    return from_hip(
+        moe::launch_combine(y, (int64_t)E * capacity, H, token_slot, topk_w, T, k, out, stream, start, stop));
+}
+
+}  // namespace
+
+MOE_API int moe_combine(const uint16_t *y, int32_t E, int32_t capacity, int32_t H, const int32_t *token_slot,
+                        const float *topk_w, int64_t T, int32_t k, uint16_t *out, hipStream_t stream)
+{
+    return combine_checked(y, E, capacity, H, token_slot, topk_w, T, k, out, stream, nullptr, nullptr);
+}
+
+MOE_API int moe_combine_timed(const uint16_t *y, int32_t E, int32_t capacity, int32_t H,
+                              const int32_t *token_slot, const float *topk_w, int64_t T, int32_t k, uint16_t *out,
+                              hipStream_t stream, hipEvent_t start, hipEvent_t stop)
+{
+    return combine_checked(y, E, capacity, H, token_slot, topk_w, T, k, out, stream, start, stop);
 }
 
 }  // extern "C"

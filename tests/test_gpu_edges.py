@@ -246,3 +246,32 @@ def test_api_rejects_bad_arguments(dev):
     bad = list(args); bad[6] = 0
     assert lib.moe_dispatch(*bad) == moe.binding.MOE_ERR_INVALID
     torch.cuda.synchronize()
+
+
+def test_combine_timed_matches_combine(dev):
+    rng = np.random.default_rng(31)
+    T, H, E, k, C = 300, 512, 16, 4, 300
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    counts, slot, src = oracle.assign_slots(idx, E, C)
+    w = rng.uniform(0, 1, (T, k)).astype(np.float32)
+    y = torch.randn(E, C, H, device=dev).to(torch.bfloat16)
+    ts, wt = torch.from_numpy(slot).to(dev), torch.from_numpy(w).to(dev)
+    ref = moe.moe_combine(y, ts, wt)
+    ev = moe.HipEvents()
+    a, b = ev.create(), ev.create()
+    got = moe.moe_combine(y, ts, wt, events=(a, b))
+    ms = ev.elapsed_ms(a, b)
+    ev.destroy(a)
+    ev.destroy(b)
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+    assert 0.0 < ms < 1000.0
+    want = oracle.combine(dev_bits(y.view(E * C, H))[slot.reshape(-1)], slot, w)
+    assert bf16_ulp_distance(dev_bits(got), want).max() <= 1
+
+
+def test_combine_rejects_overlapping_output(dev):
+    y = torch.zeros(2, 4, 64, dtype=torch.bfloat16, device=dev)
+    ts = torch.zeros(4, 1, dtype=torch.int32, device=dev)
+    w = torch.ones(4, 1, dtype=torch.float32, device=dev)
+    with pytest.raises(moe.MoeError):
+        moe.moe_combine(y, ts, w, out=y.view(8, 64)[:4])
