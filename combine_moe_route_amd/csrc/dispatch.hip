@@ -214,40 +214,48 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_bf16_kernel(
     }
 }
 
-// OCP E4M3 encode, round to nearest even, saturating at +-448.  Works on
-// the float's bit pattern: the 23-bit mantissa is rounded to 3 bits by
-// adding half-minus-one plus the kept LSB; the exponent is re-biased from
-// 127 to 7.  Magnitudes below 2^-6 are counted in units of 2^-9 (exact
-// power-of-two scaling, then round-half-even to an integer).
-__device__ __forceinline__ uint32_t e4m3_from_float(float q)
+// x / sc for one bf16 value, bit-identical to the IEEE division x / sc.
+// With r = 1/sc (one IEEE division per scale block), q0 = x*r is within an
+// ulp or so of the quotient; the residual x - q0*sc is exact in an FMA and
+// one correction step q0 + res*r rounds to the IEEE quotient (Markstein's
+// division scheme).  The residual underflows for tiny values, so |x| or sc
+// below 2^-100 use the IEEE division itself; copysign keeps the sign of a
+// zero quotient.  Checked bit for bit against the IEEE E4M3 codes for every
+// bf16 x with |x| <= amax and every bf16 amax.
+__device__ __forceinline__ float divide_by_scale(float x, float sc, float r, bool fast)
 {
-    const uint32_t u = __float_as_uint(q);
-    const uint32_t sign = (u >> 24) & 0x80u;
-    const uint32_t a = u & 0x7FFFFFFFu;
-    uint32_t code;
-    if (a > 0x7F800000u) {
-        code = 0x7Fu;                                   // NaN
-    } else if (a >= 0x43E00000u) {
-        code = 0x7Eu;                                   // |q| >= 448 (and inf): saturate
-    } else if (a < 0x3C800000u) {
-        code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);  // subnormal: units of 2^-9
-    } else {
-        const uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;       // (exp << 3 | m3), rounded
-        code = r - (120u << 3);                         // exponent bias 127 -> 7
-        code = code > 0x7Eu ? 0x7Eu : code;
-    }
-    return sign | code;
+    const float q0 = x * r;
+    float q = __builtin_copysignf(__builtin_fmaf(__builtin_fmaf(-q0, sc, x), r, q0), x);
+    if (!(fast && (__builtin_fabsf(x) >= 0x1p-100f || x == 0.0f)))
+        q = x / sc;
+    return q;
 }
 
-// 16 bf16 values -> 16 E4M3 codes scaled by 1/sc (IEEE division).
+// Four quotients -> four OCP E4M3 codes in one word.  v_cvt_pk_fp8_f32
+// rounds to nearest even; the clamp to +-448 makes it saturate (a magnitude
+// above 448 becomes 448), matching the E4M3 encoding the codes are defined
+// by on every fp32 input of magnitude <= 464 (checked exhaustively).
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d)
+{
+    a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+    b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+    c = __builtin_amdgcn_fmed3f(c, -448.0f, 448.0f);
+    d = __builtin_amdgcn_fmed3f(d, -448.0f, 448.0f);
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+
+// 16 bf16 values -> 16 E4M3 codes of x / sc.
 __device__ __forceinline__ u32x4 quantize16(const float *f, float sc)
 {
-    uint32_t packed[4];
+    const float r = 1.0f / sc;
+    const bool fast = sc >= 0x1p-100f;
+    float q[16];
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-        packed[q] = e4m3_from_float(f[4 * q] / sc) | (e4m3_from_float(f[4 * q + 1] / sc) << 8) |
-                    (e4m3_from_float(f[4 * q + 2] / sc) << 16) | (e4m3_from_float(f[4 * q + 3] / sc) << 24);
-    return (u32x4){packed[0], packed[1], packed[2], packed[3]};
+    for (int i = 0; i < 16; ++i)
+        q[i] = divide_by_scale(f[i], sc, r, fast);
+    return (u32x4){e4m3x4(q[0], q[1], q[2], q[3]), e4m3x4(q[4], q[5], q[6], q[7]), e4m3x4(q[8], q[9], q[10], q[11]),
+                   e4m3x4(q[12], q[13], q[14], q[15])};
 }
 
 constexpr int kMaxG = 8;   // most 16-element groups per lane in flight (fp8 rows)
@@ -257,7 +265,8 @@ constexpr int kMaxG = 8;   // most 16-element groups per lane in flight (fp8 row
 // seg*VPL*64 + i*64 + lane.  The 8 consecutive lanes holding one
 // 128-element block find its amax with a 3-step butterfly; the scale is
 // amax/448 (IEEE division; 1 for an all-zero block) and each code is the
-// E4M3 encoding of x / scale (IEEE division).
+// E4M3 encoding (round to nearest even, saturating) of x / scale, with the
+// quotient bit-identical to an IEEE division (divide_by_scale).
 template <int VPL>
 __global__ __launch_bounds__(kBlock) void dispatch_pack_fp8_kernel(
     const u32x4 *__restrict__ x, int64_t T, int ngrp, const int32_t *__restrict__ topk_idx,
@@ -266,6 +275,10 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_fp8_kernel(
     int32_t *__restrict__ recv_src, int32_t *__restrict__ expert_counts, u32x4 *__restrict__ recv_x,
     float *__restrict__ recv_scales)
 {
+    // the wave's block scales, staged so each slot's scale segment is
+    // written by one contiguous store instruction
+    __shared__ float s_scale[kWavesPerBlock][VPL * 8];
+    float *my_scale = s_scale[threadIdx.x / kWave];
     const int lane = lane_id();
     const int64_t task = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
     const int64_t t = task / segs;
@@ -312,14 +325,29 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_fp8_kernel(
             continue;
         const float sc = amax == 0.0f ? 1.0f : amax / 448.0f;
         const u32x4 codes = quantize16(f, sc);
+        if ((lane & 7) == 0)
+            my_scale[i * 8 + lane / 8] = sc;
 #pragma unroll 1
         for (int j = 0; j < k; ++j) {
             const int s = lane_value(slot, j * lanes_per_pair);
             if (s < 0)
                 continue;
             store_stream(recv_x + (int64_t)s * ngrp + g, codes);
-            if ((lane & 7) == 0)
-                store_stream(recv_scales + (int64_t)s * nblk + g / 8, sc);
+        }
+    }
+    // scales of this segment's blocks blk0 .. blk0+nb-1, one lane each
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int blk0 = seg * VPL * 8;
+    const int nb = min(VPL * 8, nblk - blk0);
+    if (lane < nb) {
+        const float v = my_scale[lane];
+#pragma unroll 1
+        for (int j = 0; j < k; ++j) {
+            const int s = lane_value(slot, j * lanes_per_pair);
+            if (s >= 0)
+                store_stream(recv_scales + (int64_t)s * nblk + blk0 + lane, v);
         }
     }
 }
@@ -334,12 +362,14 @@ int pair_lanes(int k)
 }
 
 // Units (vectors or groups) per lane and row segments per token: the
-// smallest power of two (>= 2) that keeps the grid at <= ~32768 waves, so
-// small batches get many short waves and large ones few long ones.
+// smallest power of two (>= 2) that keeps the grid at <= 131072 waves.  Short
+// waves balance best (measured: 2 per lane is fastest or level with larger
+// counts on every workload); the cap only bounds the redundant slot work of
+// very long rows.
 void choose_split(int64_t T, int nunits, int max_per_lane, int *vpl, int *segs)
 {
     int v = 2;
-    while (v < max_per_lane && T * ((nunits + v * kWave - 1) / (v * kWave)) > 32768)
+    while (v < max_per_lane && T * ((nunits + v * kWave - 1) / (v * kWave)) > 131072)
         v *= 2;
     *vpl = v;
     *segs = (nunits + v * kWave - 1) / (v * kWave);
