@@ -275,3 +275,31 @@ def test_combine_rejects_overlapping_output(dev):
     w = torch.ones(4, 1, dtype=torch.float32, device=dev)
     with pytest.raises(moe.MoeError):
         moe.moe_combine(y, ts, w, out=y.view(8, 64)[:4])
+
+
+def test_workspace_reused_across_shapes(dev):
+    """One workspace, sized for the largest call, serves a run of dispatches
+    whose T, E and k differ, so each call's regions (per-chunk counts,
+    in-chunk ranks) fall on words an earlier call left in another region.
+    Every call must still match the oracle exactly."""
+    cases = [(9000, 64, 4), (300, 256, 8), (70000, 8, 2), (256, 128, 8), (1, 1, 1), (20000, 256, 8),
+             (4097, 16, 2), (9000, 64, 4)]
+    ws_bytes = max(moe.moe_dispatch_workspace_bytes(T, E, k) for T, E, k in cases)
+    shared = torch.full((ws_bytes,), 0x5A, dtype=torch.uint8, device=dev)
+    H = 64
+    for n, (T, E, k) in enumerate(cases):
+        say(f"[workspace reuse] call {n}: T={T} E={E} k={k}")
+        rng = np.random.default_rng(700 + n)
+        idx_o, _ = oracle.route_topk(rng.standard_normal((T, E)).astype(np.float32), k)
+        C = max(1, T * k // E)
+        x = _bf16_bits(rng.standard_normal((T, H)))
+        bufs = moe.DispatchBuffers.allocate(T, H, E, k, C, False, dev)
+        bufs.workspace = shared
+        moe.moe_dispatch(to_dev_bf16(x, dev), torch.from_numpy(idx_o).to(dev), E, C, bufs=bufs)
+        counts_o, slot_o, src_o = oracle.assign_slots(idx_o, E, C)
+        np.testing.assert_array_equal(bufs.expert_counts.cpu().numpy(), counts_o)
+        np.testing.assert_array_equal(bufs.token_slot.cpu().numpy(), slot_o)
+        filled = src_o >= 0
+        np.testing.assert_array_equal(bufs.recv_src.cpu().numpy().reshape(-1)[filled], src_o[filled])
+        rows = dev_bits(bufs.recv_x.view(E * C, H))
+        np.testing.assert_array_equal(rows[filled], x[src_o[filled]])
