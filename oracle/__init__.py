@@ -54,6 +54,8 @@ def _load():
     i32, i64 = ctypes.c_int32, ctypes.c_int64
     lib.oracle_route_topk.argtypes = [P, i64, i32, i32, P, P]
     lib.oracle_route_topk.restype = ctypes.c_int
+    lib.oracle_route_topk_grouped.argtypes = [P, i64, i32, i32, i32, i32, P, P]
+    lib.oracle_route_topk_grouped.restype = ctypes.c_int
     lib.oracle_assign_slots.argtypes = [P, i64, i32, i32, i32, P, P, P]
     lib.oracle_assign_slots.restype = ctypes.c_int
     lib.oracle_quantize_row_fp8.argtypes = [P, i32, P, P]
@@ -103,6 +105,20 @@ def route_topk(logits: np.ndarray, k: int):
     idx = np.empty((T, k), np.int32)
     w = np.empty((T, k), np.float32)
     _check(_load().oracle_route_topk(_ptr(logits), T, E, k, _ptr(idx), _ptr(w)), "route_topk")
+    return idx, w
+
+
+def route_topk_grouped(logits: np.ndarray, k: int, n_groups: int, topk_groups: int):
+    """Group-limited top-k: experts form n_groups groups of E/n_groups
+    consecutive experts, each scored by the fp32 sum of its two largest
+    logits; the k experts are chosen among the topk_groups best groups.
+    Weights are the full softmax, as in route_topk.  Returns (idx, w)."""
+    logits = _c(logits, np.float32)
+    T, E = logits.shape
+    idx = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float32)
+    _check(_load().oracle_route_topk_grouped(_ptr(logits), T, E, k, n_groups, topk_groups, _ptr(idx), _ptr(w)),
+           "route_topk_grouped")
     return idx, w
 
 

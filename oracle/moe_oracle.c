@@ -156,6 +156,102 @@ int oracle_route_topk(const float *logits, int64_t T, int32_t E, int32_t k,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Route, group-limited ("node-limited") variant                             */
+/* [HBK] "High-throughput mode": DeepSeek-V3 limits each token to a few      */
+/* nodes -- every node is scored by the sum of its two best expert scores,   */
+/* only the best nodes stay eligible, and the top experts are then picked    */
+/* among those nodes' experts.  Here a node is a group of E/G consecutive    */
+/* experts and a score is the expert's logit (the value experts are          */
+/* selected on).                                                             */
+/* ------------------------------------------------------------------------ */
+
+/* For each token t:
+ *   score[g], g = 0..G-1: the fp32 sum of the two largest logits among
+ *     experts g*E/G .. (g+1)*E/G - 1 (a repeated largest value counts twice).
+ *   kept groups: the M groups with the largest scores, equal scores ordered
+ *     by ascending group index.
+ *   idx[t][j]: the k largest logits among the kept groups' experts, ordered
+ *     as in oracle_route_topk (descending, ties to the lower index).
+ *   w[t][j]: the full softmax over all E logits at idx[t][j], exactly as in
+ *     oracle_route_topk: limiting the groups changes which experts are
+ *     chosen, not the router's distribution.
+ * Requires E % G == 0, E/G >= 2, 1 <= M <= G, k <= M*E/G. */
+int oracle_route_topk_grouped(const float *logits, int64_t T, int32_t E, int32_t k, int32_t G, int32_t M,
+                              int32_t *idx, float *w)
+{
+    if (T < 0 || E < 1 || k < 1 || k > E || G < 1 || E % G != 0 || E / G < 2 || M < 1 || M > G ||
+        (int64_t)k > (int64_t)M * (E / G))
+        return -1;
+    if (T == 0)
+        return 0;
+    if (!logits || !idx || !w)
+        return -1;
+    const int32_t gs = E / G;
+    float *score = (float *)malloc((size_t)G * sizeof(float));
+    unsigned char *kept = (unsigned char *)malloc((size_t)G);
+    unsigned char *taken = (unsigned char *)malloc((size_t)E);
+    if (!score || !kept || !taken) {
+        free(score);
+        free(kept);
+        free(taken);
+        return -1;
+    }
+    for (int64_t t = 0; t < T; ++t) {
+        const float *row = logits + t * (int64_t)E;
+        /* group scores: largest, then largest of the rest */
+        for (int32_t g = 0; g < G; ++g) {
+            const int32_t lo = g * gs;
+            int32_t b1 = lo;
+            for (int32_t e = lo + 1; e < lo + gs; ++e)
+                if (row[e] > row[b1])
+                    b1 = e;
+            int32_t b2 = -1;
+            for (int32_t e = lo; e < lo + gs; ++e)
+                if (e != b1 && (b2 < 0 || row[e] > row[b2]))
+                    b2 = e;
+            const float a = row[b1], b = row[b2];
+            score[g] = a + b;                       /* one fp32 rounding */
+        }
+        /* the M best groups, repeated selection (strict: lower index wins) */
+        memset(kept, 0, (size_t)G);
+        for (int32_t m = 0; m < M; ++m) {
+            int32_t best = -1;
+            for (int32_t g = 0; g < G; ++g)
+                if (!kept[g] && (best < 0 || score[g] > score[best]))
+                    best = g;
+            kept[best] = 1;
+        }
+        /* top-k among the kept groups' experts */
+        for (int32_t e = 0; e < E; ++e)
+            taken[e] = kept[e / gs] ? 0 : 1;      /* a banned expert is never eligible */
+        for (int32_t j = 0; j < k; ++j) {
+            int32_t best = -1;
+            for (int32_t e = 0; e < E; ++e) {
+                if (taken[e])
+                    continue;
+                if (best < 0 || row[e] > row[best])
+                    best = e;
+            }
+            taken[best] = 1;
+            idx[t * k + j] = best;
+        }
+        double mx = (double)row[0];
+        for (int32_t e = 1; e < E; ++e)
+            if ((double)row[e] > mx)
+                mx = (double)row[e];
+        double z = 0.0;
+        for (int32_t e = 0; e < E; ++e)
+            z += exp((double)row[e] - mx);
+        for (int32_t j = 0; j < k; ++j)
+            w[t * k + j] = (float)(exp((double)row[idx[t * k + j]] - mx) / z);
+    }
+    free(score);
+    free(kept);
+    free(taken);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Dispatch, step 1+2: per-expert counts and fixed-slot assignment           */
 /* [HBK] "Why MoE's all-to-all is hard": route, then sort by destination,    */
 /* then count per destination.  [HBK] "Low-latency mode": a fixed number of  */
