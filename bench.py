@@ -1,8 +1,9 @@
 #!/usr/bin/env python3
 """Benchmark of the MoE token routing/dispatch/combine path on one MI355X.
 
-One step = moe_route_topk + moe_dispatch + moe_combine, back to back on one
-stream, over one batch of seeded synthetic input already resident in HBM.
+One step = moe_route_topk (or moe_route_topk_grouped with --route-groups) +
+moe_dispatch + moe_combine, back to back on one stream, over one batch of
+seeded synthetic input already resident in HBM.
 W untimed warm-up steps, then exactly K timed steps between device
 synchronisations.  Prints one JSON line (stdout):
 
@@ -130,7 +131,7 @@ def cpu_baseline(w: W.Workload, seconds: float) -> dict:
 class BufferSet:
     """One complete copy of a step's inputs, outputs and fixed-slot buffers."""
 
-    def __init__(self, w: W.Workload, logits_cpu, x_cpu, dev, moe, torch):
+    def __init__(self, w: W.Workload, logits_cpu, x_cpu, dev, moe, torch, route_groups=None):
         self.logits = logits_cpu.to(dev)
         self.x = x_cpu.to(dev)
         self.idx = torch.empty(w.T, w.k, dtype=torch.int32, device=dev)
@@ -139,7 +140,7 @@ class BufferSet:
         self.y = torch.empty(w.E, w.C, w.H, dtype=torch.bfloat16, device=dev)
         self.out = torch.empty(w.T, w.H, dtype=torch.bfloat16, device=dev)
         self.step = moe.PreparedStep(self.logits, w.k, self.x, w.C, w.fp8, self.bufs, self.y, self.out,
-                                     self.idx, self.wt)
+                                     self.idx, self.wt, route_groups=route_groups)
 
     def fill_expert_outputs(self, w: W.Workload, torch, gen):
         """Seeded N(0,1) bf16 expert outputs in the slots the dispatch filled."""
@@ -165,6 +166,8 @@ def main() -> int:
                     help="combine launch timing: events attached to the launch (ext) or recorded around it")
     ap.add_argument("--no-overlap", action="store_true",
                     help="skip the extra two-batches-in-flight measurement")
+    ap.add_argument("--route-groups", default="",
+                    help="G:M routes with moe_route_topk_grouped (G expert groups, the best M kept)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -190,7 +193,8 @@ def main() -> int:
 
     logits_cpu = W.make_logits(w)
     x_cpu = W.make_x(w)
-    sets = [BufferSet(w, logits_cpu, x_cpu, dev, moe, torch) for _ in range(R)]
+    route_groups = tuple(int(v) for v in args.route_groups.split(":")) if args.route_groups else None
+    sets = [BufferSet(w, logits_cpu, x_cpu, dev, moe, torch, route_groups) for _ in range(R)]
     gen = torch.Generator(device=dev)
     gen.manual_seed(w.seed * 16 + 3)
     for s in sets:
@@ -211,6 +215,7 @@ def main() -> int:
         torch.cuda.synchronize()
         for si, st in enumerate(sets):
             st.step = moe.PreparedStep(st.logits, w.k, st.x, w.C, w.fp8, st.bufs, st.y, st.out, st.idx, st.wt,
+                                       route_groups=route_groups,
                                        stream=streams[si % nstreams])
 
     def run_steps(first, n, nstreams, ev=None):
@@ -307,6 +312,7 @@ def main() -> int:
         "config": {
             "workload": w.name, "tokens": w.T, "hidden": w.H, "experts": w.E, "top_k": w.k, "capacity": w.C,
             "row_dtype": "fp8-e4m3+fp32/128" if w.fp8 else "bf16", "routing": w.routing,
+            "route_groups": ({"groups": route_groups[0], "kept": route_groups[1]} if route_groups else None),
             "parallelism": "none (1 GPU)",
             "algorithmic_bytes_per_step": nbytes["total"],
             "effective_hbm_gbps": gbps,

@@ -49,6 +49,8 @@ def load() -> ctypes.CDLL:
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_route_topk.argtypes = [P, i64, i32, i32, P, P, P]
     lib.moe_route_topk.restype = ctypes.c_int
+    lib.moe_route_topk_grouped.argtypes = [P, i64, i32, i32, i32, i32, P, P, P]
+    lib.moe_route_topk_grouped.restype = ctypes.c_int
     lib.moe_dispatch_workspace_bytes.argtypes = [i64, i32, i32]
     lib.moe_dispatch_workspace_bytes.restype = ctypes.c_size_t
     lib.moe_dispatch.argtypes = [P, i64, i32, P, i32, i32, i32, i32, P, P, P, P, P, P, ctypes.c_size_t, P]
@@ -152,6 +154,26 @@ def moe_route_topk(logits: torch.Tensor, k: int, topk_idx: torch.Tensor | None =
     return topk_idx, topk_w
 
 
+def moe_route_topk_grouped(logits: torch.Tensor, k: int, n_groups: int, topk_groups: int,
+                           topk_idx: torch.Tensor | None = None, topk_w: torch.Tensor | None = None, stream=None):
+    """Group-limited top-k: the k experts are chosen among the topk_groups
+    best of n_groups groups of consecutive experts (a group's score is the
+    sum of its two largest logits).  Weights as in moe_route_topk."""
+    T, E = logits.shape
+    _need(logits, torch.float32, (T, E), "logits")
+    if topk_idx is None:
+        topk_idx = torch.empty(T, k, dtype=torch.int32, device=logits.device)
+    if topk_w is None:
+        topk_w = torch.empty(T, k, dtype=torch.float32, device=logits.device)
+    _need(topk_idx, torch.int32, (T, k), "topk_idx")
+    _need(topk_w, torch.float32, (T, k), "topk_w")
+    rc = load().moe_route_topk_grouped(_ptr(logits), T, E, k, n_groups, topk_groups, _ptr(topk_idx), _ptr(topk_w),
+                                       _stream(stream))
+    if rc != MOE_OK:
+        raise MoeError("moe_route_topk_grouped", rc)
+    return topk_idx, topk_w
+
+
 def moe_dispatch_workspace_bytes(T: int, E: int, k: int) -> int:
     return int(load().moe_dispatch_workspace_bytes(T, E, k))
 
@@ -243,7 +265,9 @@ class PreparedStep:
 
     def __init__(self, logits: torch.Tensor, k: int, x: torch.Tensor, capacity: int, fp8: bool,
                  bufs: DispatchBuffers, y: torch.Tensor, out: torch.Tensor, topk_idx: torch.Tensor,
-                 topk_w: torch.Tensor, stream=None):
+                 topk_w: torch.Tensor, stream=None, route_groups: tuple[int, int] | None = None):
+        """route_groups = (n_groups, topk_groups) routes with
+        moe_route_topk_grouped instead of moe_route_topk."""
         T, E = logits.shape
         H = x.shape[1]
         _need(logits, torch.float32, (T, E), "logits")
@@ -256,7 +280,13 @@ class PreparedStep:
         _need(out, torch.bfloat16, (T, H), "out")
         self._lib = load()
         s = _stream(stream)
-        self.route_args = (_ptr(logits), T, E, k, _ptr(topk_idx), _ptr(topk_w), s)
+        if route_groups is None:
+            self._route_fn, self._route_name = self._lib.moe_route_topk, "moe_route_topk"
+            self.route_args = (_ptr(logits), T, E, k, _ptr(topk_idx), _ptr(topk_w), s)
+        else:
+            self._route_fn, self._route_name = self._lib.moe_route_topk_grouped, "moe_route_topk_grouped"
+            self.route_args = (_ptr(logits), T, E, k, int(route_groups[0]), int(route_groups[1]), _ptr(topk_idx),
+                               _ptr(topk_w), s)
         self.dispatch_args = (
             _ptr(x), T, H, _ptr(topk_idx), E, k, capacity, MOE_DTYPE_FP8_E4M3 if fp8 else MOE_DTYPE_BF16,
             _ptr(bufs.recv_x), _ptr(bufs.recv_scales) if fp8 else None, _ptr(bufs.recv_src),
@@ -265,9 +295,9 @@ class PreparedStep:
         self._keep = (logits, x, bufs, y, out, topk_idx, topk_w)
 
     def route(self):
-        rc = self._lib.moe_route_topk(*self.route_args)
+        rc = self._route_fn(*self.route_args)
         if rc != MOE_OK:
-            raise MoeError("moe_route_topk", rc)
+            raise MoeError(self._route_name, rc)
 
     def dispatch(self):
         rc = self._lib.moe_dispatch(*self.dispatch_args)

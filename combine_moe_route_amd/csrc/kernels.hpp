@@ -11,6 +11,9 @@ namespace moe {
 hipError_t launch_route_topk(const float *logits, int64_t T, int E, int k, int32_t *idx, float *w,
                              hipStream_t s);
 
+hipError_t launch_route_topk_grouped(const float *logits, int64_t T, int E, int k, int n_groups, int topk_groups,
+                                     int32_t *idx, float *w, hipStream_t s);
+
 size_t dispatch_workspace_bytes(int64_t T, int E, int k);
 
 hipError_t launch_dispatch(const uint16_t *x, int64_t T, int H, const int32_t *topk_idx, int E, int k, int C,

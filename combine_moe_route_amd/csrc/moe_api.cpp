@@ -59,6 +59,31 @@ MOE_API int moe_route_topk(const float *logits, int64_t T, int32_t E, int32_t k,
     return from_hip(moe::launch_route_topk(logits, T, E, k, topk_idx, topk_w, stream));
 }
 
+MOE_API int moe_route_topk_grouped(const float *logits, int64_t T, int32_t E, int32_t k, int32_t n_groups,
+                                   int32_t topk_groups, int32_t *topk_idx, float *topk_w, hipStream_t stream)
+{
+    if (T < 0)
+        return MOE_ERR_INVALID;
+    int rc = check_ek(E, k);
+    if (rc != MOE_OK)
+        return rc;
+    if (n_groups < 1 || E % n_groups != 0 || E / n_groups < 2 || topk_groups < 1 || topk_groups > n_groups ||
+        (int64_t)topk_groups * (E / n_groups) < k)
+        return MOE_ERR_INVALID;
+    if (n_groups > MOE_MAX_GROUPS)
+        return MOE_ERR_UNSUPPORTED;
+    if (T == 0)
+        return MOE_OK;
+    if (!logits || !topk_idx || !topk_w)
+        return MOE_ERR_INVALID;
+    if (!aligned(logits, 4) || !aligned(topk_idx, 4) || !aligned(topk_w, 4))
+        return MOE_ERR_INVALID;
+    if (T > MOE_MAX_TOKENS)
+        return MOE_ERR_UNSUPPORTED;
+    (void)hipGetLastError();
+    return from_hip(moe::launch_route_topk_grouped(logits, T, E, k, n_groups, topk_groups, topk_idx, topk_w, stream));
+}
+
 MOE_API size_t moe_dispatch_workspace_bytes(int64_t T, int32_t E, int32_t k)
 {
     if (T < 0 || E < 1 || k < 1 || E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK)

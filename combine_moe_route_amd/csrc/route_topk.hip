@@ -105,25 +105,13 @@ __device__ __forceinline__ float key_value(uint32_t key)
     return (key & 0x80000000u) ? __uint_as_float(key & 0x7FFFFFFFu) : __uint_as_float(~key);
 }
 
-// VEC: the row's VPL consecutive logits of a lane are one aligned vector
-// load (E % VPL == 0 and a suitably aligned base).
-template <int G, int VPL, bool VEC>
-__global__ __launch_bounds__(kBlock) void route_topk_kernel(const float *__restrict__ logits, int64_t T, int E, int k,
-                                                            int32_t *__restrict__ topk_idx,
-                                                            float *__restrict__ topk_w)
+// Loads lane gl's VPL consecutive logits of token t (VEC: as one aligned
+// vector) and their order keys; experts >= E and inactive tokens get key 0,
+// which is below every real key.
+template <int VPL, bool VEC>
+__device__ __forceinline__ void load_logits(const float *__restrict__ logits, int64_t t, bool active, int E, int gl,
+                                            float (&v)[VPL], uint32_t (&key)[VPL])
 {
-    static_assert(G >= 1 && G <= kWave && (kWave % G) == 0, "group must divide the wave");
-    static_assert(VPL == 1 || G == kWave, "several logits per lane only with one token per wave");
-    constexpr int kGroupsPerWave = kWave / G;
-    const int lane = lane_id();
-    const int grp = lane / G;
-    const int gl = lane % G;
-    const int64_t wave = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
-    const int64_t t = wave * kGroupsPerWave + grp;
-    const bool active = t < T;
-
-    float v[VPL];
-    uint32_t key[VPL];
     const float *row = logits + (active ? t : 0) * (int64_t)E + gl * VPL;
     if (VEC && active && gl * VPL < E) {
         if (VPL == 2) {
@@ -148,10 +136,23 @@ __global__ __launch_bounds__(kBlock) void route_topk_kernel(const float *__restr
         for (int i = 0; i < VPL; ++i) {
             const bool ok = active && gl * VPL + i < E;
             v[i] = ok ? row[i] : 0.0f;
-            key[i] = ok ? order_key(v[i]) : 0u;  // 0 is below every real key
+            key[i] = ok ? order_key(v[i]) : 0u;
         }
     }
+}
 
+// k selection rounds over the eligible keys (key 0 = not eligible), then the
+// full softmax over every logit of the token (eligible or not) and the
+// stores of token t's ids and weights.  ALL_ELIGIBLE: no expert was excluded,
+// so the first choice is the token's largest logit.
+template <int G, int VPL, bool ALL_ELIGIBLE>
+__device__ __forceinline__ void select_and_store(const float (&v)[VPL], uint32_t (&key)[VPL], bool active, int64_t t,
+                                                 int E, int k, int32_t *__restrict__ topk_idx,
+                                                 float *__restrict__ topk_w)
+{
+    const int lane = lane_id();
+    const int grp = lane / G;
+    const int gl = lane % G;
     float top = 0.0f;   // the largest logit of the token
     int my_e = 0;       // lane gl == j keeps the j-th choice
     float my_v = 0.0f;
@@ -191,17 +192,180 @@ __global__ __launch_bounds__(kBlock) void route_topk_kernel(const float *__restr
         }
     }
 
+    // the softmax's maximum is the largest logit of all; with every expert
+    // eligible it is the first choice
     float s = 0.0f;
+    float mx = top;
+    if (!ALL_ELIGIBLE) {
+        uint32_t mk = 0;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i)
+            if (active && gl * VPL + i < E)
+                mk = umax(mk, order_key(v[i]));
+        mx = key_value(group_max<G>(mk));
+    }
 #pragma unroll
     for (int i = 0; i < VPL; ++i)
         if (active && gl * VPL + i < E)
-            s += expf(v[i] - top);
+            s += expf(v[i] - mx);
     s = group_sum<G>(s);
 
     if (active && gl < k) {
         topk_idx[t * k + gl] = my_e;
-        topk_w[t * k + gl] = expf(my_v - top) / s;
+        topk_w[t * k + gl] = expf(my_v - mx) / s;
     }
+}
+
+template <int G, int VPL, bool VEC>
+__global__ __launch_bounds__(kBlock) void route_topk_kernel(const float *__restrict__ logits, int64_t T, int E, int k,
+                                                            int32_t *__restrict__ topk_idx,
+                                                            float *__restrict__ topk_w)
+{
+    static_assert(G >= 1 && G <= kWave && (kWave % G) == 0, "group must divide the wave");
+    static_assert(VPL == 1 || G == kWave, "several logits per lane only with one token per wave");
+    constexpr int kGroupsPerWave = kWave / G;
+    const int lane = lane_id();
+    const int64_t wave = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
+    const int64_t t = wave * kGroupsPerWave + lane / G;
+    const bool active = t < T;
+    float v[VPL];
+    uint32_t key[VPL];
+    load_logits<VPL, VEC>(logits, t, active, E, lane % G, v, key);
+    select_and_store<G, VPL, true>(v, key, active, t, E, k, topk_idx, topk_w);
+}
+
+// ---------------------------------------------------------------------------
+// Group-limited ("node-limited") selection.  Handbook "NVSHMEM and DeepEP",
+// "High-throughput mode": each node (here: a group of E/n_groups consecutive
+// experts) is scored by the sum of its two best expert scores (logits), only
+// the topk_groups best groups stay eligible (equal scores: the lower group),
+// and the k experts are chosen among them.  Weights are unchanged: the full
+// softmax over all E.
+//
+// One token per wave; lane l holds experts l*VPL .. l*VPL+VPL-1.  A group's
+// two best logits come from a "top-2 merge" reduction on order keys
+// ((a1 >= a2) with (b1 >= b2) -> max(a1, b1), max(min(a1, b1), max(a2, b2)),
+// the top two of the union), which commutes, so the result does not depend
+// on the reduction order.  When a group is a power-of-two run of whole lanes
+// (lanes_per_group = E/n_groups/VPL), every group is reduced at once by a
+// butterfly inside its own lanes; otherwise groups are reduced one by one
+// over the whole wave.  The score is the fp32 sum of the two values.
+
+__device__ __forceinline__ void top2_merge(uint32_t &a1, uint32_t &a2, uint32_t b1, uint32_t b2)
+{
+    const uint32_t n2 = umax(a1 < b1 ? a1 : b1, umax(a2, b2));
+    a1 = umax(a1, b1);
+    a2 = n2;
+}
+
+template <int CTRL>
+__device__ __forceinline__ void top2_dpp(uint32_t &a1, uint32_t &a2)
+{
+    top2_merge(a1, a2, dpp<CTRL>(a1), dpp<CTRL>(a2));
+}
+
+__device__ __forceinline__ void top2_xor(uint32_t &a1, uint32_t &a2, int m)
+{
+    top2_merge(a1, a2, (uint32_t)__shfl_xor((int)a1, m), (uint32_t)__shfl_xor((int)a2, m));
+}
+
+// Top two keys of a lane's eligible keys (a key of 0 is "none").
+template <int VPL>
+__device__ __forceinline__ void lane_top2(const uint32_t (&key)[VPL], uint32_t mask_bits, uint32_t &a1, uint32_t &a2)
+{
+    a1 = 0u;
+    a2 = 0u;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        const uint32_t x = ((mask_bits >> i) & 1u) ? key[i] : 0u;
+        if (x > a1) {
+            a2 = a1;
+            a1 = x;
+        } else if (x > a2) {
+            a2 = x;
+        }
+    }
+}
+
+__device__ __forceinline__ uint32_t group_score_key(uint32_t t1, uint32_t t2)
+{
+    return order_key(key_value(t1) + key_value(t2));
+}
+
+template <int VPL, bool VEC>
+__global__ __launch_bounds__(kBlock) void route_group_topk_kernel(const float *__restrict__ logits, int64_t T, int E,
+                                                                  int k, int n_groups, int topk_groups,
+                                                                  int lanes_per_group, int32_t *__restrict__ topk_idx,
+                                                                  float *__restrict__ topk_w)
+{
+    const int lane = lane_id();
+    const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
+    const bool active = t < T;
+    float v[VPL];
+    uint32_t key[VPL];
+    load_logits<VPL, VEC>(logits, t, active, E, lane, v, key);
+    const int gs = E / n_groups;
+    int eg[VPL];  // group of each of the lane's experts (n_groups: none)
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        const int e = lane * VPL + i;
+        eg[i] = e < E ? e / gs : n_groups;
+    }
+
+    // group scores: lane g < n_groups ends up with group g's score key
+    uint32_t gkey = 0u;
+    if (lanes_per_group > 0) {
+        const int L = lanes_per_group;
+        uint32_t a1, a2;
+        lane_top2<VPL>(key, 0xFFFFu, a1, a2);
+        if (L >= 2) top2_dpp<kDppQuadXor1>(a1, a2);
+        if (L >= 4) top2_dpp<kDppQuadXor2>(a1, a2);
+        if (L >= 8) top2_dpp<kDppHalfMirror>(a1, a2);
+        if (L >= 16) top2_dpp<kDppMirror>(a1, a2);
+        if (L >= 32) top2_xor(a1, a2, 16);
+        if (L >= 64) top2_xor(a1, a2, 32);
+        const uint32_t sk = group_score_key(a1, a2);
+        const int src = lane < n_groups ? lane * L : 0;
+        const uint32_t g_sk = (uint32_t)__shfl((int)sk, src);
+        gkey = lane < n_groups ? g_sk : 0u;
+    } else {
+        for (int g = 0; g < n_groups; ++g) {
+            uint32_t bits = 0u;
+#pragma unroll
+            for (int i = 0; i < VPL; ++i)
+                if (eg[i] == g)
+                    bits |= 1u << i;
+            uint32_t a1, a2;
+            lane_top2<VPL>(key, bits, a1, a2);
+            top2_dpp<kDppQuadXor1>(a1, a2);
+            top2_dpp<kDppQuadXor2>(a1, a2);
+            top2_dpp<kDppHalfMirror>(a1, a2);
+            top2_dpp<kDppMirror>(a1, a2);
+            uint32_t r1 = (uint32_t)lane_value((int)a1, 0), r2 = (uint32_t)lane_value((int)a2, 0);
+            top2_merge(r1, r2, (uint32_t)lane_value((int)a1, 16), (uint32_t)lane_value((int)a2, 16));
+            top2_merge(r1, r2, (uint32_t)lane_value((int)a1, 32), (uint32_t)lane_value((int)a2, 32));
+            top2_merge(r1, r2, (uint32_t)lane_value((int)a1, 48), (uint32_t)lane_value((int)a2, 48));
+            if (lane == g)
+                gkey = group_score_key(r1, r2);
+        }
+    }
+
+    // the topk_groups best groups (the lowest group among equal scores)
+    uint64_t kept = 0;
+    for (int m = 0; m < topk_groups; ++m) {
+        const uint32_t gm = group_max<kWave>(gkey);
+        const int g = __ffsll((unsigned long long)__ballot(gkey == gm)) - 1;
+        kept |= 1ull << g;
+        if (lane == g)
+            gkey = 0u;
+    }
+
+    // experts of the other groups are not eligible
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+        if (eg[i] < n_groups && !((kept >> eg[i]) & 1ull))
+            key[i] = 0u;
+    select_and_store<kWave, VPL, false>(v, key, active, t, E, k, topk_idx, topk_w);
 }
 
 template <int G, int VPL>
@@ -220,7 +384,40 @@ hipError_t launch(const float *logits, int64_t T, int E, int k, int32_t *idx, fl
     return hipGetLastError();
 }
 
+template <int VPL>
+hipError_t launch_grouped(const float *logits, int64_t T, int E, int k, int n_groups, int topk_groups, int32_t *idx,
+                          float *w, hipStream_t s)
+{
+    const int64_t blocks = (T + kWavesPerBlock - 1) / kWavesPerBlock;
+    const int gs = E / n_groups;
+    int lpg = 0;  // lanes per group when every group is a power-of-two run of whole lanes
+    if (gs % VPL == 0) {
+        const int L = gs / VPL;
+        if ((L & (L - 1)) == 0 && L <= kWave)
+            lpg = L;
+    }
+    const bool vec = VPL > 1 && E % VPL == 0 && (VPL == 2 ? ((uintptr_t)logits % 8 == 0)
+                                                           : (E % 4 == 0 && (uintptr_t)logits % 16 == 0));
+    if (vec)
+        hipLaunchKernelGGL((route_group_topk_kernel<VPL, true>), dim3((unsigned)blocks), dim3(kBlock), 0, s, logits,
+                           T, E, k, n_groups, topk_groups, lpg, idx, w);
+    else
+        hipLaunchKernelGGL((route_group_topk_kernel<VPL, false>), dim3((unsigned)blocks), dim3(kBlock), 0, s, logits,
+                           T, E, k, n_groups, topk_groups, lpg, idx, w);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_route_topk_grouped(const float *logits, int64_t T, int E, int k, int n_groups, int topk_groups,
+                                     int32_t *idx, float *w, hipStream_t s)
+{
+    if (E <= 64) return launch_grouped<1>(logits, T, E, k, n_groups, topk_groups, idx, w, s);
+    if (E <= 128) return launch_grouped<2>(logits, T, E, k, n_groups, topk_groups, idx, w, s);
+    if (E <= 256) return launch_grouped<4>(logits, T, E, k, n_groups, topk_groups, idx, w, s);
+    if (E <= 512) return launch_grouped<8>(logits, T, E, k, n_groups, topk_groups, idx, w, s);
+    return launch_grouped<16>(logits, T, E, k, n_groups, topk_groups, idx, w, s);
+}
 
 hipError_t launch_route_topk(const float *logits, int64_t T, int E, int k, int32_t *idx, float *w,
                              hipStream_t s)

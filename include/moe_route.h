@@ -63,6 +63,7 @@ extern "C" {
 /* Limits. */
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOPK 16
+#define MOE_MAX_GROUPS 64         /* expert groups of moe_route_topk_grouped */
 #define MOE_MAX_TOKENS (1 << 24)  /* T above this is MOE_ERR_UNSUPPORTED */
 
 /* Text for a status code (static storage, never NULL). */
@@ -91,6 +92,31 @@ MOE_API const char *moe_status_string(int status);
  */
 MOE_API int moe_route_topk(const float *logits, int64_t T, int32_t E, int32_t k,
                            int32_t *topk_idx, float *topk_w, hipStream_t stream);
+
+/*
+ * moe_route_topk_grouped -- group-limited ("node-limited") router top-k.
+ *
+ * Handbook "NVSHMEM and DeepEP", "High-throughput mode": DeepSeek-V3 sends a
+ * token to at most a few nodes; every node is scored by the sum of its two
+ * best expert scores, only the best nodes are eligible, and the top experts
+ * are then chosen among those nodes' experts.  Here a node is a group of
+ * E / n_groups consecutive experts and an expert's score is its logit.
+ *
+ *   logits, T, E, k, topk_idx, topk_w, stream: as for moe_route_topk
+ *   n_groups     groups, 1 <= n_groups <= MOE_MAX_GROUPS, E % n_groups == 0
+ *                and E / n_groups >= 2
+ *   topk_groups  eligible groups per token, 1 <= topk_groups <= n_groups,
+ *                with topk_groups * (E / n_groups) >= k
+ * Per token: a group's score is the fp32 sum of its two largest logits (a
+ * repeated largest value counts twice); the topk_groups groups with the
+ * largest scores are kept, equal scores ordered by ascending group index;
+ * topk_idx holds the k largest logits among the kept groups' experts,
+ * ordered as in moe_route_topk.  topk_w is unchanged by the limit: the full
+ * softmax over all E logits at each chosen expert.  With topk_groups ==
+ * n_groups the result equals moe_route_topk's.
+ */
+MOE_API int moe_route_topk_grouped(const float *logits, int64_t T, int32_t E, int32_t k, int32_t n_groups,
+                                   int32_t topk_groups, int32_t *topk_idx, float *topk_w, hipStream_t stream);
 
 /*
  * Bytes of device workspace moe_dispatch needs for T tokens and E experts

@@ -32,8 +32,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     names = _declared()
-    for n in ("moe_route_topk", "moe_dispatch", "moe_combine", "moe_dispatch_workspace_bytes",
-              "moe_status_string"):
+    for n in ("moe_route_topk", "moe_route_topk_grouped", "moe_dispatch", "moe_combine",
+              "moe_dispatch_workspace_bytes", "moe_status_string"):
         assert n in names
 
 
@@ -77,6 +77,16 @@ def test_host_validation_without_device(lib):
     assert lib.moe_route_topk(P, 4, 64, 17, P, P, P) == -2
     assert lib.moe_route_topk(P, 4, 8, 2, P, P, P) == -1          # null pointers
     assert lib.moe_route_topk(P, 0, 8, 2, P, P, P) == 0           # empty: nothing to do
+    g = lib.moe_route_topk_grouped
+    assert g(P, 4, 256, 8, 8, 4, P, P, P) == -1                     # null pointers
+    assert g(P, 0, 256, 8, 8, 4, P, P, P) == 0                      # empty
+    assert g(P, 4, 256, 8, 3, 2, P, P, P) == -1                     # E % n_groups
+    assert g(P, 4, 256, 8, 256, 4, P, P, P) == -1                   # groups of one expert
+    assert g(P, 4, 256, 8, 8, 0, P, P, P) == -1                     # no group kept
+    assert g(P, 4, 256, 8, 8, 9, P, P, P) == -1                     # more kept than groups
+    assert g(P, 4, 256, 8, 64, 1, P, P, P) == -1                    # k above the kept experts (1 x 4)
+    assert g(P, 4, 1024, 8, 128, 8, P, P, P) == -2                  # more than MOE_MAX_GROUPS groups
+    assert g(P, 4, 256, 0, 8, 4, P, P, P) == -1                     # k = 0
     assert lib.moe_combine(P, 8, 4, 64, P, P, -1, 2, P, P) == -1
     assert lib.moe_combine(P, 8, 4, 60, P, P, 4, 2, P, P) == -2
     assert lib.moe_combine(P, 8, 4, 64, P, P, 4, 17, P, P) == -2
