@@ -58,6 +58,8 @@ def _load():
     lib.oracle_route_topk_grouped.restype = ctypes.c_int
     lib.oracle_assign_slots.argtypes = [P, i64, i32, i32, i32, P, P, P]
     lib.oracle_assign_slots.restype = ctypes.c_int
+    lib.oracle_assign_packed.argtypes = [P, i64, i32, i32, P, P, P]
+    lib.oracle_assign_packed.restype = ctypes.c_int
     lib.oracle_quantize_row_fp8.argtypes = [P, i32, P, P]
     lib.oracle_quantize_row_fp8.restype = ctypes.c_int
     lib.oracle_filled_rows.argtypes = [P, i32, i32]
@@ -133,6 +135,20 @@ def assign_slots(idx: np.ndarray, E: int, capacity: int):
     _check(_load().oracle_assign_slots(_ptr(idx), T, E, k, capacity, _ptr(counts),
                                        _ptr(token_slot), _ptr(recv_src)), "assign_slots")
     return counts, token_slot, recv_src
+
+
+def assign_packed(idx: np.ndarray, E: int):
+    """Packed, count-sized layout: expert e's rows are offsets[e] ..
+    offsets[e+1]-1, in ascending token order.  Returns (offsets int32 [E+1],
+    token_slot int32 [T,k] (row of each pair), recv_src int32 [T*k])."""
+    idx = _c(idx, np.int32)
+    T, k = idx.shape
+    offsets = np.empty(E + 1, np.int32)
+    token_slot = np.empty((T, k), np.int32)
+    recv_src = np.empty(T * k, np.int32)
+    _check(_load().oracle_assign_packed(_ptr(idx), T, E, k, _ptr(offsets), _ptr(token_slot), _ptr(recv_src)),
+           "assign_packed")
+    return offsets, token_slot, recv_src
 
 
 def quantize_row_fp8(x_row_bits: np.ndarray):

@@ -307,6 +307,57 @@ int oracle_assign_slots(const int32_t *idx, int64_t T, int32_t E, int32_t k,
     return 0;
 }
 
+/* Packed, count-sized layout.  [HBK] "High-throughput mode": the number of
+ * tokens bound for each destination is computed first and the receive
+ * buffer is sized by it.  [PPLX] Dispatch: each expert's tokens are
+ * contiguous for the grouped GEMM.  Here every expert's rows follow the
+ * previous expert's, with no reserved slack:
+ *   offsets[e]   pairs routed to experts 0 .. e-1 (exclusive prefix of the
+ *                per-expert counts); offsets[E] = T*k
+ *   token_slot[t][j] = offsets[e] + r, where (t, j) is the r-th pair routed
+ *                to e = idx[t][j] in ascending token order
+ *   recv_src[row] = t for every row 0 .. T*k-1
+ * Inputs: idx[T][k] (each row k distinct experts in [0, E)). */
+int oracle_assign_packed(const int32_t *idx, int64_t T, int32_t E, int32_t k, int32_t *offsets,
+                         int32_t *token_slot, int32_t *recv_src)
+{
+    if (T < 0 || E < 1 || k < 1 || k > E || !offsets || (T > 0 && (!idx || !token_slot || !recv_src)))
+        return -1;
+    int64_t *count = (int64_t *)calloc((size_t)E, sizeof(int64_t));
+    int64_t *fill = (int64_t *)calloc((size_t)E, sizeof(int64_t));
+    if (!count || !fill) {
+        free(count);
+        free(fill);
+        return -1;
+    }
+    for (int64_t p = 0; p < T * k; ++p) {
+        const int32_t e = idx[p];
+        if (e < 0 || e >= E) {
+            free(count);
+            free(fill);
+            return -1;
+        }
+        ++count[e];
+    }
+    int64_t run = 0;
+    for (int32_t e = 0; e < E; ++e) {
+        offsets[e] = (int32_t)run;
+        run += count[e];
+    }
+    offsets[E] = (int32_t)run;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t j = 0; j < k; ++j) {
+            const int32_t e = idx[t * k + j];
+            const int64_t row = offsets[e] + fill[e]++;
+            token_slot[t * k + j] = (int32_t)row;
+            recv_src[row] = (int32_t)t;
+        }
+    }
+    free(count);
+    free(fill);
+    return 0;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Dispatch, step 3: packing rows                                            */
 /* [HBK] "High-throughput mode": FP8 for dispatch with one scale per 128     */
