@@ -2,8 +2,9 @@
 """Benchmark of the MoE token routing/dispatch/combine path on one MI355X.
 
 One step = moe_route_topk (or moe_route_topk_grouped with --route-groups) +
-moe_dispatch + moe_combine, back to back on one stream, over one batch of
-seeded synthetic input already resident in HBM.
+moe_dispatch (or moe_dispatch_packed with --layout packed) + moe_combine,
+back to back on one stream, over one batch of seeded synthetic input already
+resident in HBM.
 W untimed warm-up steps, then exactly K timed steps between device
 synchronisations.  Prints one JSON line (stdout):
 
@@ -131,13 +132,17 @@ def cpu_baseline(w: W.Workload, seconds: float) -> dict:
 class BufferSet:
     """One complete copy of a step's inputs, outputs and fixed-slot buffers."""
 
-    def __init__(self, w: W.Workload, logits_cpu, x_cpu, dev, moe, torch, route_groups=None):
+    def __init__(self, w: W.Workload, logits_cpu, x_cpu, dev, moe, torch, route_groups=None, packed=False):
         self.logits = logits_cpu.to(dev)
         self.x = x_cpu.to(dev)
         self.idx = torch.empty(w.T, w.k, dtype=torch.int32, device=dev)
         self.wt = torch.empty(w.T, w.k, dtype=torch.float32, device=dev)
-        self.bufs = moe.DispatchBuffers.allocate(w.T, w.H, w.E, w.k, w.C, w.fp8, dev)
-        self.y = torch.empty(w.E, w.C, w.H, dtype=torch.bfloat16, device=dev)
+        if packed:
+            self.bufs = moe.PackedBuffers.allocate(w.T, w.H, w.E, w.k, w.fp8, dev)
+            self.y = torch.empty(w.T * w.k, w.H, dtype=torch.bfloat16, device=dev)
+        else:
+            self.bufs = moe.DispatchBuffers.allocate(w.T, w.H, w.E, w.k, w.C, w.fp8, dev)
+            self.y = torch.empty(w.E, w.C, w.H, dtype=torch.bfloat16, device=dev)
         self.out = torch.empty(w.T, w.H, dtype=torch.bfloat16, device=dev)
         self.step = moe.PreparedStep(self.logits, w.k, self.x, w.C, w.fp8, self.bufs, self.y, self.out,
                                      self.idx, self.wt, route_groups=route_groups)
@@ -166,6 +171,9 @@ def main() -> int:
                     help="combine launch timing: events attached to the launch (ext) or recorded around it")
     ap.add_argument("--no-overlap", action="store_true",
                     help="skip the extra two-batches-in-flight measurement")
+    ap.add_argument("--layout", choices=["fixed", "packed"], default="fixed",
+                    help="dispatch layout: fixed slots per expert (moe_dispatch) or packed count-sized rows "
+                         "(moe_dispatch_packed)")
     ap.add_argument("--route-groups", default="",
                     help="G:M routes with moe_route_topk_grouped (G expert groups, the best M kept)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -194,7 +202,8 @@ def main() -> int:
     logits_cpu = W.make_logits(w)
     x_cpu = W.make_x(w)
     route_groups = tuple(int(v) for v in args.route_groups.split(":")) if args.route_groups else None
-    sets = [BufferSet(w, logits_cpu, x_cpu, dev, moe, torch, route_groups) for _ in range(R)]
+    packed = args.layout == "packed"
+    sets = [BufferSet(w, logits_cpu, x_cpu, dev, moe, torch, route_groups, packed) for _ in range(R)]
     gen = torch.Generator(device=dev)
     gen.manual_seed(w.seed * 16 + 3)
     for s in sets:
@@ -313,6 +322,7 @@ def main() -> int:
             "workload": w.name, "tokens": w.T, "hidden": w.H, "experts": w.E, "top_k": w.k, "capacity": w.C,
             "row_dtype": "fp8-e4m3+fp32/128" if w.fp8 else "bf16", "routing": w.routing,
             "route_groups": ({"groups": route_groups[0], "kept": route_groups[1]} if route_groups else None),
+            "layout": "packed count-sized rows" if packed else "fixed slots per expert",
             "parallelism": "none (1 GPU)",
             "algorithmic_bytes_per_step": nbytes["total"],
             "effective_hbm_gbps": gbps,
@@ -330,7 +340,7 @@ def main() -> int:
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": comb_gbps / HBM_PEAK_GBPS,
-            "traffic": measured_traffic(w),
+            "traffic": None if packed else measured_traffic(w),
             "traffic_source": f"profiles/{w.name}_hbm_traffic.md (bytes per launch)",
             "algorithmic_bytes_per_launch": nbytes["combine"],
             "mean_launch_us": combine_ms * 1e3,

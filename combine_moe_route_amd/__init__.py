@@ -12,10 +12,12 @@ from .binding import (  # noqa: F401
     DispatchBuffers,
     HipEvents,
     MoeError,
+    PackedBuffers,
     PreparedStep,
     load,
     moe_combine,
     moe_dispatch,
+    moe_dispatch_packed,
     moe_dispatch_workspace_bytes,
     moe_route_topk,
     moe_route_topk_grouped,

@@ -55,6 +55,8 @@ def load() -> ctypes.CDLL:
     lib.moe_dispatch_workspace_bytes.restype = ctypes.c_size_t
     lib.moe_dispatch.argtypes = [P, i64, i32, P, i32, i32, i32, i32, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.moe_dispatch.restype = ctypes.c_int
+    lib.moe_dispatch_packed.argtypes = [P, i64, i32, P, i32, i32, i32, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.moe_dispatch_packed.restype = ctypes.c_int
     lib.moe_combine.argtypes = [P, i32, i32, i32, P, P, i64, i32, P, P]
     lib.moe_combine.restype = ctypes.c_int
     lib.moe_combine_timed.argtypes = [P, i32, i32, i32, P, P, i64, i32, P, P, P, P]
@@ -232,10 +234,71 @@ def moe_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: int, capa
     return bufs
 
 
+@dataclass
+class PackedBuffers:
+    """Outputs of moe_dispatch_packed (all device tensors)."""
+    recv_x: torch.Tensor          # bf16 [T*k, H] or uint8 [T*k, H] (E4M3 codes)
+    recv_scales: torch.Tensor | None  # float32 [T*k, H/128] for fp8
+    recv_src: torch.Tensor        # int32 [T*k]
+    expert_offsets: torch.Tensor  # int32 [E+1]
+    token_slot: torch.Tensor      # int32 [T, k]
+    workspace: torch.Tensor       # uint8 scratch
+
+    @staticmethod
+    def allocate(T: int, H: int, E: int, k: int, fp8: bool, device) -> "PackedBuffers":
+        n = T * k
+        if fp8:
+            recv_x = torch.empty(n, H, dtype=torch.uint8, device=device)
+            recv_scales = torch.empty(n, H // 128, dtype=torch.float32, device=device)
+        else:
+            recv_x = torch.empty(n, H, dtype=torch.bfloat16, device=device)
+            recv_scales = None
+        ws = moe_dispatch_workspace_bytes(T, E, k)
+        return PackedBuffers(
+            recv_x=recv_x, recv_scales=recv_scales,
+            recv_src=torch.empty(max(n, 1), dtype=torch.int32, device=device),
+            expert_offsets=torch.empty(E + 1, dtype=torch.int32, device=device),
+            token_slot=torch.empty(T, k, dtype=torch.int32, device=device),
+            workspace=torch.empty(max(ws, 256), dtype=torch.uint8, device=device),
+        )
+
+
+def moe_dispatch_packed(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: int, fp8: bool = False,
+                        bufs: PackedBuffers | None = None, stream=None) -> PackedBuffers:
+    """Counts, packed count-sized rows (expert e at expert_offsets[e] ..
+    expert_offsets[e+1]-1, ascending token order) and packed row contents."""
+    T, H = x.shape
+    k = topk_idx.shape[1]
+    E = num_experts
+    _need(x, torch.bfloat16, (T, H), "x")
+    _need(topk_idx, torch.int32, (T, k), "topk_idx")
+    if bufs is None:
+        bufs = PackedBuffers.allocate(T, H, E, k, fp8, x.device)
+    _need(bufs.recv_x, torch.uint8 if fp8 else torch.bfloat16, (T * k, H), "recv_x")
+    if fp8:
+        _need(bufs.recv_scales, torch.float32, (T * k, H // 128), "recv_scales")
+    if bufs.recv_src.numel() < T * k:
+        raise ValueError("recv_src needs T*k entries")
+    _need(bufs.expert_offsets, torch.int32, (E + 1,), "expert_offsets")
+    _need(bufs.token_slot, torch.int32, (T, k), "token_slot")
+    rc = load().moe_dispatch_packed(
+        _ptr(x), T, H, _ptr(topk_idx), E, k, MOE_DTYPE_FP8_E4M3 if fp8 else MOE_DTYPE_BF16,
+        _ptr(bufs.recv_x), _ptr(bufs.recv_scales) if fp8 else None, _ptr(bufs.recv_src),
+        _ptr(bufs.expert_offsets), _ptr(bufs.token_slot), _ptr(bufs.workspace), bufs.workspace.numel(),
+        _stream(stream))
+    if rc != MOE_OK:
+        raise MoeError("moe_dispatch_packed", rc)
+    return bufs
+
+
 def moe_combine(y: torch.Tensor, token_slot: torch.Tensor, topk_w: torch.Tensor, out: torch.Tensor | None = None,
                 stream=None, events: tuple[int, int] | None = None) -> torch.Tensor:
     """out[t] = bf16(sum_j w[t,j] * y[token_slot[t,j]]), fp32 FMA in top-k order.
-    `events` = (start, stop) raw hipEvent_t handles selects moe_combine_timed."""
+    y is [E, C, H] (fixed slots) or [rows, H] (packed layout: one expert
+    with `rows` slots).  `events` = (start, stop) raw hipEvent_t handles
+    selects moe_combine_timed."""
+    if y.dim() == 2:
+        y = y.view(1, max(1, y.shape[0]), y.shape[1]) if y.shape[0] else y.new_empty(1, 1, y.shape[1])
     E, C, H = y.shape
     T, k = token_slot.shape
     _need(y, torch.bfloat16, (E, C, H), "y")
@@ -256,6 +319,8 @@ def moe_combine(y: torch.Tensor, token_slot: torch.Tensor, topk_w: torch.Tensor,
 
 class PreparedStep:
     """Route, dispatch and combine with their arguments marshalled once.
+    `bufs` selects the layout: DispatchBuffers (fixed slots; y [E, C, H]) or
+    PackedBuffers (packed rows; y [T*k, H]).
 
     For callers that repeat the same three calls on the same buffers (a
     layer's fixed, reused buffers, or a benchmark loop): each call is then a
@@ -274,9 +339,14 @@ class PreparedStep:
         _need(x, torch.bfloat16, (T, H), "x")
         _need(topk_idx, torch.int32, (T, k), "topk_idx")
         _need(topk_w, torch.float32, (T, k), "topk_w")
-        _need(bufs.recv_x, torch.uint8 if fp8 else torch.bfloat16, (E, capacity, H), "recv_x")
+        packed = isinstance(bufs, PackedBuffers)
+        if packed:
+            _need(bufs.recv_x, torch.uint8 if fp8 else torch.bfloat16, (T * k, H), "recv_x")
+            _need(y, torch.bfloat16, (T * k, H), "y")
+        else:
+            _need(bufs.recv_x, torch.uint8 if fp8 else torch.bfloat16, (E, capacity, H), "recv_x")
+            _need(y, torch.bfloat16, (E, capacity, H), "y")
         _need(bufs.token_slot, torch.int32, (T, k), "token_slot")
-        _need(y, torch.bfloat16, (E, capacity, H), "y")
         _need(out, torch.bfloat16, (T, H), "out")
         self._lib = load()
         s = _stream(stream)
@@ -287,11 +357,22 @@ class PreparedStep:
             self._route_fn, self._route_name = self._lib.moe_route_topk_grouped, "moe_route_topk_grouped"
             self.route_args = (_ptr(logits), T, E, k, int(route_groups[0]), int(route_groups[1]), _ptr(topk_idx),
                                _ptr(topk_w), s)
-        self.dispatch_args = (
-            _ptr(x), T, H, _ptr(topk_idx), E, k, capacity, MOE_DTYPE_FP8_E4M3 if fp8 else MOE_DTYPE_BF16,
-            _ptr(bufs.recv_x), _ptr(bufs.recv_scales) if fp8 else None, _ptr(bufs.recv_src),
-            _ptr(bufs.expert_counts), _ptr(bufs.token_slot), _ptr(bufs.workspace), bufs.workspace.numel(), s)
-        self.combine_args = (_ptr(y), E, capacity, H, _ptr(bufs.token_slot), _ptr(topk_w), T, k, _ptr(out), s)
+        dt = MOE_DTYPE_FP8_E4M3 if fp8 else MOE_DTYPE_BF16
+        scales = _ptr(bufs.recv_scales) if fp8 else None
+        if packed:
+            self._dispatch_fn, self._dispatch_name = self._lib.moe_dispatch_packed, "moe_dispatch_packed"
+            self.dispatch_args = (
+                _ptr(x), T, H, _ptr(topk_idx), E, k, dt, _ptr(bufs.recv_x), scales, _ptr(bufs.recv_src),
+                _ptr(bufs.expert_offsets), _ptr(bufs.token_slot), _ptr(bufs.workspace), bufs.workspace.numel(), s)
+            # combine reads the packed rows as one expert with T*k slots
+            self.combine_args = (_ptr(y), 1, max(1, T * k), H, _ptr(bufs.token_slot), _ptr(topk_w), T, k,
+                                 _ptr(out), s)
+        else:
+            self._dispatch_fn, self._dispatch_name = self._lib.moe_dispatch, "moe_dispatch"
+            self.dispatch_args = (
+                _ptr(x), T, H, _ptr(topk_idx), E, k, capacity, dt, _ptr(bufs.recv_x), scales, _ptr(bufs.recv_src),
+                _ptr(bufs.expert_counts), _ptr(bufs.token_slot), _ptr(bufs.workspace), bufs.workspace.numel(), s)
+            self.combine_args = (_ptr(y), E, capacity, H, _ptr(bufs.token_slot), _ptr(topk_w), T, k, _ptr(out), s)
         self._keep = (logits, x, bufs, y, out, topk_idx, topk_w)
 
     def route(self):
@@ -300,9 +381,9 @@ class PreparedStep:
             raise MoeError(self._route_name, rc)
 
     def dispatch(self):
-        rc = self._lib.moe_dispatch(*self.dispatch_args)
+        rc = self._dispatch_fn(*self.dispatch_args)
         if rc != MOE_OK:
-            raise MoeError("moe_dispatch", rc)
+            raise MoeError(self._dispatch_name, rc)
 
     def combine(self):
         rc = self._lib.moe_combine(*self.combine_args)

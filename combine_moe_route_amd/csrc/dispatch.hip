@@ -24,6 +24,12 @@
 //           records token_slot and recv_src; then the row is stored to
 //           each slot -- bf16 bit copies, or E4M3 codes with per-128 fp32
 //           scales.  The first E waves also write the true totals.
+// Packed, count-sized layout (handbook "High-throughput mode": count first,
+// then a receive buffer of exactly the needed size): between count and
+// pack, one work-group sums each expert's chunk counts and scans them into
+// offsets[E+1] (with a single chunk the count work-group does it itself);
+// pack then uses slot = offsets[e] + offset + rank, with no capacity and
+// nothing dropped.
 // Slot rows are written with non-temporal stores: each byte is written once
 // per call.
 #include "device_common.hpp"
@@ -35,12 +41,53 @@ namespace {
 constexpr int kChunk = 256;          // tokens per K1 work-group (one bit each)
 constexpr int kMaskWords = kChunk / 32;
 
+// Exclusive scan of the work-group's n <= 4*256 values in LDS (thread i owns
+// values 4i .. 4i+3): out[i] = sum of in[0 .. i-1] for i < n, out[n] = total.
+__device__ __forceinline__ void block_exclusive_scan(const int32_t *in, int n, int32_t *__restrict__ out,
+                                                     int32_t *wave_sums)
+{
+    const int tid = threadIdx.x;
+    const int lane = lane_id();
+    const int wv = tid / kWave;
+    int v[4];
+    int own = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        v[u] = 4 * tid + u < n ? in[4 * tid + u] : 0;
+        own += v[u];
+    }
+    int incl = own;
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int up = __shfl_up(incl, o);
+        if (lane >= o)
+            incl += up;
+    }
+    if (lane == kWave - 1)
+        wave_sums[wv] = incl;
+    __syncthreads();
+    int run = incl - own;
+    for (int w = 0; w < wv; ++w)
+        run += wave_sums[w];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        if (4 * tid + u < n)
+            out[4 * tid + u] = run;
+        run += v[u];
+        if (4 * tid + u == n - 1)
+            out[n] = run;
+    }
+}
+
+// offsets != NULL and a single chunk: the work-group holds every count, so
+// it also writes the packed layout's offsets (no separate scan launch).
 __global__ __launch_bounds__(kBlock) void dispatch_count_kernel(const int32_t *__restrict__ topk_idx, int64_t T,
                                                                 int E, int k, int nchunks,
                                                                 int32_t *__restrict__ chunk_counts,
-                                                                int32_t *__restrict__ local_rank)
+                                                                int32_t *__restrict__ local_rank,
+                                                                int32_t *__restrict__ offsets)
 {
-    extern __shared__ uint32_t mask[];  // [E][kMaskWords]
+    extern __shared__ uint32_t mask[];  // [E][kMaskWords], then [E] counts when writing offsets
+    __shared__ int32_t wave_sums[kWavesPerBlock];
     const int tid = threadIdx.x;
     const int c = blockIdx.x;
     for (int i = tid; i < E * kMaskWords; i += kBlock)
@@ -59,12 +106,19 @@ __global__ __launch_bounds__(kBlock) void dispatch_count_kernel(const int32_t *_
     }
     __syncthreads();
 
+    int32_t *counts_lds = (int32_t *)(mask + E * kMaskWords);
     for (int e = tid; e < E; e += kBlock) {
         int n = 0;
 #pragma unroll
         for (int w = 0; w < kMaskWords; ++w)
             n += __popc(mask[e * kMaskWords + w]);
         chunk_counts[(int64_t)e * nchunks + c] = n;
+        if (offsets)
+            counts_lds[e] = n;
+    }
+    if (offsets) {      // block-uniform: only launched so with one chunk
+        __syncthreads();
+        block_exclusive_scan(counts_lds, E, offsets, wave_sums);
     }
 
     if (t < T) {
@@ -81,11 +135,75 @@ __global__ __launch_bounds__(kBlock) void dispatch_count_kernel(const int32_t *_
     }
 }
 
-// T = 0: nothing routed, every count is zero.
+// T = 0: nothing routed, every count (or offset) is zero.
 __global__ __launch_bounds__(kBlock) void dispatch_zero_counts_kernel(int32_t *__restrict__ expert_counts, int E)
 {
     for (int e = blockIdx.x * kBlock + threadIdx.x; e < E; e += gridDim.x * kBlock)
         expert_counts[e] = 0;
+}
+
+constexpr int kScanBlock = 1024;                      // >= the largest E
+constexpr int kScanWaves = kScanBlock / kWave;
+
+// Packed layout: offsets[e] = sum of the counts of experts below e, and
+// offsets[E] = the total, from the [E][nchunks] chunk histograms.  One
+// work-group: `tpe` consecutive threads (a power of two <= 64) total one
+// expert's row, each summing every tpe-th chunk with eight loads in flight,
+// then a butterfly; then a work-group exclusive scan over the E totals (wave
+// scans, then the wave sums).
+__global__ __launch_bounds__(kScanBlock) void dispatch_offsets_kernel(const int32_t *__restrict__ chunk_counts,
+                                                                      int E, int nchunks,
+                                                                      int32_t *__restrict__ offsets)
+{
+    __shared__ int32_t total[kScanBlock];
+    __shared__ int32_t wave_sum[kScanWaves];
+    const int lane = lane_id();
+    const int wv = threadIdx.x / kWave;
+    int tpe = kWave;
+    while (tpe > 1 && tpe * E > kScanBlock)
+        tpe >>= 1;
+    const int per_pass = kScanBlock / tpe;
+    const int sub = threadIdx.x % tpe;
+    for (int e0 = 0; e0 < E; e0 += per_pass) {
+        const int e = e0 + (int)threadIdx.x / tpe;
+        int sum = 0;
+        if (e < E) {
+            const int32_t *row = chunk_counts + (int64_t)e * nchunks;
+            for (int cc = sub; cc < nchunks; cc += 8 * tpe) {
+                int part[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    part[u] = cc + u * tpe < nchunks ? row[cc + u * tpe] : 0;
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    sum += part[u];
+            }
+        }
+        for (int o = tpe / 2; o > 0; o >>= 1)
+            sum += __shfl_xor(sum, o);
+        if (sub == 0 && e < E)
+            total[e] = sum;
+    }
+    __syncthreads();
+    const int tid = threadIdx.x;
+    const int v = tid < E ? total[tid] : 0;
+    int incl = v;
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int up = __shfl_up(incl, o);
+        if (lane >= o)
+            incl += up;
+    }
+    if (lane == kWave - 1)
+        wave_sum[wv] = incl;
+    __syncthreads();
+    int base = 0;
+    for (int w = 0; w < wv; ++w)
+        base += wave_sum[w];
+    const int excl = base + incl - v;
+    if (tid < E)
+        offsets[tid] = excl;
+    if (tid == E - 1)
+        offsets[E] = excl + v;
 }
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -101,21 +219,25 @@ __device__ __forceinline__ void store_stream(float *p, float v) { __builtin_nont
 // in-chunk rank, and sum the expert's counts over all earlier 256-token
 // chunks (the exclusive prefix, read from the L2-resident chunk histograms
 // with up to 8 independent loads per lane in flight), then a butterfly
-// within the L lanes.  slot = e*C + prefix + rank, or -1 when that is >= C
-// or the id is out of range.  The value is valid in lane j*L.
+// within the L lanes.  Fixed slots (offs == NULL): slot = e*C + prefix +
+// rank, or -1 when that is >= C.  Packed (offs != NULL): slot = offs[e] +
+// prefix + rank.  -1 for an id out of range.  The value is valid in lane
+// j*L.
 __device__ __forceinline__ int wave_slot(const int32_t *__restrict__ topk_idx, const int32_t *__restrict__ local_rank,
-                                         const int32_t *__restrict__ chunk_counts, int64_t t, int E, int k, int C,
-                                         int nchunks, int lanes_per_pair)
+                                         const int32_t *__restrict__ chunk_counts, const int32_t *__restrict__ offs,
+                                         int64_t t, int E, int k, int C, int nchunks, int lanes_per_pair)
 {
     const int lane = lane_id();
     const int j = lane / lanes_per_pair;
     const int sub = lane - j * lanes_per_pair;
     const int c = (int)(t / kChunk);
-    int e = -1, r = -1, sum = 0;
+    int e = -1, r = -1, sum = 0, base = 0;
     if (j < k) {
         e = topk_idx[t * k + j];
         r = local_rank[t * k + j];
         if ((unsigned)e < (unsigned)E) {
+            if (offs)
+                base = offs[e];
             const int32_t *row = chunk_counts + (int64_t)e * nchunks;
             for (int base = sub; base < c; base += 8 * lanes_per_pair) {
                 int part[8];
@@ -133,8 +255,12 @@ __device__ __forceinline__ int wave_slot(const int32_t *__restrict__ topk_idx, c
     for (int o = lanes_per_pair / 2; o > 0; o >>= 1)
         sum += __shfl_xor(sum, o);
     int slot = -1;
-    if (j < k && (unsigned)e < (unsigned)E && r >= 0 && (int64_t)sum + r < C)
-        slot = (int)((int64_t)e * C + sum + r);
+    if (j < k && (unsigned)e < (unsigned)E && r >= 0) {
+        if (offs)
+            slot = base + sum + r;
+        else if ((int64_t)sum + r < C)
+            slot = (int)((int64_t)e * C + sum + r);
+    }
     return slot;
 }
 
@@ -178,9 +304,10 @@ constexpr int kMaxV = 16;  // most 16-byte vectors per lane in flight (bf16 rows
 template <int VPL>
 __global__ __launch_bounds__(kBlock) void dispatch_pack_bf16_kernel(
     const u32x4 *__restrict__ x, int64_t T, int nvec, const int32_t *__restrict__ topk_idx,
-    const int32_t *__restrict__ local_rank, const int32_t *__restrict__ chunk_counts, int E, int k, int C,
-    int nchunks, int lanes_per_pair, int segs, int32_t *__restrict__ token_slot,
-    int32_t *__restrict__ recv_src, int32_t *__restrict__ expert_counts, u32x4 *__restrict__ recv_x)
+    const int32_t *__restrict__ local_rank, const int32_t *__restrict__ chunk_counts,
+    const int32_t *__restrict__ offs, int E, int k, int C, int nchunks, int lanes_per_pair, int segs,
+    int32_t *__restrict__ token_slot, int32_t *__restrict__ recv_src, int32_t *__restrict__ expert_counts,
+    u32x4 *__restrict__ recv_x)
 {
     const int lane = lane_id();
     const int64_t task = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
@@ -195,10 +322,10 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_bf16_kernel(
     for (int i = 0; i < VPL; ++i)
         buf[i] = v0 + i * kWave < nvec ? src[v0 + i * kWave] : (u32x4){0, 0, 0, 0};
 
-    const int slot = wave_slot(topk_idx, local_rank, chunk_counts, t, E, k, C, nchunks, lanes_per_pair);
+    const int slot = wave_slot(topk_idx, local_rank, chunk_counts, offs, t, E, k, C, nchunks, lanes_per_pair);
     if (seg == 0)
         record_slot(slot, t, k, lanes_per_pair, token_slot, recv_src);
-    if (task < E)
+    if (task < E && expert_counts)
         wave_totals(task, T * segs, chunk_counts, E, nchunks, expert_counts);
 
 #pragma unroll 1
@@ -270,10 +397,10 @@ constexpr int kMaxG = 8;   // most 16-element groups per lane in flight (fp8 row
 template <int VPL>
 __global__ __launch_bounds__(kBlock) void dispatch_pack_fp8_kernel(
     const u32x4 *__restrict__ x, int64_t T, int ngrp, const int32_t *__restrict__ topk_idx,
-    const int32_t *__restrict__ local_rank, const int32_t *__restrict__ chunk_counts, int E, int k, int C,
-    int nchunks, int lanes_per_pair, int segs, int32_t *__restrict__ token_slot,
-    int32_t *__restrict__ recv_src, int32_t *__restrict__ expert_counts, u32x4 *__restrict__ recv_x,
-    float *__restrict__ recv_scales)
+    const int32_t *__restrict__ local_rank, const int32_t *__restrict__ chunk_counts,
+    const int32_t *__restrict__ offs, int E, int k, int C, int nchunks, int lanes_per_pair, int segs,
+    int32_t *__restrict__ token_slot, int32_t *__restrict__ recv_src, int32_t *__restrict__ expert_counts,
+    u32x4 *__restrict__ recv_x, float *__restrict__ recv_scales)
 {
     // the wave's block scales, staged so each slot's scale segment is
     // written by one contiguous store instruction
@@ -298,10 +425,10 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_fp8_kernel(
         }
     }
 
-    const int slot = wave_slot(topk_idx, local_rank, chunk_counts, t, E, k, C, nchunks, lanes_per_pair);
+    const int slot = wave_slot(topk_idx, local_rank, chunk_counts, offs, t, E, k, C, nchunks, lanes_per_pair);
     if (seg == 0)
         record_slot(slot, t, k, lanes_per_pair, token_slot, recv_src);
-    if (task < E)
+    if (task < E && expert_counts)
         wave_totals(task, T * segs, chunk_counts, E, nchunks, expert_counts);
 
 #pragma unroll
@@ -387,11 +514,13 @@ size_t dispatch_workspace_bytes(int64_t T, int E, int k)
 
 hipError_t launch_dispatch(const uint16_t *x, int64_t T, int H, const int32_t *topk_idx, int E, int k, int C,
                            int dtype, void *recv_x, float *recv_scales, int32_t *recv_src,
-                           int32_t *expert_counts, int32_t *token_slot, void *workspace, hipStream_t s)
+                           int32_t *expert_counts, int32_t *expert_offsets, int32_t *token_slot, void *workspace,
+                           hipStream_t s)
 {
     if (T == 0) {
-        hipLaunchKernelGGL(dispatch_zero_counts_kernel, dim3((E + kBlock - 1) / kBlock), dim3(kBlock), 0, s,
-                           expert_counts, E);
+        int32_t *zero = expert_offsets ? expert_offsets : expert_counts;
+        const int n = expert_offsets ? E + 1 : E;
+        hipLaunchKernelGGL(dispatch_zero_counts_kernel, dim3((n + kBlock - 1) / kBlock), dim3(kBlock), 0, s, zero, n);
         return hipGetLastError();
     }
     const int nchunks = (int)((T + kChunk - 1) / kChunk);
@@ -399,8 +528,16 @@ hipError_t launch_dispatch(const uint16_t *x, int64_t T, int H, const int32_t *t
     int32_t *local_rank =
         (int32_t *)((char *)workspace + ((int64_t)E * nchunks * 4 + 255) / 256 * 256);
 
-    hipLaunchKernelGGL(dispatch_count_kernel, dim3(nchunks), dim3(kBlock), (size_t)E * kMaskWords * 4, s, topk_idx,
-                       T, E, k, nchunks, chunk_counts, local_rank);
+    // packed layout: one chunk -> the count work-group scans the offsets;
+    // several -> one more work-group totals the chunks and scans
+    const bool scan_in_count = expert_offsets && nchunks == 1;
+    hipLaunchKernelGGL(dispatch_count_kernel, dim3(nchunks), dim3(kBlock),
+                       (size_t)E * (kMaskWords + (scan_in_count ? 1 : 0)) * 4, s, topk_idx, T, E, k, nchunks,
+                       chunk_counts, local_rank, scan_in_count ? expert_offsets : nullptr);
+    if (expert_offsets && !scan_in_count)
+        hipLaunchKernelGGL(dispatch_offsets_kernel, dim3(1), dim3(kScanBlock), 0, s, chunk_counts, E, nchunks,
+                           expert_offsets);
+    const int32_t *offs = expert_offsets;
 
     const int lpp = pair_lanes(k);
     int vpl, segs;
@@ -410,8 +547,8 @@ hipError_t launch_dispatch(const uint16_t *x, int64_t T, int H, const int32_t *t
         const dim3 grid((unsigned)((T * segs + kWavesPerBlock - 1) / kWavesPerBlock));
 #define MOE_PACK_BF16(V)                                                                                         \
     hipLaunchKernelGGL(dispatch_pack_bf16_kernel<V>, grid, dim3(kBlock), 0, s, (const u32x4 *)x, T, nvec, topk_idx, \
-                       local_rank, chunk_counts, E, k, C, nchunks, lpp, segs, token_slot, recv_src, expert_counts,   \
-                       (u32x4 *)recv_x)
+                       local_rank, chunk_counts, offs, E, k, C, nchunks, lpp, segs, token_slot, recv_src,            \
+                       expert_counts, (u32x4 *)recv_x)
         switch (vpl) {
         case 2: MOE_PACK_BF16(2); break;
         case 4: MOE_PACK_BF16(4); break;
@@ -425,8 +562,8 @@ hipError_t launch_dispatch(const uint16_t *x, int64_t T, int H, const int32_t *t
         const dim3 grid((unsigned)((T * segs + kWavesPerBlock - 1) / kWavesPerBlock));
 #define MOE_PACK_FP8(V)                                                                                          \
     hipLaunchKernelGGL(dispatch_pack_fp8_kernel<V>, grid, dim3(kBlock), 0, s, (const u32x4 *)x, T, ngrp, topk_idx,  \
-                       local_rank, chunk_counts, E, k, C, nchunks, lpp, segs, token_slot, recv_src, expert_counts,   \
-                       (u32x4 *)recv_x, recv_scales)
+                       local_rank, chunk_counts, offs, E, k, C, nchunks, lpp, segs, token_slot, recv_src,            \
+                       expert_counts, (u32x4 *)recv_x, recv_scales)
         switch (vpl) {
         case 2: MOE_PACK_FP8(2); break;
         case 4: MOE_PACK_FP8(4); break;

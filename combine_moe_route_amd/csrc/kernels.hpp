@@ -16,9 +16,12 @@ hipError_t launch_route_topk_grouped(const float *logits, int64_t T, int E, int 
 
 size_t dispatch_workspace_bytes(int64_t T, int E, int k);
 
+// expert_offsets != NULL selects the packed layout (C and expert_counts
+// unused); otherwise fixed slots of C rows per expert.
 hipError_t launch_dispatch(const uint16_t *x, int64_t T, int H, const int32_t *topk_idx, int E, int k, int C,
                            int dtype, void *recv_x, float *recv_scales, int32_t *recv_src,
-                           int32_t *expert_counts, int32_t *token_slot, void *workspace, hipStream_t s);
+                           int32_t *expert_counts, int32_t *expert_offsets, int32_t *token_slot, void *workspace,
+                           hipStream_t s);
 
 // start/stop: optional events recorded at the kernel's start and end
 // (hipExtLaunchKernel); both NULL for an ordinary launch.

@@ -176,6 +176,43 @@ MOE_API int moe_dispatch(const uint16_t *x, int64_t T, int32_t H, const int32_t 
                          size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * moe_dispatch_packed -- per-expert counts, packed count-sized layout and
+ * row packing.
+ *
+ * Handbook "NVSHMEM and DeepEP", "High-throughput mode": the number of
+ * tokens bound for each destination is computed first, and the receive
+ * buffer is sized by it rather than reserved for the worst case.  pplx
+ * blog, Dispatch: each expert's tokens are contiguous for the grouped GEMM.
+ * Here expert e's rows are expert_offsets[e] .. expert_offsets[e+1]-1, one
+ * row per routed pair, with no slack between experts: the buffer needs T*k
+ * rows at most, whatever the routing (no host round trip to size it).
+ *
+ *   x, T, H, topk_idx, E, k, out_dtype, workspace, workspace_bytes, stream:
+ *                  as for moe_dispatch (the same workspace size)
+ *   recv_x         (device, out) [T*k][H] rows: bf16 (2H bytes each) or E4M3
+ *                  codes (H bytes each); 16 B aligned.  Row
+ *                  expert_offsets[e] + r holds the r-th token (ascending
+ *                  token order) routed to e.  Rows from expert_offsets[E]
+ *                  on are not written.
+ *   recv_scales    (device, out) float [T*k][H/128] for fp8, as for
+ *                  moe_dispatch; NULL for bf16.
+ *   recv_src       (device, out) int32 [T*k]: source token of each row
+ *                  below expert_offsets[E].
+ *   expert_offsets (device, out) int32 [E+1]: expert_offsets[e] = number of
+ *                  pairs routed to experts below e; expert_offsets[E] = all
+ *                  routed pairs (T*k when every id is valid).  Counts are
+ *                  the differences.
+ *   token_slot     (device, out) int32 [T][k]: the recv_x row of (t, j), or
+ *                  -1 for an id outside [0, E) (dropped, not counted).
+ * moe_combine reads a packed buffer as one expert with T*k slots (E = 1,
+ * capacity = max(1, T*k)).  Buffers must not overlap.
+ */
+MOE_API int moe_dispatch_packed(const uint16_t *x, int64_t T, int32_t H, const int32_t *topk_idx,
+                                int32_t E, int32_t k, int32_t out_dtype, void *recv_x, float *recv_scales,
+                                int32_t *recv_src, int32_t *expert_offsets, int32_t *token_slot,
+                                void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * moe_combine -- gather each token's k expert outputs and return their
  * router-weighted sum in the original token order.
  *

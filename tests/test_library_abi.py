@@ -32,7 +32,7 @@ def lib():
 
 def test_header_declares_the_entry_points():
     names = _declared()
-    for n in ("moe_route_topk", "moe_route_topk_grouped", "moe_dispatch", "moe_combine",
+    for n in ("moe_route_topk", "moe_route_topk_grouped", "moe_dispatch", "moe_dispatch_packed", "moe_combine",
               "moe_dispatch_workspace_bytes", "moe_status_string"):
         assert n in names
 
@@ -93,6 +93,13 @@ def test_host_validation_without_device(lib):
     assert lib.moe_combine(P, 8, 4, 64, P, P, 0, 2, P, P) == 0
     assert lib.moe_combine(P, 8, 4, 64, P, P, 4, 2, P, P) == -1
     assert lib.moe_combine(P, 65536, 65536, 64, P, P, 4, 2, P, P) == -2   # E*C beyond int32
+    pk = lib.moe_dispatch_packed
+    assert pk(P, 4, 64, P, 8, 2, 0, P, P, P, P, P, P, 0, P) == -1        # null pointers
+    assert pk(P, 4, 64, P, 8, 2, 2, P, P, P, P, P, P, 0, P) == -1        # bad dtype
+    assert pk(P, 4, 100, P, 8, 2, 0, P, P, P, P, P, P, 0, P) == -2       # H % 8
+    assert pk(P, 4, 192, P, 8, 2, 1, P, P, P, P, P, P, 0, P) == -2       # fp8 needs H % 128
+    assert pk(P, 4, 64, P, 8, 9, 0, P, P, P, P, P, P, 0, P) == -1        # k > E
+    assert pk(P, 1 << 25, 64, P, 8, 2, 0, P, P, P, P, P, P, 0, P) == -2  # T above the limit
     d = lib.moe_dispatch
     assert d(P, 4, 64, P, 8, 2, 4, 0, P, P, P, P, P, P, 0, P) == -1     # null pointers
     assert d(P, 4, 64, P, 8, 2, 4, 2, P, P, P, P, P, P, 0, P) == -1     # bad dtype
