@@ -66,6 +66,10 @@ def _load():
     lib.oracle_filled_rows.restype = i64
     lib.oracle_pack.argtypes = [P, i64, i32, i32, P, P, i32, i32, P, P, P]
     lib.oracle_pack.restype = ctypes.c_int
+    lib.oracle_combine_residual_rmsnorm.argtypes = [P, P, P, i64, i32, i32, P, P, ctypes.c_float, P, P]
+    lib.oracle_combine_residual_rmsnorm.restype = ctypes.c_int
+    lib.oracle_bf16_round_double_n.argtypes = [P, i64, P]
+    lib.oracle_bf16_round_double_n.restype = ctypes.c_int
     lib.oracle_combine.argtypes = [P, P, P, i64, i32, i32, P, P]
     lib.oracle_combine.restype = ctypes.c_int
     lib.oracle_bf16_round.argtypes = [ctypes.c_float]
@@ -209,6 +213,34 @@ def combine(y_pairs_bits: np.ndarray, token_slot: np.ndarray, w: np.ndarray, wan
     _check(_load().oracle_combine(_ptr(y), _ptr(token_slot), _ptr(w), T, k, H, _ptr(out), _ptr(acc)),
            "combine")
     return (out, acc) if want_acc else out
+
+
+def combine_residual_rmsnorm(y_pairs_bits: np.ndarray, token_slot: np.ndarray, w: np.ndarray,
+                             residual_bits: np.ndarray, gamma_bits: np.ndarray, eps: float):
+    """Combine, then r = sum + residual (fp32), residual_out = bf16(r) and
+    normed_out = bf16(r / sqrt(mean(r^2) + eps) * gamma) (double, one
+    rounding).  Returns (residual_out uint16 [T,H], normed_out uint16 [T,H])."""
+    token_slot = _c(token_slot, np.int32)
+    T, k = token_slot.shape
+    y = _c(y_pairs_bits, np.uint16).reshape(T * k, -1)
+    H = y.shape[1]
+    w = _c(w, np.float32).reshape(T, k)
+    res = _c(residual_bits, np.uint16).reshape(T, H)
+    gamma = _c(gamma_bits, np.uint16).reshape(H)
+    res_out = np.empty((T, H), np.uint16)
+    normed = np.empty((T, H), np.uint16)
+    _check(_load().oracle_combine_residual_rmsnorm(_ptr(y), _ptr(token_slot), _ptr(w), T, k, H, _ptr(res),
+                                                   _ptr(gamma), float(eps), _ptr(res_out), _ptr(normed)),
+           "combine_residual_rmsnorm")
+    return res_out, normed
+
+
+def bf16_round_double_array(a: np.ndarray) -> np.ndarray:
+    """bf16 RNE bit patterns of float64 values, rounded in one step."""
+    flat = _c(a, np.float64).reshape(-1)
+    out = np.empty(flat.size, np.uint16)
+    _check(_load().oracle_bf16_round_double_n(_ptr(flat), flat.size, _ptr(out)), "bf16_round_double")
+    return out.reshape(np.shape(a))
 
 
 def bf16_round(f: float) -> int:

@@ -481,6 +481,98 @@ int oracle_combine(const uint16_t *y_pairs, const int32_t *token_slot,
     return 0;
 }
 
+/* bf16 nearest-even rounding of a double, in one step (no intermediate
+ * float): 8 significant bits for normal magnitudes, a fixed step of 2^-133
+ * below 2^-126; a magnitude that rounds above the largest finite bf16 is
+ * infinite. */
+static uint16_t bf16_round_double(double v)
+{
+    if (v != v)
+        return 0x7FC0;
+    const double a = fabs(v);
+    double q;
+    if (a < 0x1p-126) {
+        q = rint(a * 0x1p133) * 0x1p-133;
+    } else {
+        int e;
+        const double m = frexp(a, &e);          /* a = m * 2^e, m in [0.5, 1) */
+        q = ldexp(rint(ldexp(m, 8)), e - 8);
+    }
+    uint16_t bits;
+    if (q > 0x1.FEp127) {
+        bits = 0x7F80;
+    } else {
+        const float f = (float)q;               /* exact: q has at most 8 significant bits */
+        uint32_t u;
+        memcpy(&u, &f, 4);
+        bits = (uint16_t)(u >> 16);
+    }
+    return (uint16_t)(bits | (signbit(v) ? 0x8000 : 0));
+}
+
+/* Array form of bf16_round_double (exposed so that its rounding can be
+ * checked on its own). */
+int oracle_bf16_round_double_n(const double *v, int64_t n, uint16_t *out)
+{
+    if (n < 0 || (n > 0 && (!v || !out)))
+        return -1;
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = bf16_round_double(v[i]);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Combine epilogue: residual add and RMSNorm                                */
+/* [GPUS] section 5: right after the sum, the result is added to the        */
+/* residual stream (the updated residual is stored), and the updated stream  */
+/* goes through the next module's RMSNorm -- x * rsqrt(mean of squares over  */
+/* the token + eps) * gamma -- all before anything is written back.  Here    */
+/* the sum is combine's weighted sum.                                        */
+/* ------------------------------------------------------------------------ */
+
+/* For each token t and h:
+ *   acc = combine's fp32 accumulator (as oracle_combine: fmaf in top-k order)
+ *   r[h] = acc + residual[t][h]             (one fp32 addition)
+ *   residual_out[t][h] = bf16 RNE of r[h]
+ *   ms = (sum over h of r[h]^2) / H         (double)
+ *   normed_out[t][h] = bf16 RNE of r[h] / sqrt(ms + eps) * gamma[h], evaluated
+ *                      in double and rounded once.
+ * residual, gamma: bf16.  With eps = 0 an all-zero row is 0/0 (NaN). */
+int oracle_combine_residual_rmsnorm(const uint16_t *y_pairs, const int32_t *token_slot, const float *w, int64_t T,
+                                    int32_t k, int32_t H, const uint16_t *residual, const uint16_t *gamma,
+                                    float eps, uint16_t *residual_out, uint16_t *normed_out)
+{
+    if (T < 0 || k < 1 || H < 1 || !(eps >= 0.0f))
+        return -1;
+    if (T == 0)
+        return 0;
+    if (!y_pairs || !token_slot || !w || !residual || !gamma || !residual_out || !normed_out)
+        return -1;
+    float *r = (float *)malloc((size_t)H * sizeof(float));
+    if (!r)
+        return -1;
+    for (int64_t t = 0; t < T; ++t) {
+        double ss = 0.0;
+        for (int32_t h = 0; h < H; ++h) {
+            float acc = 0.0f;
+            for (int32_t j = 0; j < k; ++j) {
+                if (token_slot[t * k + j] < 0)
+                    continue;
+                const float y = bf16_bits_to_float(y_pairs[(t * k + j) * (int64_t)H + h]);
+                acc = fmaf(w[t * k + j], y, acc);
+            }
+            r[h] = acc + bf16_bits_to_float(residual[t * H + h]);
+            residual_out[t * H + h] = oracle_bf16_round(r[h]);
+            ss += (double)r[h] * (double)r[h];
+        }
+        const double inv = 1.0 / sqrt(ss / H + (double)eps);
+        for (int32_t h = 0; h < H; ++h)
+            normed_out[t * H + h] = bf16_round_double((double)r[h] * inv * (double)bf16_bits_to_float(gamma[h]));
+    }
+    free(r);
+    return 0;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Buffer sizing                                                             */
 /* [HBK] simulation listing: an FP8 token is H bytes plus one fp32 scale per */
