@@ -2,8 +2,9 @@
 """Benchmark of the MoE token routing/dispatch/combine path on one MI355X.
 
 One step = moe_route_topk (or moe_route_topk_grouped with --route-groups) +
-moe_dispatch (or moe_dispatch_packed with --layout packed) + moe_combine,
-back to back on one stream, over one batch of seeded synthetic input already
+moe_dispatch (or moe_dispatch_packed with --layout packed) + moe_combine (or
+moe_combine_residual_rmsnorm with --epilogue rmsnorm), back to back on one
+stream, over one batch of seeded synthetic input already
 resident in HBM.
 W untimed warm-up steps, then exactly K timed steps between device
 synchronisations.  Prints one JSON line (stdout):
@@ -43,15 +44,18 @@ HBM_PEAK_GBPS = 8000.0
 LLC_BYTES = 256 * 2 ** 20
 
 
-def algorithmic_bytes(w: W.Workload) -> dict:
-    """Bytes each step must move: every row read once and written k times."""
+def algorithmic_bytes(w: W.Workload, epilogue: bool = False) -> dict:
+    """Bytes each step must move: every row read once and written k times.
+    With the fused residual + RMSNorm epilogue, combine also reads the
+    residual and gamma and writes the updated residual (its normalised rows
+    take the place of the plain output)."""
     T, H, E, k = w.T, w.H, w.E, w.k
     row = (H + H // 32) if w.fp8 else 2 * H
     b = {
         "route": T * E * 4 + T * k * 8,
         "count_scan_slot": T * k * 12 + E * 4,
         "pack": T * H * 2 + T * k * 4 + T * k * row,
-        "combine": T * k * 2 * H + T * k * 8 + T * H * 2,
+        "combine": T * k * 2 * H + T * k * 8 + T * H * 2 + ((T * H * 4 + H * 2) if epilogue else 0),
     }
     b["total"] = sum(b.values())
     return b
@@ -98,9 +102,10 @@ def host_cpu() -> str:
     return "unknown"
 
 
-def cpu_baseline(w: W.Workload, seconds: float) -> dict:
-    """Time the CPU oracle (route, slots, pack, combine) on the first
-    min(T, 2048) tokens of the workload, repeated for ~`seconds`."""
+def cpu_baseline(w: W.Workload, seconds: float, epilogue: bool = False) -> dict:
+    """Time the CPU oracle (route, slots, pack, combine -- with the residual
+    + RMSNorm epilogue if `epilogue`) on the first min(T, 2048) tokens of the
+    workload, repeated for ~`seconds`."""
     import numpy as np
     import oracle
 
@@ -109,12 +114,17 @@ def cpu_baseline(w: W.Workload, seconds: float) -> dict:
     logits = W.make_logits(w)[:ts].numpy()
     x = W.bits(W.make_x(w)[:ts])
     y_pairs = W.bits(W.make_y_pairs(w, rows=ts * w.k))
+    residual = x                     # any bf16 rows of the right shape
+    gamma = x[0]
     passes, t0 = 0, time.perf_counter()
     while True:
         idx, wt = oracle.route_topk(logits, ws.k)
         counts, token_slot, recv_src = oracle.assign_slots(idx, ws.E, ws.C)
         oracle.pack(x, oracle.FP8_E4M3 if w.fp8 else oracle.BF16, recv_src, counts, ws.C)
-        oracle.combine(y_pairs, token_slot, wt)
+        if epilogue:
+            oracle.combine_residual_rmsnorm(y_pairs, token_slot, wt, residual, gamma, 1e-6)
+        else:
+            oracle.combine(y_pairs, token_slot, wt)
         passes += 1
         el = time.perf_counter() - t0
         if el >= seconds:
@@ -122,9 +132,9 @@ def cpu_baseline(w: W.Workload, seconds: float) -> dict:
     tok_s = passes * ts / el
     return {
         "value": tok_s, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-        "sample": f"{passes} passes of route+slots+pack+combine over the first {ts} of {w.T} tokens "
-                  f"({w.name}), {el:.1f} s",
-        "gbps": algorithmic_bytes(ws)["total"] * passes / el / 1e9,
+        "sample": f"{passes} passes of route+slots+pack+combine{'+residual+rmsnorm' if epilogue else ''} over the "
+                  f"first {ts} of {w.T} tokens ({w.name}), {el:.1f} s",
+        "gbps": algorithmic_bytes(ws, epilogue)["total"] * passes / el / 1e9,
         "host": f"{host_cpu()}, {os.cpu_count()} threads visible",
     }
 
@@ -132,7 +142,8 @@ def cpu_baseline(w: W.Workload, seconds: float) -> dict:
 class BufferSet:
     """One complete copy of a step's inputs, outputs and fixed-slot buffers."""
 
-    def __init__(self, w: W.Workload, logits_cpu, x_cpu, dev, moe, torch, route_groups=None, packed=False):
+    def __init__(self, w: W.Workload, logits_cpu, x_cpu, dev, moe, torch, route_groups=None, packed=False,
+                 epilogue=False):
         self.logits = logits_cpu.to(dev)
         self.x = x_cpu.to(dev)
         self.idx = torch.empty(w.T, w.k, dtype=torch.int32, device=dev)
@@ -144,8 +155,17 @@ class BufferSet:
             self.bufs = moe.DispatchBuffers.allocate(w.T, w.H, w.E, w.k, w.C, w.fp8, dev)
             self.y = torch.empty(w.E, w.C, w.H, dtype=torch.bfloat16, device=dev)
         self.out = torch.empty(w.T, w.H, dtype=torch.bfloat16, device=dev)
-        self.step = moe.PreparedStep(self.logits, w.k, self.x, w.C, w.fp8, self.bufs, self.y, self.out,
-                                     self.idx, self.wt, route_groups=route_groups)
+        self.epilogue = None
+        if epilogue:
+            # residual stream (the activations stand in for it) and RMSNorm weight
+            gamma = torch.linspace(0.5, 1.5, w.H, device=dev).to(torch.bfloat16)
+            self.epilogue = (self.x, gamma, 1e-6, torch.empty(w.T, w.H, dtype=torch.bfloat16, device=dev))
+        self.route_groups = route_groups
+        self.step = self.prepare(w, moe)
+
+    def prepare(self, w, moe, stream=None):
+        return moe.PreparedStep(self.logits, w.k, self.x, w.C, w.fp8, self.bufs, self.y, self.out, self.idx,
+                                self.wt, stream=stream, route_groups=self.route_groups, epilogue=self.epilogue)
 
     def fill_expert_outputs(self, w: W.Workload, torch, gen):
         """Seeded N(0,1) bf16 expert outputs in the slots the dispatch filled."""
@@ -174,6 +194,8 @@ def main() -> int:
     ap.add_argument("--layout", choices=["fixed", "packed"], default="fixed",
                     help="dispatch layout: fixed slots per expert (moe_dispatch) or packed count-sized rows "
                          "(moe_dispatch_packed)")
+    ap.add_argument("--epilogue", choices=["none", "rmsnorm"], default="none",
+                    help="combine with the fused residual add + RMSNorm (moe_combine_residual_rmsnorm)")
     ap.add_argument("--route-groups", default="",
                     help="G:M routes with moe_route_topk_grouped (G expert groups, the best M kept)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -196,14 +218,17 @@ def main() -> int:
     moe.load()
     dev = torch.device("cuda:0")
     w = W.WORKLOADS[args.workload]
-    nbytes = algorithmic_bytes(w)
+    epilogue = args.epilogue == "rmsnorm"
+    if epilogue:
+        args.timing = "marker"       # the fused kernel has no launch-attached timing entry point
+    nbytes = algorithmic_bytes(w, epilogue)
     R = args.rotate or max(1, min(32, math.ceil(2 * 2 ** 30 / nbytes["total"])))
 
     logits_cpu = W.make_logits(w)
     x_cpu = W.make_x(w)
     route_groups = tuple(int(v) for v in args.route_groups.split(":")) if args.route_groups else None
     packed = args.layout == "packed"
-    sets = [BufferSet(w, logits_cpu, x_cpu, dev, moe, torch, route_groups, packed) for _ in range(R)]
+    sets = [BufferSet(w, logits_cpu, x_cpu, dev, moe, torch, route_groups, packed, epilogue) for _ in range(R)]
     gen = torch.Generator(device=dev)
     gen.manual_seed(w.seed * 16 + 3)
     for s in sets:
@@ -223,9 +248,7 @@ def main() -> int:
         while steps are queued)."""
         torch.cuda.synchronize()
         for si, st in enumerate(sets):
-            st.step = moe.PreparedStep(st.logits, w.k, st.x, w.C, w.fp8, st.bufs, st.y, st.out, st.idx, st.wt,
-                                       route_groups=route_groups,
-                                       stream=streams[si % nstreams])
+            st.step = st.prepare(w, moe, stream=streams[si % nstreams])
 
     def run_steps(first, n, nstreams, ev=None):
         """n steps over buffer sets first, first+1, ...; when `ev` maps step
@@ -323,6 +346,7 @@ def main() -> int:
             "row_dtype": "fp8-e4m3+fp32/128" if w.fp8 else "bf16", "routing": w.routing,
             "route_groups": ({"groups": route_groups[0], "kept": route_groups[1]} if route_groups else None),
             "layout": "packed count-sized rows" if packed else "fixed slots per expert",
+            "combine_epilogue": "residual add + RMSNorm (fused)" if epilogue else None,
             "parallelism": "none (1 GPU)",
             "algorithmic_bytes_per_step": nbytes["total"],
             "effective_hbm_gbps": gbps,
@@ -334,13 +358,13 @@ def main() -> int:
             "two_batches_in_flight": overlap,
         },
         "roofline": {
-            "kernel": f"combine_kernel<{w.k}>",
+            "kernel": f"combine_rmsnorm_kernel (k={w.k})" if epilogue else f"combine_kernel<{w.k}>",
             "bound": "hbm",
             "achieved": comb_gbps,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": comb_gbps / HBM_PEAK_GBPS,
-            "traffic": None if packed else measured_traffic(w),
+            "traffic": None if (packed or epilogue) else measured_traffic(w),
             "traffic_source": f"profiles/{w.name}_hbm_traffic.md (bytes per launch)",
             "algorithmic_bytes_per_launch": nbytes["combine"],
             "mean_launch_us": combine_ms * 1e3,
@@ -352,7 +376,7 @@ def main() -> int:
         },
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, epilogue)
     print(json.dumps(result), flush=True)
     return 0
 

@@ -16,6 +16,7 @@ from .binding import (  # noqa: F401
     PreparedStep,
     load,
     moe_combine,
+    moe_combine_residual_rmsnorm,
     moe_dispatch,
     moe_dispatch_packed,
     moe_dispatch_workspace_bytes,

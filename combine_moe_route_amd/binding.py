@@ -59,6 +59,8 @@ def load() -> ctypes.CDLL:
     lib.moe_dispatch_packed.restype = ctypes.c_int
     lib.moe_combine.argtypes = [P, i32, i32, i32, P, P, i64, i32, P, P]
     lib.moe_combine.restype = ctypes.c_int
+    lib.moe_combine_residual_rmsnorm.argtypes = [P, i32, i32, i32, P, P, i64, i32, P, P, ctypes.c_float, P, P, P]
+    lib.moe_combine_residual_rmsnorm.restype = ctypes.c_int
     lib.moe_combine_timed.argtypes = [P, i32, i32, i32, P, P, i64, i32, P, P, P, P]
     lib.moe_combine_timed.restype = ctypes.c_int
     _lib = lib
@@ -317,6 +319,36 @@ def moe_combine(y: torch.Tensor, token_slot: torch.Tensor, topk_w: torch.Tensor,
     return out
 
 
+def moe_combine_residual_rmsnorm(y: torch.Tensor, token_slot: torch.Tensor, topk_w: torch.Tensor,
+                                 residual: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6,
+                                 residual_out: torch.Tensor | None = None, normed_out: torch.Tensor | None = None,
+                                 stream=None):
+    """Combine, then r = sum + residual: returns (residual_out = bf16(r),
+    normed_out = bf16(r * rsqrt(mean(r^2) + eps) * gamma)).  y as for
+    moe_combine; residual_out may be `residual` (in-place update)."""
+    if y.dim() == 2:
+        y = y.view(1, max(1, y.shape[0]), y.shape[1]) if y.shape[0] else y.new_empty(1, 1, y.shape[1])
+    E, C, H = y.shape
+    T, k = token_slot.shape
+    _need(y, torch.bfloat16, (E, C, H), "y")
+    _need(token_slot, torch.int32, (T, k), "token_slot")
+    _need(topk_w, torch.float32, (T, k), "topk_w")
+    _need(residual, torch.bfloat16, (T, H), "residual")
+    _need(gamma, torch.bfloat16, (H,), "gamma")
+    if residual_out is None:
+        residual_out = torch.empty(T, H, dtype=torch.bfloat16, device=y.device)
+    if normed_out is None:
+        normed_out = torch.empty(T, H, dtype=torch.bfloat16, device=y.device)
+    _need(residual_out, torch.bfloat16, (T, H), "residual_out")
+    _need(normed_out, torch.bfloat16, (T, H), "normed_out")
+    rc = load().moe_combine_residual_rmsnorm(_ptr(y), E, C, H, _ptr(token_slot), _ptr(topk_w), T, k,
+                                             _ptr(residual), _ptr(gamma), float(eps), _ptr(residual_out),
+                                             _ptr(normed_out), _stream(stream))
+    if rc != MOE_OK:
+        raise MoeError("moe_combine_residual_rmsnorm", rc)
+    return residual_out, normed_out
+
+
 class PreparedStep:
     """Route, dispatch and combine with their arguments marshalled once.
     `bufs` selects the layout: DispatchBuffers (fixed slots; y [E, C, H]) or
@@ -330,9 +362,12 @@ class PreparedStep:
 
     def __init__(self, logits: torch.Tensor, k: int, x: torch.Tensor, capacity: int, fp8: bool,
                  bufs: DispatchBuffers, y: torch.Tensor, out: torch.Tensor, topk_idx: torch.Tensor,
-                 topk_w: torch.Tensor, stream=None, route_groups: tuple[int, int] | None = None):
+                 topk_w: torch.Tensor, stream=None, route_groups: tuple[int, int] | None = None,
+                 epilogue: tuple | None = None):
         """route_groups = (n_groups, topk_groups) routes with
-        moe_route_topk_grouped instead of moe_route_topk."""
+        moe_route_topk_grouped instead of moe_route_topk.  epilogue =
+        (residual, gamma, eps, residual_out) combines with
+        moe_combine_residual_rmsnorm, writing the normalised rows to `out`."""
         T, E = logits.shape
         H = x.shape[1]
         _need(logits, torch.float32, (T, E), "logits")
@@ -373,7 +408,15 @@ class PreparedStep:
                 _ptr(x), T, H, _ptr(topk_idx), E, k, capacity, dt, _ptr(bufs.recv_x), scales, _ptr(bufs.recv_src),
                 _ptr(bufs.expert_counts), _ptr(bufs.token_slot), _ptr(bufs.workspace), bufs.workspace.numel(), s)
             self.combine_args = (_ptr(y), E, capacity, H, _ptr(bufs.token_slot), _ptr(topk_w), T, k, _ptr(out), s)
-        self._keep = (logits, x, bufs, y, out, topk_idx, topk_w)
+        self._epilogue_args = None
+        if epilogue is not None:
+            residual, gamma, eps, residual_out = epilogue
+            _need(residual, torch.bfloat16, (T, H), "residual")
+            _need(gamma, torch.bfloat16, (H,), "gamma")
+            _need(residual_out, torch.bfloat16, (T, H), "residual_out")
+            c = self.combine_args
+            self._epilogue_args = (*c[:8], _ptr(residual), _ptr(gamma), float(eps), _ptr(residual_out), _ptr(out), s)
+        self._keep = (logits, x, bufs, y, out, topk_idx, topk_w, epilogue)
 
     def route(self):
         rc = self._route_fn(*self.route_args)
@@ -386,12 +429,19 @@ class PreparedStep:
             raise MoeError(self._dispatch_name, rc)
 
     def combine(self):
+        if self._epilogue_args is not None:
+            rc = self._lib.moe_combine_residual_rmsnorm(*self._epilogue_args)
+            if rc != MOE_OK:
+                raise MoeError("moe_combine_residual_rmsnorm", rc)
+            return
         rc = self._lib.moe_combine(*self.combine_args)
         if rc != MOE_OK:
             raise MoeError("moe_combine", rc)
 
     def combine_timed(self, start_event: int, stop_event: int):
         """combine, with raw hipEvent_t handles recording its kernel's start and end."""
+        if self._epilogue_args is not None:
+            raise MoeError("moe_combine_timed", MOE_ERR_INVALID)
         rc = self._lib.moe_combine_timed(*self.combine_args, start_event, stop_event)
         if rc != MOE_OK:
             raise MoeError("moe_combine_timed", rc)

@@ -29,4 +29,9 @@ hipError_t launch_combine(const uint16_t *y, int64_t nrows, int H, const int32_t
                           int64_t T, int k, uint16_t *out, hipStream_t s, hipEvent_t start = nullptr,
                           hipEvent_t stop = nullptr);
 
+// combine + residual add + RMSNorm; residual_out may be residual (in place).
+hipError_t launch_combine_rmsnorm(const uint16_t *y, int64_t nrows, int H, const int32_t *token_slot, const float *w,
+                                  int64_t T, int k, const uint16_t *residual, const uint16_t *gamma, float eps,
+                                  uint16_t *residual_out, uint16_t *normed_out, hipStream_t s);
+
 }  // namespace moe

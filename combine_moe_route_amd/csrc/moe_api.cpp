@@ -11,6 +11,13 @@ namespace {
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Do the byte ranges [a, a + na) and [b, b + nb) overlap?
+bool overlaps(const void *a, uint64_t na, const void *b, uint64_t nb)
+{
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
 int from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 // Shared checks of E and k.
@@ -195,6 +202,37 @@ MOE_API int moe_combine_timed(const uint16_t *y, int32_t E, int32_t capacity, in
                               hipStream_t stream, hipEvent_t start, hipEvent_t stop)
 {
     return combine_checked(y, E, capacity, H, token_slot, topk_w, T, k, out, stream, start, stop);
+}
+
+MOE_API int moe_combine_residual_rmsnorm(const uint16_t *y, int32_t E, int32_t capacity, int32_t H,
+                                         const int32_t *token_slot, const float *topk_w, int64_t T, int32_t k,
+                                         const uint16_t *residual, const uint16_t *gamma, float eps,
+                                         uint16_t *residual_out, uint16_t *normed_out, hipStream_t stream)
+{
+    if (T < 0 || H < 1 || capacity < 1 || E < 1 || k < 1 || !(eps >= 0.0f) || !(eps <= 3.4e38f))
+        return MOE_ERR_INVALID;
+    if (k > MOE_MAX_TOPK || H % 8 != 0 || H > MOE_MAX_NORM_HIDDEN)
+        return MOE_ERR_UNSUPPORTED;
+    if ((int64_t)E * capacity > INT32_MAX || T > MOE_MAX_TOKENS)
+        return MOE_ERR_UNSUPPORTED;
+    if (T == 0)
+        return MOE_OK;
+    if (!y || !token_slot || !topk_w || !residual || !gamma || !residual_out || !normed_out)
+        return MOE_ERR_INVALID;
+    if (!aligned(y, 16) || !aligned(residual, 16) || !aligned(gamma, 16) || !aligned(residual_out, 16) ||
+        !aligned(normed_out, 16) || !aligned(token_slot, 4) || !aligned(topk_w, 4))
+        return MOE_ERR_INVALID;
+    const uint64_t ybytes = (uint64_t)E * capacity * H * 2, row_bytes = (uint64_t)T * H * 2;
+    // outputs must not overlap the inputs or each other; residual_out may be
+    // residual itself (an in-place update of the residual stream)
+    if (overlaps(normed_out, row_bytes, y, ybytes) || overlaps(normed_out, row_bytes, residual, row_bytes) ||
+        overlaps(normed_out, row_bytes, residual_out, row_bytes) || overlaps(normed_out, row_bytes, gamma, 2 * H) ||
+        overlaps(residual_out, row_bytes, y, ybytes) || overlaps(residual_out, row_bytes, gamma, 2 * H) ||
+        (residual_out != residual && overlaps(residual_out, row_bytes, residual, row_bytes)))
+        return MOE_ERR_INVALID;
+    (void)hipGetLastError();
+    return from_hip(moe::launch_combine_rmsnorm(y, (int64_t)E * capacity, H, token_slot, topk_w, T, k, residual,
+                                                gamma, eps, residual_out, normed_out, stream));
 }
 
 }  // extern "C"

@@ -64,6 +64,7 @@ extern "C" {
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOPK 16
 #define MOE_MAX_GROUPS 64         /* expert groups of moe_route_topk_grouped */
+#define MOE_MAX_NORM_HIDDEN 16384 /* H of moe_combine_residual_rmsnorm */
 #define MOE_MAX_TOKENS (1 << 24)  /* T above this is MOE_ERR_UNSUPPORTED */
 
 /* Text for a status code (static storage, never NULL). */
@@ -252,6 +253,42 @@ MOE_API int moe_combine(const uint16_t *y, int32_t E, int32_t capacity, int32_t 
 MOE_API int moe_combine_timed(const uint16_t *y, int32_t E, int32_t capacity, int32_t H,
                               const int32_t *token_slot, const float *topk_w, int64_t T, int32_t k,
                               uint16_t *out, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
+
+/*
+ * moe_combine_residual_rmsnorm -- moe_combine with its epilogue fused: the
+ * residual add and the next module's RMSNorm.
+ *
+ * "How GPUs Talk to Each Other During LLM Inference", section 5: right
+ * after a sum, the result is added to the residual stream, the updated
+ * stream is stored, and it is normalised (x * rsqrt(mean of squares over the
+ * token + eps) * gamma) before anything else is written -- one pass instead
+ * of three kernels that each read and write the same tensor.  Here the sum
+ * is combine's weighted sum.
+ *
+ *   y, E, capacity, token_slot, topk_w, T, k: as for moe_combine
+ *   H             hidden size, multiple of 8, <= MOE_MAX_NORM_HIDDEN
+ *   residual      (device, in)  bf16 [T][H], 16 B aligned
+ *   gamma         (device, in)  bf16 [H] RMSNorm weight, 16 B aligned
+ *   eps           >= 0, finite
+ *   residual_out  (device, out) bf16 [T][H], 16 B aligned: bf16 RNE of
+ *                 r = acc + residual (one fp32 addition; acc is exactly
+ *                 moe_combine's fp32 accumulator).  May be `residual`
+ *                 itself (in-place update); must not overlap it otherwise.
+ *   normed_out    (device, out) bf16 [T][H], 16 B aligned: (r * inv) *
+ *                 gamma with inv = 1 / sqrt(sum(r^2)/H + eps), from the
+ *                 unrounded fp32 r, evaluated in double and rounded to bf16
+ *                 (nearest even) in one step; no underflow or overflow for
+ *                 any finite row.  The sum of squares runs in a fixed order
+ *                 per launch shape, so results are identical run to run.
+ *                 Must not overlap any other buffer.  With eps = 0 an
+ *                 all-zero row gives NaN.
+ *   stream        HIP stream
+ * T = 0 enqueues nothing.
+ */
+MOE_API int moe_combine_residual_rmsnorm(const uint16_t *y, int32_t E, int32_t capacity, int32_t H,
+                                         const int32_t *token_slot, const float *topk_w, int64_t T, int32_t k,
+                                         const uint16_t *residual, const uint16_t *gamma, float eps,
+                                         uint16_t *residual_out, uint16_t *normed_out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

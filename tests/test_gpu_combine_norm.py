@@ -1,0 +1,131 @@
+"""GPU parity of the fused combine epilogue (moe_combine_residual_rmsnorm;
+"How GPUs Talk to Each Other During LLM Inference", section 5: residual add
+and RMSNorm right after the sum) through the C ABI, against the CPU oracle.
+
+residual_out must be bit-identical (the same fp32 operations in the same
+order as the oracle: combine's fma chain, one fp32 add, nearest-even bf16).
+normed_out within one bf16 ulp: the oracle evaluates the norm in double and
+rounds once, the kernel in fp32 with its own order for the sum of squares
+(relative error ~2^-20 before the final rounding), so an element can land on
+the other side of a rounding midpoint.  Cases: the five workloads at full
+size (fixed slots), the packed layout, in-place residual update, dropped
+pairs, row widths on every vector-count path, k from 1 to 16, eps = 0 with
+constant rows, and canaries past the outputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import combine_moe_route_amd as moe
+import oracle
+import workloads as W
+from gpu_common import OracleRun, bf16_ulp_distance, dev_bits, place_rows, require_gpu, say, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+SENT_BF16 = 0x7FBD
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return require_gpu()
+
+
+def _bf16(a):
+    return W.bits(torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(torch.bfloat16))
+
+
+def _compare(label, res_g, normed_g, res_o, normed_o):
+    np.testing.assert_array_equal(res_g, res_o)
+    d = bf16_ulp_distance(normed_g, normed_o)
+    say(f"  {label}: normed max ulp {int(d.max(initial=0))}, not identical {int((d > 0).sum())} of {d.size}")
+    assert d.max(initial=0) <= 1
+
+
+def _run(dev, y_dev, slot, w, res_bits, gamma_bits, eps, in_place=False):
+    T, H = res_bits.shape
+    res = to_dev_bf16(res_bits, dev)
+    gamma = to_dev_bf16(gamma_bits, dev)
+    normed = torch.empty(T + 1, H, dtype=torch.bfloat16, device=dev)
+    normed.view(torch.int16).fill_(SENT_BF16)
+    res_out = res if in_place else torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    moe.moe_combine_residual_rmsnorm(y_dev, torch.from_numpy(slot).to(dev), torch.from_numpy(w).to(dev), res, gamma,
+                                     eps, residual_out=res_out, normed_out=normed[:T])
+    got = dev_bits(normed)
+    assert (got[T] == SENT_BF16).all(), "normed_out written past its end"
+    return dev_bits(res_out), got[:T]
+
+
+@pytest.mark.parametrize("name", W.ORDER)
+def test_workloads_full_size(dev, name):
+    w = W.WORKLOADS[name]
+    o = OracleRun.get(w)
+    say(f"[combine+norm] {name}")
+    rng = np.random.default_rng(w.seed)
+    res_bits = _bf16(rng.standard_normal((w.T, w.H)))
+    gamma_bits = _bf16(rng.uniform(0.5, 1.5, w.H))
+    y = place_rows(w, o.y_pairs, o.token_slot, dev)
+    res_g, normed_g = _run(dev, y, o.token_slot, o.wt, res_bits, gamma_bits, 1e-6)
+    res_o, normed_o = oracle.combine_residual_rmsnorm(o.y_pairs, o.token_slot, o.wt, res_bits, gamma_bits, 1e-6)
+    _compare(name, res_g, normed_g, res_o, normed_o)
+    del y
+
+
+def test_packed_layout_in_place(dev):
+    w = W.WORKLOADS["dsr1_decode"]
+    o = OracleRun.get(w)
+    offsets, slot, _ = oracle.assign_packed(o.idx, w.E)
+    rng = np.random.default_rng(5)
+    res_bits = _bf16(rng.standard_normal((w.T, w.H)) * 4)
+    gamma_bits = _bf16(rng.uniform(-1, 1, w.H))
+    y = torch.empty(w.T * w.k, w.H, dtype=torch.bfloat16, device=dev)
+    y.index_copy_(0, torch.from_numpy(slot.reshape(-1).astype(np.int64)).to(dev), to_dev_bf16(o.y_pairs, dev))
+    res_g, normed_g = _run(dev, y, slot, o.wt, res_bits, gamma_bits, 1e-5, in_place=True)
+    res_o, normed_o = oracle.combine_residual_rmsnorm(o.y_pairs, slot, o.wt, res_bits, gamma_bits, 1e-5)
+    _compare("packed, in place", res_g, normed_g, res_o, normed_o)
+
+
+@pytest.mark.parametrize("T,H,k", [(1, 8, 1), (3, 64, 2), (50, 2048, 3), (37, 2056, 8), (20, 4104, 4),
+                                   (64, 7168, 8), (9, 16384, 16), (17, 8192, 5), (300, 1024, 16), (129, 6144, 2)])
+def test_shapes(dev, T, H, k):
+    rng = np.random.default_rng(T * 7 + H + k)
+    rows = T * k
+    slot = rng.permutation(rows).astype(np.int32).reshape(T, k)
+    slot[rng.random((T, k)) < 0.15] = -1                       # dropped pairs are skipped
+    wt = rng.random((T, k)).astype(np.float32)
+    y_rows = _bf16(rng.standard_normal((rows, H)))
+    y_pairs = np.zeros((rows, H), np.uint16)
+    keep = slot.reshape(-1) >= 0
+    y_pairs[keep] = y_rows[slot.reshape(-1)[keep]]
+    res_bits = _bf16(rng.standard_normal((T, H)) * rng.choice([1e-3, 1.0, 50.0], (T, 1)))
+    gamma_bits = _bf16(rng.uniform(0.25, 2.0, H))
+    say(f"[combine+norm] T={T} H={H} k={k}")
+    res_g, normed_g = _run(dev, to_dev_bf16(y_rows, dev).view(1, rows, H), slot, wt, res_bits, gamma_bits, 1e-6)
+    res_o, normed_o = oracle.combine_residual_rmsnorm(y_pairs, slot, wt, res_bits, gamma_bits, 1e-6)
+    _compare(f"T={T} H={H} k={k}", res_g, normed_g, res_o, normed_o)
+
+
+def test_constant_rows_without_eps(dev):
+    """Nothing routed, eps = 0: each row is its residual, a constant c, and
+    normalises to sign(c) * gamma exactly on both sides."""
+    T, H = 6, 512
+    vals = np.array([3.0, -0.75, 1e-3, -1e3, 2.0 ** -100, 7.0], np.float32)
+    res_bits = _bf16(np.repeat(vals[:, None], H, axis=1))
+    gamma_bits = _bf16(np.random.default_rng(6).uniform(0.25, 2, H))
+    slot = np.full((T, 2), -1, np.int32)
+    wt = np.zeros((T, 2), np.float32)
+    y = torch.zeros(1, 8, H, dtype=torch.bfloat16, device=dev)
+    res_g, normed_g = _run(dev, y, slot, wt, res_bits, gamma_bits, 0.0)
+    res_o, normed_o = oracle.combine_residual_rmsnorm(np.zeros((T * 2, H), np.uint16), slot, wt, res_bits,
+                                                      gamma_bits, 0.0)
+    np.testing.assert_array_equal(res_g, res_o)
+    np.testing.assert_array_equal(normed_g, normed_o)
+
+
+def test_empty(dev):
+    y = torch.zeros(1, 4, 64, dtype=torch.bfloat16, device=dev)
+    e = torch.empty(0, 2, dtype=torch.int32, device=dev)
+    r, n = moe.moe_combine_residual_rmsnorm(y, e, torch.empty(0, 2, device=dev),
+                                            torch.empty(0, 64, dtype=torch.bfloat16, device=dev),
+                                            torch.ones(64, dtype=torch.bfloat16, device=dev))
+    assert r.shape == (0, 64) and n.shape == (0, 64)

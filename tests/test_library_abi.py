@@ -33,7 +33,7 @@ def lib():
 def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("moe_route_topk", "moe_route_topk_grouped", "moe_dispatch", "moe_dispatch_packed", "moe_combine",
-              "moe_dispatch_workspace_bytes", "moe_status_string"):
+              "moe_combine_residual_rmsnorm", "moe_dispatch_workspace_bytes", "moe_status_string"):
         assert n in names
 
 
@@ -93,6 +93,20 @@ def test_host_validation_without_device(lib):
     assert lib.moe_combine(P, 8, 4, 64, P, P, 0, 2, P, P) == 0
     assert lib.moe_combine(P, 8, 4, 64, P, P, 4, 2, P, P) == -1
     assert lib.moe_combine(P, 65536, 65536, 64, P, P, 4, 2, P, P) == -2   # E*C beyond int32
+    cn = lib.moe_combine_residual_rmsnorm
+    A = 1 << 20                                                      # fake, 16 B aligned addresses (never used)
+    assert cn(P, 8, 4, 64, P, P, 4, 2, P, P, 1e-6, P, P, P) == -1     # null pointers
+    assert cn(P, 8, 4, 64, P, P, 0, 2, P, P, 1e-6, P, P, P) == 0      # empty
+    assert cn(P, 8, 4, 64, P, P, 4, 2, P, P, -1.0, P, P, P) == -1     # eps < 0
+    assert cn(P, 8, 4, 64, P, P, 4, 2, P, P, float("nan"), P, P, P) == -1
+    assert cn(P, 8, 4, 60, P, P, 4, 2, P, P, 1e-6, P, P, P) == -2     # H % 8
+    assert cn(P, 8, 4, 16392, P, P, 4, 2, P, P, 1e-6, P, P, P) == -2  # H above MOE_MAX_NORM_HIDDEN
+    assert cn(P, 8, 4, 64, P, P, 4, 17, P, P, 1e-6, P, P, P) == -2    # k above MOE_MAX_TOPK
+    # normed_out overlapping y, residual_out overlapping residual (not equal): rejected before any launch
+    assert cn(A, 8, 4, 64, A + 4096, A + 8192, 4, 2, A + 2 * 4096, A + 3 * 4096, 1e-6, A + 4 * 4096, A + 256,
+              P) == -1
+    assert cn(A, 8, 4, 64, A + 8192, A + 12288, 4, 2, A + 4 * 4096, A + 5 * 4096, 1e-6, A + 4 * 4096 + 16,
+              A + 7 * 4096, P) == -1
     pk = lib.moe_dispatch_packed
     assert pk(P, 4, 64, P, 8, 2, 0, P, P, P, P, P, P, 0, P) == -1        # null pointers
     assert pk(P, 4, 64, P, 8, 2, 2, P, P, P, P, P, P, 0, P) == -1        # bad dtype
