@@ -4,8 +4,9 @@
 One step = moe_route_topk (or moe_route_topk_grouped with --route-groups) +
 moe_dispatch (or moe_dispatch_packed with --layout packed) + moe_combine (or
 moe_combine_residual_rmsnorm with --epilogue rmsnorm), back to back on one
-stream, over one batch of seeded synthetic input already
-resident in HBM.
+stream, over one batch of seeded synthetic input already resident in HBM.
+With fixed slots and plain top-k the first two are the single call
+moe_route_dispatch (identical outputs; --separate-route calls them apart).
 W untimed warm-up steps, then exactly K timed steps between device
 synchronisations.  Prints one JSON line (stdout):
 
@@ -143,7 +144,8 @@ class BufferSet:
     """One complete copy of a step's inputs, outputs and fixed-slot buffers."""
 
     def __init__(self, w: W.Workload, logits_cpu, x_cpu, dev, moe, torch, route_groups=None, packed=False,
-                 epilogue=False):
+                 epilogue=False, fuse_route=True):
+        self.fuse_route = fuse_route
         self.logits = logits_cpu.to(dev)
         self.x = x_cpu.to(dev)
         self.idx = torch.empty(w.T, w.k, dtype=torch.int32, device=dev)
@@ -165,7 +167,8 @@ class BufferSet:
 
     def prepare(self, w, moe, stream=None):
         return moe.PreparedStep(self.logits, w.k, self.x, w.C, w.fp8, self.bufs, self.y, self.out, self.idx,
-                                self.wt, stream=stream, route_groups=self.route_groups, epilogue=self.epilogue)
+                                self.wt, stream=stream, route_groups=self.route_groups, epilogue=self.epilogue,
+                                fuse_route=self.fuse_route)
 
     def fill_expert_outputs(self, w: W.Workload, torch, gen):
         """Seeded N(0,1) bf16 expert outputs in the slots the dispatch filled."""
@@ -196,6 +199,8 @@ def main() -> int:
                          "(moe_dispatch_packed)")
     ap.add_argument("--epilogue", choices=["none", "rmsnorm"], default="none",
                     help="combine with the fused residual add + RMSNorm (moe_combine_residual_rmsnorm)")
+    ap.add_argument("--separate-route", action="store_true",
+                    help="call moe_route_topk and moe_dispatch separately instead of moe_route_dispatch")
     ap.add_argument("--route-groups", default="",
                     help="G:M routes with moe_route_topk_grouped (G expert groups, the best M kept)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -228,12 +233,13 @@ def main() -> int:
     x_cpu = W.make_x(w)
     route_groups = tuple(int(v) for v in args.route_groups.split(":")) if args.route_groups else None
     packed = args.layout == "packed"
-    sets = [BufferSet(w, logits_cpu, x_cpu, dev, moe, torch, route_groups, packed, epilogue) for _ in range(R)]
+    fuse_route = not args.separate_route and not packed and route_groups is None
+    sets = [BufferSet(w, logits_cpu, x_cpu, dev, moe, torch, route_groups, packed, epilogue, fuse_route)
+            for _ in range(R)]
     gen = torch.Generator(device=dev)
     gen.manual_seed(w.seed * 16 + 3)
     for s in sets:
-        s.step.route()
-        s.step.dispatch()
+        s.step.route_and_dispatch()
         s.fill_expert_outputs(w, torch, gen)
     torch.cuda.synchronize()
 
@@ -257,8 +263,7 @@ def main() -> int:
         for i in range(n):
             si = (first + i) % R
             st = sets[si].step
-            st.route()
-            st.dispatch()
+            st.route_and_dispatch()
             pair = ev.get(i) if ev else None
             if pair is None:
                 st.combine()
@@ -346,6 +351,7 @@ def main() -> int:
             "row_dtype": "fp8-e4m3+fp32/128" if w.fp8 else "bf16", "routing": w.routing,
             "route_groups": ({"groups": route_groups[0], "kept": route_groups[1]} if route_groups else None),
             "layout": "packed count-sized rows" if packed else "fixed slots per expert",
+            "route_dispatch_call": "moe_route_dispatch" if fuse_route else "separate",
             "combine_epilogue": "residual add + RMSNorm (fused)" if epilogue else None,
             "parallelism": "none (1 GPU)",
             "algorithmic_bytes_per_step": nbytes["total"],

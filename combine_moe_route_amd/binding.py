@@ -55,6 +55,9 @@ def load() -> ctypes.CDLL:
     lib.moe_dispatch_workspace_bytes.restype = ctypes.c_size_t
     lib.moe_dispatch.argtypes = [P, i64, i32, P, i32, i32, i32, i32, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.moe_dispatch.restype = ctypes.c_int
+    lib.moe_route_dispatch.argtypes = [P, i64, i32, i32, P, i32, i32, i32, P, P, P, P, P, P, P, P,
+                                       ctypes.c_size_t, P]
+    lib.moe_route_dispatch.restype = ctypes.c_int
     lib.moe_dispatch_packed.argtypes = [P, i64, i32, P, i32, i32, i32, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.moe_dispatch_packed.restype = ctypes.c_int
     lib.moe_combine.argtypes = [P, i32, i32, i32, P, P, i64, i32, P, P]
@@ -236,6 +239,39 @@ def moe_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: int, capa
     return bufs
 
 
+def moe_route_dispatch(logits: torch.Tensor, x: torch.Tensor, k: int, capacity: int, fp8: bool = False,
+                       bufs: DispatchBuffers | None = None, topk_idx: torch.Tensor | None = None,
+                       topk_w: torch.Tensor | None = None, stream=None):
+    """moe_route_topk + moe_dispatch in one call (identical outputs).
+    Returns (topk_idx, topk_w, bufs)."""
+    T, E = logits.shape
+    H = x.shape[1]
+    _need(logits, torch.float32, (T, E), "logits")
+    _need(x, torch.bfloat16, (T, H), "x")
+    if topk_idx is None:
+        topk_idx = torch.empty(T, k, dtype=torch.int32, device=x.device)
+    if topk_w is None:
+        topk_w = torch.empty(T, k, dtype=torch.float32, device=x.device)
+    _need(topk_idx, torch.int32, (T, k), "topk_idx")
+    _need(topk_w, torch.float32, (T, k), "topk_w")
+    if bufs is None:
+        bufs = DispatchBuffers.allocate(T, H, E, k, capacity, fp8, x.device)
+    _need(bufs.recv_x, torch.uint8 if fp8 else torch.bfloat16, (E, capacity, H), "recv_x")
+    if fp8:
+        _need(bufs.recv_scales, torch.float32, (E, capacity, H // 128), "recv_scales")
+    _need(bufs.recv_src, torch.int32, (E, capacity), "recv_src")
+    _need(bufs.expert_counts, torch.int32, (E,), "expert_counts")
+    _need(bufs.token_slot, torch.int32, (T, k), "token_slot")
+    rc = load().moe_route_dispatch(
+        _ptr(logits), T, E, k, _ptr(x), H, capacity, MOE_DTYPE_FP8_E4M3 if fp8 else MOE_DTYPE_BF16, _ptr(topk_idx),
+        _ptr(topk_w), _ptr(bufs.recv_x), _ptr(bufs.recv_scales) if fp8 else None, _ptr(bufs.recv_src),
+        _ptr(bufs.expert_counts), _ptr(bufs.token_slot), _ptr(bufs.workspace), bufs.workspace.numel(),
+        _stream(stream))
+    if rc != MOE_OK:
+        raise MoeError("moe_route_dispatch", rc)
+    return topk_idx, topk_w, bufs
+
+
 @dataclass
 class PackedBuffers:
     """Outputs of moe_dispatch_packed (all device tensors)."""
@@ -363,11 +399,13 @@ class PreparedStep:
     def __init__(self, logits: torch.Tensor, k: int, x: torch.Tensor, capacity: int, fp8: bool,
                  bufs: DispatchBuffers, y: torch.Tensor, out: torch.Tensor, topk_idx: torch.Tensor,
                  topk_w: torch.Tensor, stream=None, route_groups: tuple[int, int] | None = None,
-                 epilogue: tuple | None = None):
+                 epilogue: tuple | None = None, fuse_route: bool = True):
         """route_groups = (n_groups, topk_groups) routes with
         moe_route_topk_grouped instead of moe_route_topk.  epilogue =
         (residual, gamma, eps, residual_out) combines with
-        moe_combine_residual_rmsnorm, writing the normalised rows to `out`."""
+        moe_combine_residual_rmsnorm, writing the normalised rows to `out`.
+        fuse_route: route_and_dispatch() uses moe_route_dispatch (fixed slots
+        and plain top-k only)."""
         T, E = logits.shape
         H = x.shape[1]
         _need(logits, torch.float32, (T, E), "logits")
@@ -408,6 +446,11 @@ class PreparedStep:
                 _ptr(x), T, H, _ptr(topk_idx), E, k, capacity, dt, _ptr(bufs.recv_x), scales, _ptr(bufs.recv_src),
                 _ptr(bufs.expert_counts), _ptr(bufs.token_slot), _ptr(bufs.workspace), bufs.workspace.numel(), s)
             self.combine_args = (_ptr(y), E, capacity, H, _ptr(bufs.token_slot), _ptr(topk_w), T, k, _ptr(out), s)
+        self._fused_args = None
+        if not packed and route_groups is None and fuse_route:
+            self._fused_args = (_ptr(logits), T, E, k, _ptr(x), H, capacity, dt, _ptr(topk_idx), _ptr(topk_w),
+                                _ptr(bufs.recv_x), scales, _ptr(bufs.recv_src), _ptr(bufs.expert_counts),
+                                _ptr(bufs.token_slot), _ptr(bufs.workspace), bufs.workspace.numel(), s)
         self._epilogue_args = None
         if epilogue is not None:
             residual, gamma, eps, residual_out = epilogue
@@ -417,6 +460,17 @@ class PreparedStep:
             c = self.combine_args
             self._epilogue_args = (*c[:8], _ptr(residual), _ptr(gamma), float(eps), _ptr(residual_out), _ptr(out), s)
         self._keep = (logits, x, bufs, y, out, topk_idx, topk_w, epilogue)
+
+    def route_and_dispatch(self):
+        """route then dispatch; one moe_route_dispatch call where it applies
+        (fixed slots, plain top-k)."""
+        if self._fused_args is not None:
+            rc = self._lib.moe_route_dispatch(*self._fused_args)
+            if rc != MOE_OK:
+                raise MoeError("moe_route_dispatch", rc)
+            return
+        self.route()
+        self.dispatch()
 
     def route(self):
         rc = self._route_fn(*self.route_args)

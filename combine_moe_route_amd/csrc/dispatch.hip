@@ -40,6 +40,7 @@ namespace {
 
 constexpr int kChunk = 256;          // tokens per K1 work-group (one bit each)
 constexpr int kMaskWords = kChunk / 32;
+constexpr int kMaskChunk = 32;       // tokens per router membership word
 
 // Exclusive scan of the work-group's n <= 4*256 values in LDS (thread i owns
 // values 4i .. 4i+3): out[i] = sum of in[0 .. i-1] for i < n, out[n] = total.
@@ -223,32 +224,54 @@ __device__ __forceinline__ void store_stream(float *p, float v) { __builtin_nont
 // rank, or -1 when that is >= C.  Packed (offs != NULL): slot = offs[e] +
 // prefix + rank.  -1 for an id out of range.  The value is valid in lane
 // j*L.
+//
+// With masks != NULL the counts come from the router's 32-token membership
+// words instead (bit b of masks[e][c] = token 32c + b chose e): the prefix
+// sums the popcounts of the expert's earlier words and the rank is the
+// popcount of its own word below the token's bit.
 __device__ __forceinline__ int wave_slot(const int32_t *__restrict__ topk_idx, const int32_t *__restrict__ local_rank,
-                                         const int32_t *__restrict__ chunk_counts, const int32_t *__restrict__ offs,
-                                         int64_t t, int E, int k, int C, int nchunks, int lanes_per_pair)
+                                         const int32_t *__restrict__ chunk_counts, const uint32_t *__restrict__ masks,
+                                         const int32_t *__restrict__ offs, int64_t t, int E, int k, int C, int nchunks,
+                                         int lanes_per_pair)
 {
     const int lane = lane_id();
     const int j = lane / lanes_per_pair;
     const int sub = lane - j * lanes_per_pair;
-    const int c = (int)(t / kChunk);
+    const int c = (int)(masks ? t / kMaskChunk : t / kChunk);
     int e = -1, r = -1, sum = 0, base = 0;
     if (j < k) {
         e = topk_idx[t * k + j];
-        r = local_rank[t * k + j];
         if ((unsigned)e < (unsigned)E) {
             if (offs)
                 base = offs[e];
-            const int32_t *row = chunk_counts + (int64_t)e * nchunks;
-            for (int base = sub; base < c; base += 8 * lanes_per_pair) {
-                int part[8];
+            if (masks) {
+                const uint32_t *row = masks + (int64_t)e * nchunks;
+                r = __popc(row[c] & ((1u << (int)(t % kMaskChunk)) - 1u));
+                for (int b0 = sub; b0 < c; b0 += 8 * lanes_per_pair) {
+                    uint32_t part[8];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int cc = base + u * lanes_per_pair;
-                    part[u] = cc < c ? row[cc] : 0;
+                    for (int u = 0; u < 8; ++u) {
+                        const int cc = b0 + u * lanes_per_pair;
+                        part[u] = cc < c ? row[cc] : 0u;
+                    }
+#pragma unroll
+                    for (int u = 0; u < 8; ++u)
+                        sum += __popc(part[u]);
                 }
+            } else {
+                r = local_rank[t * k + j];
+                const int32_t *row = chunk_counts + (int64_t)e * nchunks;
+                for (int b0 = sub; b0 < c; b0 += 8 * lanes_per_pair) {
+                    int part[8];
 #pragma unroll
-                for (int u = 0; u < 8; ++u)
-                    sum += part[u];
+                    for (int u = 0; u < 8; ++u) {
+                        const int cc = b0 + u * lanes_per_pair;
+                        part[u] = cc < c ? row[cc] : 0;
+                    }
+#pragma unroll
+                    for (int u = 0; u < 8; ++u)
+                        sum += part[u];
+                }
             }
         }
     }
@@ -277,16 +300,17 @@ __device__ __forceinline__ void record_slot(int slot, int64_t t, int k, int lane
     }
 }
 
-// The true per-expert totals, spread over the first waves of the grid.
+// The true per-expert totals, spread over the first waves of the grid
+// (from the chunk histograms, or the popcounts of the router's masks).
 __device__ __forceinline__ void wave_totals(int64_t task, int64_t ntasks, const int32_t *__restrict__ chunk_counts,
-                                            int E, int nchunks, int32_t *__restrict__ expert_counts)
+                                            const uint32_t *__restrict__ masks, int E, int nchunks,
+                                            int32_t *__restrict__ expert_counts)
 {
     const int lane = lane_id();
     for (int64_t e = task; e < E; e += ntasks) {
-        const int32_t *row = chunk_counts + e * nchunks;
         int sum = 0;
         for (int cc = lane; cc < nchunks; cc += kWave)
-            sum += row[cc];
+            sum += masks ? __popc(masks[e * nchunks + cc]) : chunk_counts[e * nchunks + cc];
         for (int o = kWave / 2; o > 0; o >>= 1)
             sum += __shfl_xor(sum, o);
         if (lane == 0)
@@ -305,7 +329,8 @@ template <int VPL>
 __global__ __launch_bounds__(kBlock) void dispatch_pack_bf16_kernel(
     const u32x4 *__restrict__ x, int64_t T, int nvec, const int32_t *__restrict__ topk_idx,
     const int32_t *__restrict__ local_rank, const int32_t *__restrict__ chunk_counts,
-    const int32_t *__restrict__ offs, int E, int k, int C, int nchunks, int lanes_per_pair, int segs,
+    const uint32_t *__restrict__ masks, const int32_t *__restrict__ offs, int E, int k, int C, int nchunks,
+    int lanes_per_pair, int segs,
     int32_t *__restrict__ token_slot, int32_t *__restrict__ recv_src, int32_t *__restrict__ expert_counts,
     u32x4 *__restrict__ recv_x)
 {
@@ -322,11 +347,11 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_bf16_kernel(
     for (int i = 0; i < VPL; ++i)
         buf[i] = v0 + i * kWave < nvec ? src[v0 + i * kWave] : (u32x4){0, 0, 0, 0};
 
-    const int slot = wave_slot(topk_idx, local_rank, chunk_counts, offs, t, E, k, C, nchunks, lanes_per_pair);
+    const int slot = wave_slot(topk_idx, local_rank, chunk_counts, masks, offs, t, E, k, C, nchunks, lanes_per_pair);
     if (seg == 0)
         record_slot(slot, t, k, lanes_per_pair, token_slot, recv_src);
     if (task < E && expert_counts)
-        wave_totals(task, T * segs, chunk_counts, E, nchunks, expert_counts);
+        wave_totals(task, T * segs, chunk_counts, masks, E, nchunks, expert_counts);
 
 #pragma unroll 1
     for (int j = 0; j < k; ++j) {
@@ -398,7 +423,8 @@ template <int VPL>
 __global__ __launch_bounds__(kBlock) void dispatch_pack_fp8_kernel(
     const u32x4 *__restrict__ x, int64_t T, int ngrp, const int32_t *__restrict__ topk_idx,
     const int32_t *__restrict__ local_rank, const int32_t *__restrict__ chunk_counts,
-    const int32_t *__restrict__ offs, int E, int k, int C, int nchunks, int lanes_per_pair, int segs,
+    const uint32_t *__restrict__ masks, const int32_t *__restrict__ offs, int E, int k, int C, int nchunks,
+    int lanes_per_pair, int segs,
     int32_t *__restrict__ token_slot, int32_t *__restrict__ recv_src, int32_t *__restrict__ expert_counts,
     u32x4 *__restrict__ recv_x, float *__restrict__ recv_scales)
 {
@@ -425,11 +451,11 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_fp8_kernel(
         }
     }
 
-    const int slot = wave_slot(topk_idx, local_rank, chunk_counts, offs, t, E, k, C, nchunks, lanes_per_pair);
+    const int slot = wave_slot(topk_idx, local_rank, chunk_counts, masks, offs, t, E, k, C, nchunks, lanes_per_pair);
     if (seg == 0)
         record_slot(slot, t, k, lanes_per_pair, token_slot, recv_src);
     if (task < E && expert_counts)
-        wave_totals(task, T * segs, chunk_counts, E, nchunks, expert_counts);
+        wave_totals(task, T * segs, chunk_counts, masks, E, nchunks, expert_counts);
 
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
@@ -502,6 +528,49 @@ void choose_split(int64_t T, int nunits, int max_per_lane, int *vpl, int *segs)
     *segs = (nunits + v * kWave - 1) / (v * kWave);
 }
 
+// The pack launch shared by every path: `masks` (router membership words of
+// 32-token chunks) or chunk_counts + local_rank (256-token chunks) give the
+// counts; offs selects the packed layout.
+hipError_t launch_pack(const uint16_t *x, int64_t T, int H, const int32_t *topk_idx, const int32_t *local_rank,
+                       const int32_t *chunk_counts, const uint32_t *masks, const int32_t *offs, int E, int k, int C,
+                       int nchunks, int dtype, void *recv_x, float *recv_scales, int32_t *recv_src,
+                       int32_t *expert_counts, int32_t *token_slot, hipStream_t s)
+{
+    const int lpp = pair_lanes(k);
+    int vpl, segs;
+    if (dtype == 0) {
+        const int nvec = H / 8;
+        choose_split(T, nvec, kMaxV, &vpl, &segs);
+        const dim3 grid((unsigned)((T * segs + kWavesPerBlock - 1) / kWavesPerBlock));
+#define MOE_PACK_BF16(V)                                                                                         \
+    hipLaunchKernelGGL(dispatch_pack_bf16_kernel<V>, grid, dim3(kBlock), 0, s, (const u32x4 *)x, T, nvec, topk_idx, \
+                       local_rank, chunk_counts, masks, offs, E, k, C, nchunks, lpp, segs, token_slot, recv_src,            \
+                       expert_counts, (u32x4 *)recv_x)
+        switch (vpl) {
+        case 2: MOE_PACK_BF16(2); break;
+        case 4: MOE_PACK_BF16(4); break;
+        case 8: MOE_PACK_BF16(8); break;
+        default: MOE_PACK_BF16(16); break;
+        }
+#undef MOE_PACK_BF16
+    } else {
+        const int ngrp = H / 16;
+        choose_split(T, ngrp, kMaxG, &vpl, &segs);
+        const dim3 grid((unsigned)((T * segs + kWavesPerBlock - 1) / kWavesPerBlock));
+#define MOE_PACK_FP8(V)                                                                                          \
+    hipLaunchKernelGGL(dispatch_pack_fp8_kernel<V>, grid, dim3(kBlock), 0, s, (const u32x4 *)x, T, ngrp, topk_idx,  \
+                       local_rank, chunk_counts, masks, offs, E, k, C, nchunks, lpp, segs, token_slot, recv_src,            \
+                       expert_counts, (u32x4 *)recv_x, recv_scales)
+        switch (vpl) {
+        case 2: MOE_PACK_FP8(2); break;
+        case 4: MOE_PACK_FP8(4); break;
+        default: MOE_PACK_FP8(8); break;
+        }
+#undef MOE_PACK_FP8
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
 
 size_t dispatch_workspace_bytes(int64_t T, int E, int k)
@@ -539,39 +608,39 @@ hipError_t launch_dispatch(const uint16_t *x, int64_t T, int H, const int32_t *t
                            expert_offsets);
     const int32_t *offs = expert_offsets;
 
-    const int lpp = pair_lanes(k);
-    int vpl, segs;
-    if (dtype == 0) {
-        const int nvec = H / 8;
-        choose_split(T, nvec, kMaxV, &vpl, &segs);
-        const dim3 grid((unsigned)((T * segs + kWavesPerBlock - 1) / kWavesPerBlock));
-#define MOE_PACK_BF16(V)                                                                                         \
-    hipLaunchKernelGGL(dispatch_pack_bf16_kernel<V>, grid, dim3(kBlock), 0, s, (const u32x4 *)x, T, nvec, topk_idx, \
-                       local_rank, chunk_counts, offs, E, k, C, nchunks, lpp, segs, token_slot, recv_src,            \
-                       expert_counts, (u32x4 *)recv_x)
-        switch (vpl) {
-        case 2: MOE_PACK_BF16(2); break;
-        case 4: MOE_PACK_BF16(4); break;
-        case 8: MOE_PACK_BF16(8); break;
-        default: MOE_PACK_BF16(16); break;
-        }
-#undef MOE_PACK_BF16
-    } else {
-        const int ngrp = H / 16;
-        choose_split(T, ngrp, kMaxG, &vpl, &segs);
-        const dim3 grid((unsigned)((T * segs + kWavesPerBlock - 1) / kWavesPerBlock));
-#define MOE_PACK_FP8(V)                                                                                          \
-    hipLaunchKernelGGL(dispatch_pack_fp8_kernel<V>, grid, dim3(kBlock), 0, s, (const u32x4 *)x, T, ngrp, topk_idx,  \
-                       local_rank, chunk_counts, offs, E, k, C, nchunks, lpp, segs, token_slot, recv_src,            \
-                       expert_counts, (u32x4 *)recv_x, recv_scales)
-        switch (vpl) {
-        case 2: MOE_PACK_FP8(2); break;
-        case 4: MOE_PACK_FP8(4); break;
-        default: MOE_PACK_FP8(8); break;
-        }
-#undef MOE_PACK_FP8
+    return launch_pack(x, T, H, topk_idx, local_rank, chunk_counts, nullptr, offs, E, k, C, nchunks, dtype, recv_x,
+                       recv_scales, recv_src, expert_counts, token_slot, s);
+}
+
+hipError_t launch_route_dispatch(const float *logits, int64_t T, int E, int k, const uint16_t *x, int H, int C,
+                                 int dtype, int32_t *topk_idx, float *topk_w, void *recv_x, float *recv_scales,
+                                 int32_t *recv_src, int32_t *expert_counts, int32_t *token_slot, void *workspace,
+                                 hipStream_t s)
+{
+    if (T == 0) {
+        hipLaunchKernelGGL(dispatch_zero_counts_kernel, dim3((E + kBlock - 1) / kBlock), dim3(kBlock), 0, s,
+                           expert_counts, E);
+        return hipGetLastError();
     }
-    return hipGetLastError();
+    // E <= 8: the router writes 32-token membership words and pack derives
+    // the slots from them (two launches).  Otherwise, or when the prefix
+    // over those words would exceed 64 loads per lane: route, count, pack.
+    const int64_t nmask = (T + kMaskChunk - 1) / kMaskChunk;
+    const int lpp = pair_lanes(k);
+    if (E <= 8 && nmask <= 64 * (int64_t)lpp &&
+        (size_t)E * nmask * 4 <= dispatch_workspace_bytes(T, E, k)) {
+        uint32_t *masks = (uint32_t *)workspace;
+        hipError_t e = launch_route_topk_masks(logits, T, E, k, topk_idx, topk_w, masks, s);
+        if (e != hipSuccess)
+            return e;
+        return launch_pack(x, T, H, topk_idx, nullptr, nullptr, masks, nullptr, E, k, C, (int)nmask, dtype, recv_x,
+                           recv_scales, recv_src, expert_counts, token_slot, s);
+    }
+    hipError_t e = launch_route_topk(logits, T, E, k, topk_idx, topk_w, s);
+    if (e != hipSuccess)
+        return e;
+    return launch_dispatch(x, T, H, topk_idx, E, k, C, dtype, recv_x, recv_scales, recv_src, expert_counts, nullptr,
+                           token_slot, workspace, s);
 }
 
 }  // namespace moe

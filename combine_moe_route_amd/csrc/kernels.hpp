@@ -11,6 +11,18 @@ namespace moe {
 hipError_t launch_route_topk(const float *logits, int64_t T, int E, int k, int32_t *idx, float *w,
                              hipStream_t s);
 
+// Router top-k for E <= 8 that also writes each expert's 32-token
+// membership words: masks[e * ceil(T/32) + c].
+hipError_t launch_route_topk_masks(const float *logits, int64_t T, int E, int k, int32_t *idx, float *w,
+                                   uint32_t *masks, hipStream_t s);
+
+// Route + dispatch (fixed slots) in one call; the workspace is
+// dispatch_workspace_bytes(T, E, k).
+hipError_t launch_route_dispatch(const float *logits, int64_t T, int E, int k, const uint16_t *x, int H, int C,
+                                 int dtype, int32_t *topk_idx, float *topk_w, void *recv_x, float *recv_scales,
+                                 int32_t *recv_src, int32_t *expert_counts, int32_t *token_slot, void *workspace,
+                                 hipStream_t s);
+
 hipError_t launch_route_topk_grouped(const float *logits, int64_t T, int E, int k, int n_groups, int topk_groups,
                                      int32_t *idx, float *w, hipStream_t s);
 

@@ -151,6 +151,43 @@ MOE_API int moe_dispatch(const uint16_t *x, int64_t T, int32_t H, const int32_t 
                             expert_counts, nullptr, token_slot, workspace, workspace_bytes, stream);
 }
 
+MOE_API int moe_route_dispatch(const float *logits, int64_t T, int32_t E, int32_t k, const uint16_t *x, int32_t H,
+                               int32_t capacity, int32_t out_dtype, int32_t *topk_idx, float *topk_w, void *recv_x,
+                               float *recv_scales, int32_t *recv_src, int32_t *expert_counts, int32_t *token_slot,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (T < 0 || H < 1 || capacity < 1)
+        return MOE_ERR_INVALID;
+    int rc = check_ek(E, k);
+    if (rc != MOE_OK)
+        return rc;
+    if (out_dtype != MOE_DTYPE_BF16 && out_dtype != MOE_DTYPE_FP8_E4M3)
+        return MOE_ERR_INVALID;
+    if (H % 8 != 0 || (out_dtype == MOE_DTYPE_FP8_E4M3 && H % 128 != 0))
+        return MOE_ERR_UNSUPPORTED;
+    if ((int64_t)E * capacity > INT32_MAX || T > MOE_MAX_TOKENS)
+        return MOE_ERR_UNSUPPORTED;
+    if (!expert_counts || !aligned(expert_counts, 4))
+        return MOE_ERR_INVALID;
+    if (T > 0) {
+        if (!logits || !x || !topk_idx || !topk_w || !recv_x || !recv_src || !token_slot)
+            return MOE_ERR_INVALID;
+        if (!aligned(logits, 4) || !aligned(x, 16) || !aligned(recv_x, 16) || !aligned(topk_idx, 4) ||
+            !aligned(topk_w, 4) || !aligned(recv_src, 4) || !aligned(token_slot, 4))
+            return MOE_ERR_INVALID;
+        if (out_dtype == MOE_DTYPE_FP8_E4M3 && (!recv_scales || !aligned(recv_scales, 4)))
+            return MOE_ERR_INVALID;
+    }
+    if (out_dtype == MOE_DTYPE_BF16 && recv_scales)
+        return MOE_ERR_INVALID;
+    const size_t need = moe::dispatch_workspace_bytes(T, E, k);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+        return MOE_ERR_WORKSPACE;
+    (void)hipGetLastError();
+    return from_hip(moe::launch_route_dispatch(logits, T, E, k, x, H, capacity, out_dtype, topk_idx, topk_w, recv_x,
+                                               recv_scales, recv_src, expert_counts, token_slot, workspace, stream));
+}
+
 MOE_API int moe_dispatch_packed(const uint16_t *x, int64_t T, int32_t H, const int32_t *topk_idx, int32_t E,
                                 int32_t k, int32_t out_dtype, void *recv_x, float *recv_scales, int32_t *recv_src,
                                 int32_t *expert_offsets, int32_t *token_slot, void *workspace,

@@ -146,7 +146,7 @@ __device__ __forceinline__ void load_logits(const float *__restrict__ logits, in
 // stores of token t's ids and weights.  ALL_ELIGIBLE: no expert was excluded,
 // so the first choice is the token's largest logit.
 template <int G, int VPL, bool ALL_ELIGIBLE>
-__device__ __forceinline__ void select_and_store(const float (&v)[VPL], uint32_t (&key)[VPL], bool active, int64_t t,
+__device__ __forceinline__ int select_and_store(const float (&v)[VPL], uint32_t (&key)[VPL], bool active, int64_t t,
                                                  int E, int k, int32_t *__restrict__ topk_idx,
                                                  float *__restrict__ topk_w)
 {
@@ -214,6 +214,7 @@ __device__ __forceinline__ void select_and_store(const float (&v)[VPL], uint32_t
         topk_idx[t * k + gl] = my_e;
         topk_w[t * k + gl] = expf(my_v - mx) / s;
     }
+    return my_e;    // lane gl < k of an active token: its choice j = gl
 }
 
 template <int G, int VPL, bool VEC>
@@ -232,6 +233,41 @@ __global__ __launch_bounds__(kBlock) void route_topk_kernel(const float *__restr
     uint32_t key[VPL];
     load_logits<VPL, VEC>(logits, t, active, E, lane % G, v, key);
     select_and_store<G, VPL, true>(v, key, active, t, E, k, topk_idx, topk_w);
+}
+
+// Router top-k for E <= 8 with the dispatch count step folded in.  A
+// work-group routes 32 tokens (four waves of eight 8-lane groups) and, since
+// it then holds every choice of those tokens, also records which of them
+// chose each expert: masks[e * nchunks + c] has bit b set when token
+// 32c + b routed to e (LDS atomic OR, which commutes, so the words do not
+// depend on scheduling).  Dispatch derives counts, prefixes and in-chunk
+// ranks from these words by popcount.
+constexpr int kMaskChunk = 32;   // tokens per mask word
+
+__global__ __launch_bounds__(kBlock) void route_topk_mask_kernel(const float *__restrict__ logits, int64_t T, int E,
+                                                                 int k, int32_t *__restrict__ topk_idx,
+                                                                 float *__restrict__ topk_w,
+                                                                 uint32_t *__restrict__ masks, int nchunks)
+{
+    constexpr int G = 8;
+    static_assert(kWavesPerBlock * (kWave / G) == kMaskChunk, "one work-group per mask word");
+    __shared__ uint32_t smask[G];
+    if (threadIdx.x < G)
+        smask[threadIdx.x] = 0u;
+    __syncthreads();
+    const int lane = lane_id();
+    const int64_t wave = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
+    const int64_t t = wave * (kWave / G) + lane / G;
+    const bool active = t < T;
+    float v[1];
+    uint32_t key[1];
+    load_logits<1, false>(logits, t, active, E, lane % G, v, key);
+    const int my_e = select_and_store<G, 1, true>(v, key, active, t, E, k, topk_idx, topk_w);
+    if (active && lane % G < k)
+        atomicOr(&smask[my_e], 1u << (int)(t - (int64_t)blockIdx.x * kMaskChunk));
+    __syncthreads();
+    if ((int)threadIdx.x < E)
+        masks[(int64_t)threadIdx.x * nchunks + blockIdx.x] = smask[threadIdx.x];
 }
 
 // ---------------------------------------------------------------------------
@@ -417,6 +453,15 @@ hipError_t launch_route_topk_grouped(const float *logits, int64_t T, int E, int 
     if (E <= 256) return launch_grouped<4>(logits, T, E, k, n_groups, topk_groups, idx, w, s);
     if (E <= 512) return launch_grouped<8>(logits, T, E, k, n_groups, topk_groups, idx, w, s);
     return launch_grouped<16>(logits, T, E, k, n_groups, topk_groups, idx, w, s);
+}
+
+hipError_t launch_route_topk_masks(const float *logits, int64_t T, int E, int k, int32_t *idx, float *w,
+                                   uint32_t *masks, hipStream_t s)
+{
+    const int64_t nchunks = (T + kMaskChunk - 1) / kMaskChunk;
+    hipLaunchKernelGGL(route_topk_mask_kernel, dim3((unsigned)nchunks), dim3(kBlock), 0, s, logits, T, E, k, idx, w,
+                       masks, (int)nchunks);
+    return hipGetLastError();
 }
 
 hipError_t launch_route_topk(const float *logits, int64_t T, int E, int k, int32_t *idx, float *w,

@@ -177,6 +177,31 @@ MOE_API int moe_dispatch(const uint16_t *x, int64_t T, int32_t H, const int32_t 
                          size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * moe_route_dispatch -- moe_route_topk followed by moe_dispatch (fixed
+ * slots) in one call.
+ *
+ * The same steps and citations as the two calls; every output (topk_idx,
+ * topk_w, expert_counts, token_slot, recv_src, recv_x, recv_scales) is
+ * identical to calling moe_route_topk and then moe_dispatch.  For E <= 8
+ * the count step is folded into the router's kernel: a work-group that
+ * routes 32 tokens also records which of them chose each expert, and the
+ * pack derives counts, prefixes and ranks from those words, so the call is
+ * two kernel launches instead of three.  Larger E (or more than 64·2048
+ * tokens per pair lane group) use the three-step path.
+ *
+ *   logits, T, E, k, topk_idx, topk_w: as for moe_route_topk
+ *   x, H, capacity, out_dtype, recv_x, recv_scales, recv_src, expert_counts,
+ *   token_slot, workspace (moe_dispatch_workspace_bytes(T, E, k) bytes),
+ *   workspace_bytes, stream: as for moe_dispatch
+ * Buffers must not overlap.
+ */
+MOE_API int moe_route_dispatch(const float *logits, int64_t T, int32_t E, int32_t k, const uint16_t *x,
+                               int32_t H, int32_t capacity, int32_t out_dtype, int32_t *topk_idx,
+                               float *topk_w, void *recv_x, float *recv_scales, int32_t *recv_src,
+                               int32_t *expert_counts, int32_t *token_slot, void *workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
+/*
  * moe_dispatch_packed -- per-expert counts, packed count-sized layout and
  * row packing.
  *

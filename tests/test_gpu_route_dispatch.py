@@ -1,0 +1,111 @@
+"""GPU parity of moe_route_dispatch (router top-k and fixed-slot dispatch in
+one call; for E <= 8 the count step is folded into the router kernel as
+32-token membership words), through the C ABI.
+
+Every output must equal the CPU oracle (ids, counts, slots, sources, rows
+bit for bit; weights within the router tolerance) and must be bit-identical
+to the separate moe_route_topk + moe_dispatch calls.  Cases: the five
+workloads (E = 8 on the fused path, E = 128 and 256 on the three-step path),
+token counts around the 32-token word and 256-token chunk boundaries, every
+E <= 8 with every k, capacity overflow, fp8 rows, and token counts past the
+fused path's limit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import combine_moe_route_amd as moe
+import oracle
+import workloads as W
+from gpu_common import OracleRun, W_RTOL, dev_bits, require_gpu, say, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return require_gpu()
+
+
+def _run_both(dev, logits, x_bits, k, C, fp8):
+    T, E = logits.shape
+    lg = torch.from_numpy(logits).to(dev)
+    xd = to_dev_bf16(x_bits, dev)
+    i1, w1, b1 = moe.moe_route_dispatch(lg, xd, k, C, fp8=fp8)
+    i2, w2 = moe.moe_route_topk(lg, k)
+    b2 = moe.moe_dispatch(xd, i2, E, C, fp8=fp8)
+    return (i1, w1, b1), (i2, w2, b2)
+
+
+def _check(label, logits, x_bits, k, C, fp8, fused, separate):
+    T, E = logits.shape
+    H = x_bits.shape[1]
+    i1, w1, b1 = fused
+    i2, w2, b2 = separate
+    say(f"[route+dispatch] {label}: T={T} E={E} k={k} C={C} fp8={fp8}")
+    idx_o, w_o = oracle.route_topk(logits, k)
+    counts_o, slot_o, src_o = oracle.assign_slots(idx_o, E, C)
+    np.testing.assert_array_equal(i1.cpu().numpy(), idx_o)
+    np.testing.assert_allclose(w1.cpu().numpy(), w_o, rtol=W_RTOL, atol=0)
+    np.testing.assert_array_equal(b1.expert_counts.cpu().numpy(), counts_o)
+    np.testing.assert_array_equal(b1.token_slot.cpu().numpy(), slot_o)
+    filled = src_o >= 0
+    np.testing.assert_array_equal(b1.recv_src.cpu().numpy().reshape(-1)[filled], src_o[filled])
+    if fp8:
+        codes = b1.recv_x.view(E * C, H).cpu().numpy()
+        c_tok, s_tok = oracle.quantize_rows_fp8(x_bits)
+        np.testing.assert_array_equal(codes[filled], c_tok[src_o[filled]])
+        np.testing.assert_array_equal(b1.recv_scales.view(E * C, H // 128).cpu().numpy()[filled], s_tok[src_o[filled]])
+    else:
+        rows = dev_bits(b1.recv_x.view(E * C, H))
+        np.testing.assert_array_equal(rows[filled], x_bits[src_o[filled]])
+    # identical to the separate calls, bit for bit
+    assert torch.equal(i1, i2) and torch.equal(w1.view(torch.int32), w2.view(torch.int32))
+    assert torch.equal(b1.expert_counts, b2.expert_counts) and torch.equal(b1.token_slot, b2.token_slot)
+
+
+@pytest.mark.parametrize("name", W.ORDER)
+def test_workloads(dev, name):
+    w = W.WORKLOADS[name]
+    o = OracleRun.get(w)
+    fused, separate = _run_both(dev, o.logits, o.x, w.k, w.C, w.fp8)
+    _check(name, o.logits, o.x, w.k, w.C, w.fp8, fused, separate)
+
+
+@pytest.mark.parametrize("T", [1, 31, 32, 33, 255, 256, 257, 1000, 65536, 65537])
+def test_token_counts(dev, T):
+    rng = np.random.default_rng(T)
+    E, k, H = 8, 2, 64
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    x = W.bits(torch.from_numpy(rng.standard_normal((T, H)).astype(np.float32)).to(torch.bfloat16))
+    fused, separate = _run_both(dev, logits, x, k, T, False)
+    _check(f"T={T}", logits, x, k, T, False, fused, separate)
+
+
+@pytest.mark.parametrize("E", [1, 2, 3, 5, 8])
+def test_every_k(dev, E):
+    rng = np.random.default_rng(100 + E)
+    T, H = 777, 128
+    x = W.bits(torch.from_numpy(rng.standard_normal((T, H)).astype(np.float32)).to(torch.bfloat16))
+    for k in range(1, E + 1):
+        logits = rng.integers(-2, 3, (T, E)).astype(np.float32)     # ties everywhere
+        fused, separate = _run_both(dev, logits, x, k, T, k % 2 == 1 and H % 128 == 0)
+        _check(f"E={E} k={k}", logits, x, k, T, k % 2 == 1, fused, separate)
+
+
+def test_capacity_overflow(dev):
+    rng = np.random.default_rng(9)
+    T, E, k, H, C = 3000, 8, 2, 256, 300
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    logits[:, 3] += 2.0                                              # a hot expert overflows
+    x = W.bits(torch.from_numpy(rng.standard_normal((T, H)).astype(np.float32)).to(torch.bfloat16))
+    for fp8 in (False, True):
+        fused, separate = _run_both(dev, logits, x, k, C, fp8)
+        _check(f"overflow fp8={fp8}", logits, x, k, C, fp8, fused, separate)
+
+
+def test_empty(dev):
+    lg = torch.empty(0, 8, device=dev)
+    x = torch.empty(0, 64, dtype=torch.bfloat16, device=dev)
+    i, w, b = moe.moe_route_dispatch(lg, x, 2, 4)
+    assert (b.expert_counts.cpu().numpy() == 0).all()

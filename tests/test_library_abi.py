@@ -32,7 +32,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     names = _declared()
-    for n in ("moe_route_topk", "moe_route_topk_grouped", "moe_dispatch", "moe_dispatch_packed", "moe_combine",
+    for n in ("moe_route_topk", "moe_route_topk_grouped", "moe_dispatch", "moe_dispatch_packed", "moe_route_dispatch",
+              "moe_combine",
               "moe_combine_residual_rmsnorm", "moe_dispatch_workspace_bytes", "moe_status_string"):
         assert n in names
 
@@ -107,6 +108,13 @@ def test_host_validation_without_device(lib):
               P) == -1
     assert cn(A, 8, 4, 64, A + 8192, A + 12288, 4, 2, A + 4 * 4096, A + 5 * 4096, 1e-6, A + 4 * 4096 + 16,
               A + 7 * 4096, P) == -1
+    rd = lib.moe_route_dispatch
+    assert rd(P, 4, 8, 2, P, 64, 4, 0, P, P, P, P, P, P, P, P, 0, P) == -1    # null pointers
+    assert rd(P, 4, 8, 9, P, 64, 4, 0, P, P, P, P, P, P, P, P, 0, P) == -1    # k > E
+    assert rd(P, 4, 8, 2, P, 64, 0, 0, P, P, P, P, P, P, P, P, 0, P) == -1    # capacity 0
+    assert rd(P, 4, 8, 2, P, 100, 4, 0, P, P, P, P, P, P, P, P, 0, P) == -2   # H % 8
+    assert rd(P, 4, 8, 2, P, 192, 4, 1, P, P, P, P, P, P, P, P, 0, P) == -2   # fp8 needs H % 128
+    assert rd(P, 4, 4096, 2, P, 64, 4, 0, P, P, P, P, P, P, P, P, 0, P) == -2 # E above the limit
     pk = lib.moe_dispatch_packed
     assert pk(P, 4, 64, P, 8, 2, 0, P, P, P, P, P, P, 0, P) == -1        # null pointers
     assert pk(P, 4, 64, P, 8, 2, 2, P, P, P, P, P, P, 0, P) == -1        # bad dtype
