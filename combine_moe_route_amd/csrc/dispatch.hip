@@ -24,10 +24,12 @@
 //           records token_slot and recv_src; then the row is stored to
 //           each slot -- bf16 bit copies, or E4M3 codes with per-128 fp32
 //           scales.  The first E waves also write the true totals.
+// A batch of at most 256 tokens is a single chunk: then there is no count
+// launch, and every pack work-group rebuilds the chunk's masks in LDS.
 // Packed, count-sized layout (handbook "High-throughput mode": count first,
 // then a receive buffer of exactly the needed size): between count and
 // pack, one work-group sums each expert's chunk counts and scans them into
-// offsets[E+1] (with a single chunk the count work-group does it itself);
+// offsets[E+1] (a single chunk's pack work-groups scan their LDS counts);
 // pack then uses slot = offsets[e] + offset + rank, with no capacity and
 // nothing dropped.
 // Slot rows are written with non-temporal stores: each byte is written once
@@ -44,8 +46,9 @@ constexpr int kMaskChunk = 32;       // tokens per router membership word
 
 // Exclusive scan of the work-group's n <= 4*256 values in LDS (thread i owns
 // values 4i .. 4i+3): out[i] = sum of in[0 .. i-1] for i < n, out[n] = total.
-__device__ __forceinline__ void block_exclusive_scan(const int32_t *in, int n, int32_t *__restrict__ out,
-                                                     int32_t *wave_sums)
+// out may be in: a thread reads its own values before the barrier and
+// writes only those (and out[n]) after it.
+__device__ __forceinline__ void block_exclusive_scan(const int32_t *in, int n, int32_t *out, int32_t *wave_sums)
 {
     const int tid = threadIdx.x;
     const int lane = lane_id();
@@ -79,16 +82,12 @@ __device__ __forceinline__ void block_exclusive_scan(const int32_t *in, int n, i
     }
 }
 
-// offsets != NULL and a single chunk: the work-group holds every count, so
-// it also writes the packed layout's offsets (no separate scan launch).
 __global__ __launch_bounds__(kBlock) void dispatch_count_kernel(const int32_t *__restrict__ topk_idx, int64_t T,
                                                                 int E, int k, int nchunks,
                                                                 int32_t *__restrict__ chunk_counts,
-                                                                int32_t *__restrict__ local_rank,
-                                                                int32_t *__restrict__ offsets)
+                                                                int32_t *__restrict__ local_rank)
 {
-    extern __shared__ uint32_t mask[];  // [E][kMaskWords], then [E] counts when writing offsets
-    __shared__ int32_t wave_sums[kWavesPerBlock];
+    extern __shared__ uint32_t mask[];  // [E][kMaskWords]
     const int tid = threadIdx.x;
     const int c = blockIdx.x;
     for (int i = tid; i < E * kMaskWords; i += kBlock)
@@ -107,19 +106,12 @@ __global__ __launch_bounds__(kBlock) void dispatch_count_kernel(const int32_t *_
     }
     __syncthreads();
 
-    int32_t *counts_lds = (int32_t *)(mask + E * kMaskWords);
     for (int e = tid; e < E; e += kBlock) {
         int n = 0;
 #pragma unroll
         for (int w = 0; w < kMaskWords; ++w)
             n += __popc(mask[e * kMaskWords + w]);
         chunk_counts[(int64_t)e * nchunks + c] = n;
-        if (offsets)
-            counts_lds[e] = n;
-    }
-    if (offsets) {      // block-uniform: only launched so with one chunk
-        __syncthreads();
-        block_exclusive_scan(counts_lds, E, offsets, wave_sums);
     }
 
     if (t < T) {
@@ -215,6 +207,48 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void store_stream(u32x4 *p, u32x4 v) { __builtin_nontemporal_store(v, p); }
 __device__ __forceinline__ void store_stream(float *p, float v) { __builtin_nontemporal_store(v, p); }
 
+// A batch of at most 256 tokens is one chunk: every pack work-group then
+// rebuilds that chunk's membership masks from the ids itself (T*k ids, read
+// from L2), so no count launch is needed.  lds: [E][8] mask words, then for
+// the packed layout [E+1] offsets (the exclusive scan of the popcounts).
+// Work-group 0 publishes the totals (or offsets).  All threads must call it.
+__device__ __forceinline__ void local_chunk_counts(const int32_t *__restrict__ topk_idx, int64_t T, int E, int k,
+                                                   bool packed, uint32_t *lmask, int32_t *loffs, int32_t *wave_sums,
+                                                   int32_t *__restrict__ expert_counts,
+                                                   int32_t *__restrict__ expert_offsets)
+{
+    const int tid = threadIdx.x;
+    for (int i = tid; i < E * kMaskWords; i += kBlock)
+        lmask[i] = 0u;
+    __syncthreads();
+    if (tid < T) {
+        for (int j = 0; j < k; ++j) {
+            const int e = topk_idx[(int64_t)tid * k + j];
+            if ((unsigned)e < (unsigned)E)
+                atomicOr(&lmask[e * kMaskWords + (tid >> 5)], 1u << (tid & 31));
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += kBlock) {
+        int n = 0;
+#pragma unroll
+        for (int w = 0; w < kMaskWords; ++w)
+            n += __popc(lmask[e * kMaskWords + w]);
+        if (packed)
+            loffs[e] = n;
+        else if (blockIdx.x == 0)
+            expert_counts[e] = n;
+    }
+    if (packed) {
+        __syncthreads();
+        block_exclusive_scan(loffs, E, loffs, wave_sums);   // in place: each thread rewrites only what it read
+        __syncthreads();
+        if (blockIdx.x == 0)
+            for (int e = tid; e <= E; e += kBlock)
+                expert_offsets[e] = loffs[e];
+    }
+}
+
 // Slot of pair (t, j) for the lanes that own it, -1 elsewhere.  L =
 // lanes_per_pair lanes serve pair j = lane / L: they load the expert id and
 // in-chunk rank, and sum the expert's counts over all earlier 256-token
@@ -229,10 +263,14 @@ __device__ __forceinline__ void store_stream(float *p, float v) { __builtin_nont
 // words instead (bit b of masks[e][c] = token 32c + b chose e): the prefix
 // sums the popcounts of the expert's earlier words and the rank is the
 // popcount of its own word below the token's bit.
+//
+// With lmask != NULL (a single chunk, masks rebuilt in LDS) the rank comes
+// from the LDS words, there is no earlier chunk, and the packed offsets are
+// loffs (LDS).
 __device__ __forceinline__ int wave_slot(const int32_t *__restrict__ topk_idx, const int32_t *__restrict__ local_rank,
                                          const int32_t *__restrict__ chunk_counts, const uint32_t *__restrict__ masks,
-                                         const int32_t *__restrict__ offs, int64_t t, int E, int k, int C, int nchunks,
-                                         int lanes_per_pair)
+                                         const int32_t *__restrict__ offs, const uint32_t *lmask, const int32_t *loffs,
+                                         int64_t t, int E, int k, int C, int nchunks, int lanes_per_pair)
 {
     const int lane = lane_id();
     const int j = lane / lanes_per_pair;
@@ -243,8 +281,13 @@ __device__ __forceinline__ int wave_slot(const int32_t *__restrict__ topk_idx, c
         e = topk_idx[t * k + j];
         if ((unsigned)e < (unsigned)E) {
             if (offs)
-                base = offs[e];
-            if (masks) {
+                base = lmask ? loffs[e] : offs[e];
+            if (lmask) {
+                const int word = (int)t >> 5;
+                r = __popc(lmask[e * kMaskWords + word] & ((1u << ((int)t & 31)) - 1u));
+                for (int w = 0; w < word; ++w)
+                    r += __popc(lmask[e * kMaskWords + w]);
+            } else if (masks) {
                 const uint32_t *row = masks + (int64_t)e * nchunks;
                 r = __popc(row[c] & ((1u << (int)(t % kMaskChunk)) - 1u));
                 for (int b0 = sub; b0 < c; b0 += 8 * lanes_per_pair) {
@@ -329,11 +372,18 @@ template <int VPL>
 __global__ __launch_bounds__(kBlock) void dispatch_pack_bf16_kernel(
     const u32x4 *__restrict__ x, int64_t T, int nvec, const int32_t *__restrict__ topk_idx,
     const int32_t *__restrict__ local_rank, const int32_t *__restrict__ chunk_counts,
-    const uint32_t *__restrict__ masks, const int32_t *__restrict__ offs, int E, int k, int C, int nchunks,
-    int lanes_per_pair, int segs,
+    const uint32_t *__restrict__ masks, int32_t *offs, int E, int k, int C, int nchunks, int lanes_per_pair,
+    int segs,
     int32_t *__restrict__ token_slot, int32_t *__restrict__ recv_src, int32_t *__restrict__ expert_counts,
-    u32x4 *__restrict__ recv_x)
+    u32x4 *__restrict__ recv_x, int local)
 {
+    extern __shared__ uint32_t lds_words[];  // local counting only: masks, then packed offsets
+    __shared__ int32_t wave_sums[kWavesPerBlock];
+    uint32_t *lmask = local ? lds_words : nullptr;
+    int32_t *loffs = local && offs ? (int32_t *)(lds_words + E * kMaskWords) : nullptr;
+    if (local)
+        local_chunk_counts(topk_idx, T, E, k, offs != nullptr, lds_words, (int32_t *)(lds_words + E * kMaskWords),
+                           wave_sums, expert_counts, offs);
     const int lane = lane_id();
     const int64_t task = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
     const int64_t t = task / segs;
@@ -347,10 +397,11 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_bf16_kernel(
     for (int i = 0; i < VPL; ++i)
         buf[i] = v0 + i * kWave < nvec ? src[v0 + i * kWave] : (u32x4){0, 0, 0, 0};
 
-    const int slot = wave_slot(topk_idx, local_rank, chunk_counts, masks, offs, t, E, k, C, nchunks, lanes_per_pair);
+    const int slot = wave_slot(topk_idx, local_rank, chunk_counts, masks, offs, lmask, loffs, t, E, k, C, nchunks,
+                               lanes_per_pair);
     if (seg == 0)
         record_slot(slot, t, k, lanes_per_pair, token_slot, recv_src);
-    if (task < E && expert_counts)
+    if (task < E && expert_counts && !local)
         wave_totals(task, T * segs, chunk_counts, masks, E, nchunks, expert_counts);
 
 #pragma unroll 1
@@ -423,15 +474,22 @@ template <int VPL>
 __global__ __launch_bounds__(kBlock) void dispatch_pack_fp8_kernel(
     const u32x4 *__restrict__ x, int64_t T, int ngrp, const int32_t *__restrict__ topk_idx,
     const int32_t *__restrict__ local_rank, const int32_t *__restrict__ chunk_counts,
-    const uint32_t *__restrict__ masks, const int32_t *__restrict__ offs, int E, int k, int C, int nchunks,
-    int lanes_per_pair, int segs,
+    const uint32_t *__restrict__ masks, int32_t *offs, int E, int k, int C, int nchunks, int lanes_per_pair,
+    int segs,
     int32_t *__restrict__ token_slot, int32_t *__restrict__ recv_src, int32_t *__restrict__ expert_counts,
-    u32x4 *__restrict__ recv_x, float *__restrict__ recv_scales)
+    u32x4 *__restrict__ recv_x, float *__restrict__ recv_scales, int local)
 {
     // the wave's block scales, staged so each slot's scale segment is
     // written by one contiguous store instruction
     __shared__ float s_scale[kWavesPerBlock][VPL * 8];
     float *my_scale = s_scale[threadIdx.x / kWave];
+    extern __shared__ uint32_t lds_words[];  // local counting only: masks, then packed offsets
+    __shared__ int32_t wave_sums[kWavesPerBlock];
+    uint32_t *lmask = local ? lds_words : nullptr;
+    int32_t *loffs = local && offs ? (int32_t *)(lds_words + E * kMaskWords) : nullptr;
+    if (local)
+        local_chunk_counts(topk_idx, T, E, k, offs != nullptr, lds_words, (int32_t *)(lds_words + E * kMaskWords),
+                           wave_sums, expert_counts, offs);
     const int lane = lane_id();
     const int64_t task = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
     const int64_t t = task / segs;
@@ -451,10 +509,11 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_fp8_kernel(
         }
     }
 
-    const int slot = wave_slot(topk_idx, local_rank, chunk_counts, masks, offs, t, E, k, C, nchunks, lanes_per_pair);
+    const int slot = wave_slot(topk_idx, local_rank, chunk_counts, masks, offs, lmask, loffs, t, E, k, C, nchunks,
+                               lanes_per_pair);
     if (seg == 0)
         record_slot(slot, t, k, lanes_per_pair, token_slot, recv_src);
-    if (task < E && expert_counts)
+    if (task < E && expert_counts && !local)
         wave_totals(task, T * segs, chunk_counts, masks, E, nchunks, expert_counts);
 
 #pragma unroll
@@ -532,10 +591,12 @@ void choose_split(int64_t T, int nunits, int max_per_lane, int *vpl, int *segs)
 // 32-token chunks) or chunk_counts + local_rank (256-token chunks) give the
 // counts; offs selects the packed layout.
 hipError_t launch_pack(const uint16_t *x, int64_t T, int H, const int32_t *topk_idx, const int32_t *local_rank,
-                       const int32_t *chunk_counts, const uint32_t *masks, const int32_t *offs, int E, int k, int C,
+                       const int32_t *chunk_counts, const uint32_t *masks, int32_t *offs, int E, int k, int C,
                        int nchunks, int dtype, void *recv_x, float *recv_scales, int32_t *recv_src,
-                       int32_t *expert_counts, int32_t *token_slot, hipStream_t s)
+                       int32_t *expert_counts, int32_t *token_slot, hipStream_t s, bool local = false)
 {
+    // local: a single chunk whose masks every work-group rebuilds in LDS
+    const size_t lds = local ? (size_t)(E * kMaskWords + (offs ? E + 1 : 0)) * 4 : 0;
     const int lpp = pair_lanes(k);
     int vpl, segs;
     if (dtype == 0) {
@@ -543,9 +604,9 @@ hipError_t launch_pack(const uint16_t *x, int64_t T, int H, const int32_t *topk_
         choose_split(T, nvec, kMaxV, &vpl, &segs);
         const dim3 grid((unsigned)((T * segs + kWavesPerBlock - 1) / kWavesPerBlock));
 #define MOE_PACK_BF16(V)                                                                                         \
-    hipLaunchKernelGGL(dispatch_pack_bf16_kernel<V>, grid, dim3(kBlock), 0, s, (const u32x4 *)x, T, nvec, topk_idx, \
+    hipLaunchKernelGGL(dispatch_pack_bf16_kernel<V>, grid, dim3(kBlock), lds, s, (const u32x4 *)x, T, nvec, topk_idx, \
                        local_rank, chunk_counts, masks, offs, E, k, C, nchunks, lpp, segs, token_slot, recv_src,            \
-                       expert_counts, (u32x4 *)recv_x)
+                       expert_counts, (u32x4 *)recv_x, (int)local)
         switch (vpl) {
         case 2: MOE_PACK_BF16(2); break;
         case 4: MOE_PACK_BF16(4); break;
@@ -558,9 +619,9 @@ hipError_t launch_pack(const uint16_t *x, int64_t T, int H, const int32_t *topk_
         choose_split(T, ngrp, kMaxG, &vpl, &segs);
         const dim3 grid((unsigned)((T * segs + kWavesPerBlock - 1) / kWavesPerBlock));
 #define MOE_PACK_FP8(V)                                                                                          \
-    hipLaunchKernelGGL(dispatch_pack_fp8_kernel<V>, grid, dim3(kBlock), 0, s, (const u32x4 *)x, T, ngrp, topk_idx,  \
+    hipLaunchKernelGGL(dispatch_pack_fp8_kernel<V>, grid, dim3(kBlock), lds, s, (const u32x4 *)x, T, ngrp, topk_idx,  \
                        local_rank, chunk_counts, masks, offs, E, k, C, nchunks, lpp, segs, token_slot, recv_src,            \
-                       expert_counts, (u32x4 *)recv_x, recv_scales)
+                       expert_counts, (u32x4 *)recv_x, recv_scales, (int)local)
         switch (vpl) {
         case 2: MOE_PACK_FP8(2); break;
         case 4: MOE_PACK_FP8(4); break;
@@ -593,20 +654,20 @@ hipError_t launch_dispatch(const uint16_t *x, int64_t T, int H, const int32_t *t
         return hipGetLastError();
     }
     const int nchunks = (int)((T + kChunk - 1) / kChunk);
+    if (nchunks == 1)   // one chunk: pack counts it itself, no count launch
+        return launch_pack(x, T, H, topk_idx, nullptr, nullptr, nullptr, expert_offsets, E, k, C, 1, dtype, recv_x,
+                           recv_scales, recv_src, expert_counts, token_slot, s, true);
     int32_t *chunk_counts = (int32_t *)workspace;
     int32_t *local_rank =
         (int32_t *)((char *)workspace + ((int64_t)E * nchunks * 4 + 255) / 256 * 256);
 
-    // packed layout: one chunk -> the count work-group scans the offsets;
-    // several -> one more work-group totals the chunks and scans
-    const bool scan_in_count = expert_offsets && nchunks == 1;
-    hipLaunchKernelGGL(dispatch_count_kernel, dim3(nchunks), dim3(kBlock),
-                       (size_t)E * (kMaskWords + (scan_in_count ? 1 : 0)) * 4, s, topk_idx, T, E, k, nchunks,
-                       chunk_counts, local_rank, scan_in_count ? expert_offsets : nullptr);
-    if (expert_offsets && !scan_in_count)
+    // packed layout: one more work-group totals the chunks and scans
+    hipLaunchKernelGGL(dispatch_count_kernel, dim3(nchunks), dim3(kBlock), (size_t)E * kMaskWords * 4, s, topk_idx,
+                       T, E, k, nchunks, chunk_counts, local_rank);
+    if (expert_offsets)
         hipLaunchKernelGGL(dispatch_offsets_kernel, dim3(1), dim3(kScanBlock), 0, s, chunk_counts, E, nchunks,
                            expert_offsets);
-    const int32_t *offs = expert_offsets;
+    int32_t *offs = expert_offsets;
 
     return launch_pack(x, T, H, topk_idx, local_rank, chunk_counts, nullptr, offs, E, k, C, nchunks, dtype, recv_x,
                        recv_scales, recv_src, expert_counts, token_slot, s);
