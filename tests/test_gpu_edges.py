@@ -303,3 +303,18 @@ def test_workspace_reused_across_shapes(dev):
         np.testing.assert_array_equal(bufs.recv_src.cpu().numpy().reshape(-1)[filled], src_o[filled])
         rows = dev_bits(bufs.recv_x.view(E * C, H))
         np.testing.assert_array_equal(rows[filled], x[src_o[filled]])
+
+
+@pytest.mark.parametrize("E", [33, 50, 64, 65, 100, 127, 128, 129, 200, 255, 256, 257, 300, 512, 513, 1000])
+@pytest.mark.parametrize("kind", ["normal", "ties", "zeros"])
+def test_route_lane_layouts(dev, E, kind):
+    """Every lane layout of the router (16-lane groups with 4, 8 or 16
+    logits per lane, or one wave with 8 or 16 per lane), aligned and ragged
+    E, with ties and signed zeros: ids exact, weights within tolerance."""
+    rng = np.random.default_rng(E * 3 + len(kind))
+    T, k = (333 if E % 2 else 6200), min(8, E)      # both sides of the 6144-token layout switch
+    logits = _logits(rng, T, E, kind)
+    idx_g, w_g = moe.moe_route_topk(torch.from_numpy(logits).to(dev), k)
+    idx_o, w_o = oracle.route_topk(logits, k)
+    np.testing.assert_array_equal(idx_g.cpu().numpy(), idx_o)
+    np.testing.assert_allclose(w_g.cpu().numpy(), w_o, rtol=W_RTOL, atol=0)
