@@ -194,6 +194,8 @@ def main() -> int:
                     help="combine launch timing: events attached to the launch (ext) or recorded around it")
     ap.add_argument("--no-overlap", action="store_true",
                     help="skip the extra two-batches-in-flight measurement")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the extra HIP-graph-replay measurement")
     ap.add_argument("--layout", choices=["fixed", "packed"], default="fixed",
                     help="dispatch layout: fixed slots per expert (moe_dispatch) or packed count-sized rows "
                          "(moe_dispatch_packed)")
@@ -313,6 +315,34 @@ def main() -> int:
     # the same steps without timing events, for comparison
     plain_ms = timed(Wm + K, K, S)
 
+    # the same steps replayed from HIP graphs (one captured step per buffer
+    # set): no host launch cost, so small batches show their GPU time
+    graph = None
+    if not args.no_graph and S == 1:
+        cap = torch.cuda.Stream()
+        torch.cuda.synchronize()
+        for st in sets:
+            st.step = st.prepare(w, moe, stream=cap)
+        graphs = []
+        for st in sets:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                st.step.route_and_dispatch()
+                st.step.combine()
+            graphs.append(g)
+        for i in range(Wm):
+            graphs[i % R].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            graphs[(Wm + i) % R].replay()
+        torch.cuda.synchronize()
+        g_ms = (time.perf_counter() - t0) * 1e3 / K
+        graph = {"ms_per_step": g_ms, "tokens_per_s": w.T / (g_ms * 1e-3),
+                 "hbm_frac": nbytes["total"] / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+        del graphs
+        bind(S)
+
     # two independent batches in flight (steps alternate over two streams)
     overlap = None
     if not args.no_overlap and S == 1 and R >= 2:
@@ -362,6 +392,7 @@ def main() -> int:
             "ms_per_step_events": event_ms,
             "ms_per_step_without_timing_events": plain_ms,
             "two_batches_in_flight": overlap,
+            "graph_replay": graph,
         },
         "roofline": {
             "kernel": f"combine_rmsnorm_kernel (k={w.k})" if epilogue else f"combine_kernel<{w.k}>",
