@@ -181,7 +181,8 @@ class BufferSet:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=0,
+                    help="timed steps (default 50; 200 for batches of at most 256 tokens)")
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mixtral_prefill", choices=W.ORDER)
     ap.add_argument("--rotate", type=int, default=0,
@@ -225,6 +226,8 @@ def main() -> int:
     moe.load()
     dev = torch.device("cuda:0")
     w = W.WORKLOADS[args.workload]
+    if args.steps <= 0:
+        args.steps = 200 if w.T <= 256 else 50
     epilogue = args.epilogue == "rmsnorm"
     if epilogue:
         args.timing = "marker"       # the fused kernel has no launch-attached timing entry point
