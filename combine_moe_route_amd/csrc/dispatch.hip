@@ -26,6 +26,9 @@
 //           scales.  The first E waves also write the true totals.
 // A batch of at most 256 tokens is a single chunk: then there is no count
 // launch, and every pack work-group rebuilds the chunk's masks in LDS.
+// Route + dispatch in one call with E <= 8: the router already wrote one
+// membership word per expert and 32-token chunk, and pack takes prefixes and
+// ranks from their popcounts (no count launch either).
 // Packed, count-sized layout (handbook "High-throughput mode": count first,
 // then a receive buffer of exactly the needed size): between count and
 // pack, one work-group sums each expert's chunk counts and scans them into
@@ -40,7 +43,7 @@
 namespace moe {
 namespace {
 
-constexpr int kChunk = 256;          // tokens per K1 work-group (one bit each)
+constexpr int kChunk = 256;          // tokens per count work-group (one mask bit each)
 constexpr int kMaskWords = kChunk / 32;
 constexpr int kMaskChunk = 32;       // tokens per router membership word
 
@@ -381,21 +384,23 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_bf16_kernel(
     __shared__ int32_t wave_sums[kWavesPerBlock];
     uint32_t *lmask = local ? lds_words : nullptr;
     int32_t *loffs = local && offs ? (int32_t *)(lds_words + E * kMaskWords) : nullptr;
-    if (local)
-        local_chunk_counts(topk_idx, T, E, k, offs != nullptr, lds_words, (int32_t *)(lds_words + E * kMaskWords),
-                           wave_sums, expert_counts, offs);
     const int lane = lane_id();
     const int64_t task = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
     const int64_t t = task / segs;
     const int seg = (int)(task - t * segs);
-    if (t >= T)
-        return;
-    const u32x4 *src = x + t * nvec;
+    const bool active = t < T;
+    const u32x4 *src = x + (active ? t : 0) * nvec;
     const int v0 = seg * VPL * kWave + lane;
     u32x4 buf[VPL];
 #pragma unroll
     for (int i = 0; i < VPL; ++i)
-        buf[i] = v0 + i * kWave < nvec ? src[v0 + i * kWave] : (u32x4){0, 0, 0, 0};
+        buf[i] = active && v0 + i * kWave < nvec ? src[v0 + i * kWave] : (u32x4){0, 0, 0, 0};
+    // (local counting overlaps the row loads; every thread takes part)
+    if (local)
+        local_chunk_counts(topk_idx, T, E, k, offs != nullptr, lds_words, (int32_t *)(lds_words + E * kMaskWords),
+                           wave_sums, expert_counts, offs);
+    if (!active)
+        return;
 
     const int slot = wave_slot(topk_idx, local_rank, chunk_counts, masks, offs, lmask, loffs, t, E, k, C, nchunks,
                                lanes_per_pair);
@@ -487,27 +492,29 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_fp8_kernel(
     __shared__ int32_t wave_sums[kWavesPerBlock];
     uint32_t *lmask = local ? lds_words : nullptr;
     int32_t *loffs = local && offs ? (int32_t *)(lds_words + E * kMaskWords) : nullptr;
-    if (local)
-        local_chunk_counts(topk_idx, T, E, k, offs != nullptr, lds_words, (int32_t *)(lds_words + E * kMaskWords),
-                           wave_sums, expert_counts, offs);
     const int lane = lane_id();
     const int64_t task = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
     const int64_t t = task / segs;
     const int seg = (int)(task - t * segs);
-    if (t >= T)
-        return;
-    const u32x4 *src = x + t * (int64_t)ngrp * 2;
+    const bool active = t < T;
+    const u32x4 *src = x + (active ? t : 0) * (int64_t)ngrp * 2;
     const int nblk = ngrp / 8;
     const int g0 = seg * VPL * kWave + lane;
     u32x4 lo[VPL], hi[VPL];
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
         lo[i] = hi[i] = (u32x4){0, 0, 0, 0};
-        if (g0 + i * kWave < ngrp) {
+        if (active && g0 + i * kWave < ngrp) {
             lo[i] = src[2 * (g0 + i * kWave)];
             hi[i] = src[2 * (g0 + i * kWave) + 1];
         }
     }
+    // (local counting overlaps the row loads; every thread takes part)
+    if (local)
+        local_chunk_counts(topk_idx, T, E, k, offs != nullptr, lds_words, (int32_t *)(lds_words + E * kMaskWords),
+                           wave_sums, expert_counts, offs);
+    if (!active)
+        return;
 
     const int slot = wave_slot(topk_idx, local_rank, chunk_counts, masks, offs, lmask, loffs, t, E, k, C, nchunks,
                                lanes_per_pair);
