@@ -144,12 +144,13 @@ __device__ __forceinline__ void load_logits(const float *__restrict__ logits, in
 
 // k selection rounds over the eligible keys (key 0 = not eligible), then the
 // full softmax over every logit of the token (eligible or not) and the
-// stores of token t's ids and weights.  ALL_ELIGIBLE: no expert was excluded,
-// so the first choice is the token's largest logit.
-template <int G, int VPL, bool ALL_ELIGIBLE>
+// stores of token t's ids and weights.  max_key: order key of the token's
+// largest logit when some experts were excluded; 0 when every expert was
+// eligible, so that the first choice is the largest logit.
+template <int G, int VPL>
 __device__ __forceinline__ int select_and_store(const float (&v)[VPL], uint32_t (&key)[VPL], bool active, int64_t t,
                                                  int E, int k, int32_t *__restrict__ topk_idx,
-                                                 float *__restrict__ topk_w)
+                                                 float *__restrict__ topk_w, uint32_t max_key = 0u)
 {
     const int lane = lane_id();
     const int grp = lane / G;
@@ -196,15 +197,7 @@ __device__ __forceinline__ int select_and_store(const float (&v)[VPL], uint32_t 
     // the softmax's maximum is the largest logit of all; with every expert
     // eligible it is the first choice
     float s = 0.0f;
-    float mx = top;
-    if (!ALL_ELIGIBLE) {
-        uint32_t mk = 0;
-#pragma unroll
-        for (int i = 0; i < VPL; ++i)
-            if (active && gl * VPL + i < E)
-                mk = umax(mk, order_key(v[i]));
-        mx = key_value(group_max<G>(mk));
-    }
+    const float mx = max_key ? key_value(max_key) : top;
 #pragma unroll
     for (int i = 0; i < VPL; ++i)
         if (active && gl * VPL + i < E)
@@ -232,7 +225,7 @@ __global__ __launch_bounds__(kBlock) void route_topk_kernel(const float *__restr
     float v[VPL];
     uint32_t key[VPL];
     load_logits<VPL, VEC>(logits, t, active, E, lane % G, v, key);
-    select_and_store<G, VPL, true>(v, key, active, t, E, k, topk_idx, topk_w);
+    select_and_store<G, VPL>(v, key, active, t, E, k, topk_idx, topk_w);
 }
 
 // Router top-k for E <= 8 with the dispatch count step folded in.  A
@@ -262,7 +255,7 @@ __global__ __launch_bounds__(kBlock) void route_topk_mask_kernel(const float *__
     float v[1];
     uint32_t key[1];
     load_logits<1, false>(logits, t, active, E, lane % G, v, key);
-    const int my_e = select_and_store<G, 1, true>(v, key, active, t, E, k, topk_idx, topk_w);
+    const int my_e = select_and_store<G, 1>(v, key, active, t, E, k, topk_idx, topk_w);
     if (active && lane % G < k)
         atomicOr(&smask[my_e], 1u << (int)(t - (int64_t)blockIdx.x * kMaskChunk));
     __syncthreads();
@@ -278,7 +271,8 @@ __global__ __launch_bounds__(kBlock) void route_topk_mask_kernel(const float *__
 // and the k experts are chosen among them.  Weights are unchanged: the full
 // softmax over all E.
 //
-// One token per wave; lane l holds experts l*VPL .. l*VPL+VPL-1.  A group's
+// One token per wave, or (large batches, at most 16 groups) one token per
+// 16-lane group; lane l of a token holds experts l*VPL .. l*VPL+VPL-1.  A group's
 // two best logits come from a "top-2 merge" reduction on order keys
 // ((a1 >= a2) with (b1 >= b2) -> max(a1, b1), max(min(a1, b1), max(a2, b2)),
 // the top two of the union), which commutes, so the result does not depend
@@ -305,7 +299,10 @@ __device__ __forceinline__ void top2_xor(uint32_t &a1, uint32_t &a2, int m)
     top2_merge(a1, a2, (uint32_t)__shfl_xor((int)a1, m), (uint32_t)__shfl_xor((int)a2, m));
 }
 
-// Top two keys of a lane's eligible keys (a key of 0 is "none").
+// Top two keys of a lane's eligible keys (a key of 0 is "none"), branch
+// free: adding x to a multiset whose top two are (a1 >= a2) gives
+// (max(a1, x), max(a2, min(a1, x))).  (An if/else chain here compiled to
+// divergent branches and doubled the grouped router's time.)
 template <int VPL>
 __device__ __forceinline__ void lane_top2(const uint32_t (&key)[VPL], uint32_t mask_bits, uint32_t &a1, uint32_t &a2)
 {
@@ -314,12 +311,8 @@ __device__ __forceinline__ void lane_top2(const uint32_t (&key)[VPL], uint32_t m
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
         const uint32_t x = ((mask_bits >> i) & 1u) ? key[i] : 0u;
-        if (x > a1) {
-            a2 = a1;
-            a1 = x;
-        } else if (x > a2) {
-            a2 = x;
-        }
+        a2 = umax(a2, a1 < x ? a1 : x);
+        a1 = umax(a1, x);
     }
 }
 
@@ -328,29 +321,50 @@ __device__ __forceinline__ uint32_t group_score_key(uint32_t t1, uint32_t t2)
     return order_key(key_value(t1) + key_value(t2));
 }
 
-template <int VPL, bool VEC>
+// The token's topk_groups best groups as a bit set, from the score keys that
+// lanes 0 .. n_groups-1 of its G lanes hold (the lowest group among equal
+// scores): topk_groups rounds of a group max and a ballot.
+template <int G>
+__device__ __forceinline__ uint64_t pick_groups(uint32_t gkey, int topk_groups)
+{
+    const int lane = lane_id();
+    const int grp = lane / G;
+    const int gl = lane % G;
+    uint64_t kept = 0;
+    for (int m = 0; m < topk_groups; ++m) {
+        const uint32_t gm = group_max<G>(gkey);
+        const uint64_t ball = __ballot(gkey == gm);
+        const int g = __ffsll((unsigned long long)(G == kWave ? ball : (ball >> (grp * G)) & 0xFFFFull)) - 1;
+        kept |= 1ull << g;
+        if (gl == g)
+            gkey = 0u;
+    }
+    return kept;
+}
+
+template <int G, int VPL, bool VEC, bool ALIGNED>
 __global__ __launch_bounds__(kBlock) void route_group_topk_kernel(const float *__restrict__ logits, int64_t T, int E,
                                                                   int k, int n_groups, int topk_groups,
                                                                   int lanes_per_group, int32_t *__restrict__ topk_idx,
                                                                   float *__restrict__ topk_w)
 {
+    static_assert(G == 16 || G == kWave, "16-lane groups or whole waves");
     const int lane = lane_id();
-    const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
+    const int grp = lane / G;
+    const int gl = lane % G;
+    const int64_t wave = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
+    const int64_t t = wave * (kWave / G) + grp;
     const bool active = t < T;
     float v[VPL];
     uint32_t key[VPL];
-    load_logits<VPL, VEC>(logits, t, active, E, lane, v, key);
+    load_logits<VPL, VEC>(logits, t, active, E, gl, v, key);
     const int gs = E / n_groups;
-    int eg[VPL];  // group of each of the lane's experts (n_groups: none)
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-        const int e = lane * VPL + i;
-        eg[i] = e < E ? e / gs : n_groups;
-    }
-
-    // group scores: lane g < n_groups ends up with group g's score key
-    uint32_t gkey = 0u;
-    if (lanes_per_group > 0) {
+    uint32_t gkey = 0u;   // lane g < n_groups of the token: group g's score key (n_groups <= G)
+    uint32_t tmax = 0u;   // the token's largest logit (key): the best group top-1
+    uint64_t kept = 0;    // the token's kept groups
+    if (ALIGNED) {
+        // every group is a power-of-two run of L whole lanes: all groups at
+        // once, by a butterfly inside their own lanes
         const int L = lanes_per_group;
         uint32_t a1, a2;
         lane_top2<VPL>(key, 0xFFFFu, a1, a2);
@@ -360,11 +374,29 @@ __global__ __launch_bounds__(kBlock) void route_group_topk_kernel(const float *_
         if (L >= 16) top2_dpp<kDppMirror>(a1, a2);
         if (L >= 32) top2_xor(a1, a2, 16);
         if (L >= 64) top2_xor(a1, a2, 32);
+        tmax = group_max<G>(a1);
         const uint32_t sk = group_score_key(a1, a2);
-        const int src = lane < n_groups ? lane * L : 0;
+        const int src = grp * G + (gl < n_groups ? gl * L : 0);
         const uint32_t g_sk = (uint32_t)__shfl((int)sk, src);
-        gkey = lane < n_groups ? g_sk : 0u;
+        gkey = gl < n_groups ? g_sk : 0u;
     } else {
+        // group of each of the lane's experts (n_groups: none).  The experts
+        // are consecutive, so one division gives the first group and offset
+        // and the rest follow by counting.
+        int eg[VPL];
+        {
+            const int e0 = gl * VPL;
+            int g = e0 / gs;
+            int r = e0 - g * gs;
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) {
+                eg[i] = e0 + i < E ? g : n_groups;
+                if (++r == gs) {
+                    r = 0;
+                    ++g;
+                }
+            }
+        }
         for (int g = 0; g < n_groups; ++g) {
             uint32_t bits = 0u;
 #pragma unroll
@@ -377,31 +409,34 @@ __global__ __launch_bounds__(kBlock) void route_group_topk_kernel(const float *_
             top2_dpp<kDppQuadXor2>(a1, a2);
             top2_dpp<kDppHalfMirror>(a1, a2);
             top2_dpp<kDppMirror>(a1, a2);
-            uint32_t r1 = (uint32_t)lane_value((int)a1, 0), r2 = (uint32_t)lane_value((int)a2, 0);
-            top2_merge(r1, r2, (uint32_t)lane_value((int)a1, 16), (uint32_t)lane_value((int)a2, 16));
-            top2_merge(r1, r2, (uint32_t)lane_value((int)a1, 32), (uint32_t)lane_value((int)a2, 32));
-            top2_merge(r1, r2, (uint32_t)lane_value((int)a1, 48), (uint32_t)lane_value((int)a2, 48));
-            if (lane == g)
+            uint32_t r1 = a1, r2 = a2;      // 16-lane groups: every lane of the row holds the result
+            if (G == kWave) {
+                r1 = (uint32_t)lane_value((int)a1, 0);
+                r2 = (uint32_t)lane_value((int)a2, 0);
+                top2_merge(r1, r2, (uint32_t)lane_value((int)a1, 16), (uint32_t)lane_value((int)a2, 16));
+                top2_merge(r1, r2, (uint32_t)lane_value((int)a1, 32), (uint32_t)lane_value((int)a2, 32));
+                top2_merge(r1, r2, (uint32_t)lane_value((int)a1, 48), (uint32_t)lane_value((int)a2, 48));
+            }
+            tmax = umax(tmax, r1);
+            if (gl == g)
                 gkey = group_score_key(r1, r2);
         }
-    }
-
-    // the topk_groups best groups (the lowest group among equal scores)
-    uint64_t kept = 0;
-    for (int m = 0; m < topk_groups; ++m) {
-        const uint32_t gm = group_max<kWave>(gkey);
-        const int g = __ffsll((unsigned long long)__ballot(gkey == gm)) - 1;
-        kept |= 1ull << g;
-        if (lane == g)
-            gkey = 0u;
-    }
-
-    // experts of the other groups are not eligible
+        kept = pick_groups<G>(gkey, topk_groups);
 #pragma unroll
-    for (int i = 0; i < VPL; ++i)
-        if (eg[i] < n_groups && !((kept >> eg[i]) & 1ull))
-            key[i] = 0u;
-    select_and_store<kWave, VPL, false>(v, key, active, t, E, k, topk_idx, topk_w);
+        for (int i = 0; i < VPL; ++i)
+            if (eg[i] < n_groups && !((kept >> eg[i]) & 1ull))
+                key[i] = 0u;
+    }
+    if (ALIGNED) {
+        kept = pick_groups<G>(gkey, topk_groups);
+        // a lane's experts all belong to group gl / L: one test per lane
+        if (!((kept >> (gl / lanes_per_group)) & 1ull)) {
+#pragma unroll
+            for (int i = 0; i < VPL; ++i)
+                key[i] = 0u;
+        }
+    }
+    select_and_store<G, VPL>(v, key, active, t, E, k, topk_idx, topk_w, tmax);
 }
 
 template <int G, int VPL>
@@ -420,26 +455,33 @@ hipError_t launch(const float *logits, int64_t T, int E, int k, int32_t *idx, fl
     return hipGetLastError();
 }
 
-template <int VPL>
+template <int G, int VPL>
 hipError_t launch_grouped(const float *logits, int64_t T, int E, int k, int n_groups, int topk_groups, int32_t *idx,
                           float *w, hipStream_t s)
 {
-    const int64_t blocks = (T + kWavesPerBlock - 1) / kWavesPerBlock;
+    constexpr int64_t tokens_per_block = (int64_t)kWavesPerBlock * (kWave / G);
+    const int64_t blocks = (T + tokens_per_block - 1) / tokens_per_block;
     const int gs = E / n_groups;
     int lpg = 0;  // lanes per group when every group is a power-of-two run of whole lanes
     if (gs % VPL == 0) {
         const int L = gs / VPL;
-        if ((L & (L - 1)) == 0 && L <= kWave)
+        if ((L & (L - 1)) == 0 && L <= G)
             lpg = L;
     }
     const bool vec = VPL > 1 && E % VPL == 0 && (VPL == 2 ? ((uintptr_t)logits % 8 == 0)
                                                            : (E % 4 == 0 && (uintptr_t)logits % 16 == 0));
-    if (vec)
-        hipLaunchKernelGGL((route_group_topk_kernel<VPL, true>), dim3((unsigned)blocks), dim3(kBlock), 0, s, logits,
-                           T, E, k, n_groups, topk_groups, lpg, idx, w);
+#define MOE_GROUPED(V, A)                                                                                         \
+    hipLaunchKernelGGL((route_group_topk_kernel<G, VPL, V, A>), dim3((unsigned)blocks), dim3(kBlock), 0, s, logits, \
+                       T, E, k, n_groups, topk_groups, lpg, idx, w)
+    if (vec && lpg)
+        MOE_GROUPED(true, true);
+    else if (vec)
+        MOE_GROUPED(true, false);
+    else if (lpg)
+        MOE_GROUPED(false, true);
     else
-        hipLaunchKernelGGL((route_group_topk_kernel<VPL, false>), dim3((unsigned)blocks), dim3(kBlock), 0, s, logits,
-                           T, E, k, n_groups, topk_groups, lpg, idx, w);
+        MOE_GROUPED(false, false);
+#undef MOE_GROUPED
     return hipGetLastError();
 }
 
@@ -448,11 +490,18 @@ hipError_t launch_grouped(const float *logits, int64_t T, int E, int k, int n_gr
 hipError_t launch_route_topk_grouped(const float *logits, int64_t T, int E, int k, int n_groups, int topk_groups,
                                      int32_t *idx, float *w, hipStream_t s)
 {
-    if (E <= 64) return launch_grouped<1>(logits, T, E, k, n_groups, topk_groups, idx, w, s);
-    if (E <= 128) return launch_grouped<2>(logits, T, E, k, n_groups, topk_groups, idx, w, s);
-    if (E <= 256) return launch_grouped<4>(logits, T, E, k, n_groups, topk_groups, idx, w, s);
-    if (E <= 512) return launch_grouped<8>(logits, T, E, k, n_groups, topk_groups, idx, w, s);
-    return launch_grouped<16>(logits, T, E, k, n_groups, topk_groups, idx, w, s);
+    // as for the plain router: four tokens per wave (16-lane groups) for
+    // large batches, when every group's score fits a lane of the token
+    if (T >= 6144 && n_groups <= 16 && E > 32 && E <= 256) {
+        if (E <= 64) return launch_grouped<16, 4>(logits, T, E, k, n_groups, topk_groups, idx, w, s);
+        if (E <= 128) return launch_grouped<16, 8>(logits, T, E, k, n_groups, topk_groups, idx, w, s);
+        return launch_grouped<16, 16>(logits, T, E, k, n_groups, topk_groups, idx, w, s);
+    }
+    if (E <= 64) return launch_grouped<kWave, 1>(logits, T, E, k, n_groups, topk_groups, idx, w, s);
+    if (E <= 128) return launch_grouped<kWave, 2>(logits, T, E, k, n_groups, topk_groups, idx, w, s);
+    if (E <= 256) return launch_grouped<kWave, 4>(logits, T, E, k, n_groups, topk_groups, idx, w, s);
+    if (E <= 512) return launch_grouped<kWave, 8>(logits, T, E, k, n_groups, topk_groups, idx, w, s);
+    return launch_grouped<kWave, 16>(logits, T, E, k, n_groups, topk_groups, idx, w, s);
 }
 
 hipError_t launch_route_topk_masks(const float *logits, int64_t T, int E, int k, int32_t *idx, float *w,

@@ -73,9 +73,12 @@ CASES = [
 
 
 @pytest.mark.parametrize("E,G,M,k", CASES)
-def test_group_layouts(dev, E, G, M, k):
-    rng = np.random.default_rng(31 * E + 7 * G + 3 * M + k)
-    T = 1000 + (E % 7)                                   # ragged: not a multiple of 4 tokens per block
+@pytest.mark.parametrize("many", [False, True])
+def test_group_layouts(dev, E, G, M, k, many):
+    """Both kernel layouts: one token per wave, and (from 6144 tokens, at
+    most 16 groups) four tokens per wave; ragged token counts."""
+    rng = np.random.default_rng(31 * E + 7 * G + 3 * M + k + many)
+    T = (6200 if many else 1000) + (E % 7)
     _check(dev, _rows(rng, T, E), k, G, M, "layout")
 
 
