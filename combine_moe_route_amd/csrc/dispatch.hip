@@ -584,10 +584,13 @@ int pair_lanes(int k)
 // smallest power of two (>= 2) that keeps the grid at <= 131072 waves.  Short
 // waves balance best (measured: 2 per lane is fastest or level with larger
 // counts on every workload); the cap only bounds the redundant slot work of
-// very long rows.
+// very long rows.  Batches too small to fill the chip with two units per
+// lane (fewer than 2048 waves) take one, for twice the waves.
 void choose_split(int64_t T, int nunits, int max_per_lane, int *vpl, int *segs)
 {
     int v = 2;
+    if (T * ((nunits + 2 * kWave - 1) / (2 * kWave)) < 2048)
+        v = 1;
     while (v < max_per_lane && T * ((nunits + v * kWave - 1) / (v * kWave)) > 131072)
         v *= 2;
     *vpl = v;
@@ -615,6 +618,7 @@ hipError_t launch_pack(const uint16_t *x, int64_t T, int H, const int32_t *topk_
                        local_rank, chunk_counts, masks, offs, E, k, C, nchunks, lpp, segs, token_slot, recv_src,            \
                        expert_counts, (u32x4 *)recv_x, (int)local)
         switch (vpl) {
+        case 1: MOE_PACK_BF16(1); break;
         case 2: MOE_PACK_BF16(2); break;
         case 4: MOE_PACK_BF16(4); break;
         case 8: MOE_PACK_BF16(8); break;
@@ -630,6 +634,7 @@ hipError_t launch_pack(const uint16_t *x, int64_t T, int H, const int32_t *topk_
                        local_rank, chunk_counts, masks, offs, E, k, C, nchunks, lpp, segs, token_slot, recv_src,            \
                        expert_counts, (u32x4 *)recv_x, recv_scales, (int)local)
         switch (vpl) {
+        case 1: MOE_PACK_FP8(1); break;
         case 2: MOE_PACK_FP8(2); break;
         case 4: MOE_PACK_FP8(4); break;
         default: MOE_PACK_FP8(8); break;
