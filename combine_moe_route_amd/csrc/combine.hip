@@ -103,6 +103,8 @@ hipError_t launch_vpl(const uint16_t *y, int64_t nrows, int nvec, const int32_t 
 {
     const int segs = (nvec + VPL * kWave - 1) / (VPL * kWave);
     const int64_t blocks = (T * segs + kWavesPerBlock - 1) / kWavesPerBlock;
+    if (!grid_fits(blocks, kBlock))
+        return hipErrorInvalidConfiguration;
     if (start || stop)
         hipExtLaunchKernelGGL((combine_kernel<K, VPL>), dim3((unsigned)blocks), dim3(kBlock), 0, s, start, stop, 0,
                               (const u32x4 *)y, nrows, nvec, token_slot, w, T, segs, (u32x4 *)out);

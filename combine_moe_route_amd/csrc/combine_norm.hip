@@ -181,6 +181,8 @@ hipError_t launch_nv(const uint16_t *y, int64_t nrows, int H, const int32_t *tok
     // about 16 row loads in flight per lane
     constexpr int P0 = 16 / KMAX > 0 ? 16 / KMAX : 1;
     constexpr int P = P0 < NV ? P0 : NV;
+    if (!grid_fits(T, BS))
+        return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((combine_rmsnorm_kernel<KMAX, NV, P, BS>), dim3((unsigned)T), dim3(BS), 0, s,
                        (const u32x4 *)y, nrows, H / 8, token_slot, w, k, (const u32x4 *)residual,
                        (const u32x4 *)gamma, eps, H, (u32x4 *)residual_out, (u32x4 *)normed_out);

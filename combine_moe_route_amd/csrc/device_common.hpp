@@ -13,6 +13,11 @@ constexpr int kWave = 64;
 constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / kWave;
 
+// A launch holds at most 2^32 - 1 work-items along x (the dispatch packet's
+// grid size is 32-bit); launchers check their grid against it.
+constexpr int64_t kMaxGridItems = 0xFFFFFFFFll;
+inline bool grid_fits(int64_t blocks, int block_size) { return blocks * block_size <= kMaxGridItems; }
+
 // Lane id within the wavefront.
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
 

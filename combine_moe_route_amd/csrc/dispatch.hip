@@ -580,18 +580,23 @@ int pair_lanes(int k)
     return kWave / p;
 }
 
-// Units (vectors or groups) per lane and row segments per token: the
-// smallest power of two (>= 2) that keeps the grid at <= 131072 waves.  Short
-// waves balance best (measured: 2 per lane is fastest or level with larger
-// counts on every workload); the cap only bounds the redundant slot work of
-// very long rows.  Batches too small to fill the chip with two units per
-// lane (fewer than 2048 waves) take one, for twice the waves.
-void choose_split(int64_t T, int nunits, int max_per_lane, int *vpl, int *segs)
+// Units (vectors or groups) per lane and row segments per token.  A lane
+// aims at about eight row stores in flight: `target` units per lane (8 / k
+// for bf16 rows, whose unit is one 16-byte store per copy; 2 for fp8, whose
+// unit already reads 32 bytes).  Fewer, longer waves also repeat the slot
+// lookup fewer times per token.  Measured with rotated buffers: at 4096
+// tokens of width 4096, top-2, four vectors per lane beat two by 2.4 us;
+// at 16384 tokens of width 7168, top-8, one beats two; fp8 rows are fastest
+// at two.  The count halves while the grid would hold fewer than 2048 waves,
+// so small batches still spread over the chip.
+void choose_split(int64_t T, int nunits, int max_per_lane, int target, int *vpl, int *segs)
 {
-    int v = 2;
-    if (T * ((nunits + 2 * kWave - 1) / (2 * kWave)) < 2048)
-        v = 1;
-    while (v < max_per_lane && T * ((nunits + v * kWave - 1) / (v * kWave)) > 131072)
+    int v = 1;
+    while (v * 2 <= target && v * 2 <= max_per_lane)
+        v *= 2;
+    while (v > 1 && T * ((nunits + v * kWave - 1) / (v * kWave)) < 2048)
+        v /= 2;
+    while (v < max_per_lane && T * ((nunits + v * kWave - 1) / (v * kWave)) * kWave > kMaxGridItems)
         v *= 2;
     *vpl = v;
     *segs = (nunits + v * kWave - 1) / (v * kWave);
@@ -611,8 +616,11 @@ hipError_t launch_pack(const uint16_t *x, int64_t T, int H, const int32_t *topk_
     int vpl, segs;
     if (dtype == 0) {
         const int nvec = H / 8;
-        choose_split(T, nvec, kMaxV, &vpl, &segs);
-        const dim3 grid((unsigned)((T * segs + kWavesPerBlock - 1) / kWavesPerBlock));
+        choose_split(T, nvec, kMaxV, k >= 8 ? 1 : 8 / k, &vpl, &segs);
+        const int64_t blocks = (T * segs + kWavesPerBlock - 1) / kWavesPerBlock;
+        if (!grid_fits(blocks, kBlock))
+            return hipErrorInvalidConfiguration;
+        const dim3 grid((unsigned)blocks);
 #define MOE_PACK_BF16(V)                                                                                         \
     hipLaunchKernelGGL(dispatch_pack_bf16_kernel<V>, grid, dim3(kBlock), lds, s, (const u32x4 *)x, T, nvec, topk_idx, \
                        local_rank, chunk_counts, masks, offs, E, k, C, nchunks, lpp, segs, token_slot, recv_src,            \
@@ -627,8 +635,11 @@ hipError_t launch_pack(const uint16_t *x, int64_t T, int H, const int32_t *topk_
 #undef MOE_PACK_BF16
     } else {
         const int ngrp = H / 16;
-        choose_split(T, ngrp, kMaxG, &vpl, &segs);
-        const dim3 grid((unsigned)((T * segs + kWavesPerBlock - 1) / kWavesPerBlock));
+        choose_split(T, ngrp, kMaxG, 2, &vpl, &segs);
+        const int64_t blocks = (T * segs + kWavesPerBlock - 1) / kWavesPerBlock;
+        if (!grid_fits(blocks, kBlock))
+            return hipErrorInvalidConfiguration;
+        const dim3 grid((unsigned)blocks);
 #define MOE_PACK_FP8(V)                                                                                          \
     hipLaunchKernelGGL(dispatch_pack_fp8_kernel<V>, grid, dim3(kBlock), lds, s, (const u32x4 *)x, T, ngrp, topk_idx,  \
                        local_rank, chunk_counts, masks, offs, E, k, C, nchunks, lpp, segs, token_slot, recv_src,            \
