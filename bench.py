@@ -182,7 +182,7 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=0,
-                    help="timed steps (default 50; 200 for batches of at most 256 tokens)")
+                    help="timed steps (default 200 for batches of at most 4096 tokens, else 50)")
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mixtral_prefill", choices=W.ORDER)
     ap.add_argument("--rotate", type=int, default=0,
@@ -227,7 +227,7 @@ def main() -> int:
     dev = torch.device("cuda:0")
     w = W.WORKLOADS[args.workload]
     if args.steps <= 0:
-        args.steps = 200 if w.T <= 256 else 50
+        args.steps = 200 if w.T <= 4096 else 50
     epilogue = args.epilogue == "rmsnorm"
     if epilogue:
         args.timing = "marker"       # the fused kernel has no launch-attached timing entry point
