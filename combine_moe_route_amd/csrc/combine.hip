@@ -129,6 +129,16 @@ hipError_t launch(const uint16_t *y, int64_t nrows, int H, const int32_t *token_
 
 }  // namespace
 
+bool combine_grid_fits(int64_t T, int H, int k)
+{
+    if (k < 1 || k > 16)
+        return false;
+    const int nvec = H / 8, V = vpl_for(k);
+    const int64_t segs_wide = (nvec + V * kWave - 1) / (V * kWave);
+    const int64_t segs = T * segs_wide < 2048 ? (nvec + kWave - 1) / kWave : segs_wide;
+    return grid_fits((T * segs + kWavesPerBlock - 1) / kWavesPerBlock, kBlock);
+}
+
 hipError_t launch_combine(const uint16_t *y, int64_t nrows, int H, const int32_t *token_slot, const float *w,
                           int64_t T, int k, uint16_t *out, hipStream_t s, hipEvent_t start, hipEvent_t stop)
 {

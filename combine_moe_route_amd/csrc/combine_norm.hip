@@ -214,9 +214,11 @@ hipError_t launch_k(const uint16_t *y, int64_t nrows, int H, const int32_t *toke
 
 }  // namespace
 
-hipError_t launch_combine_rmsnorm(const uint16_t *y, int64_t nrows, int H, const int32_t *token_slot, const float *w,
-                                  int64_t T, int k, const uint16_t *residual, const uint16_t *gamma, float eps,
-                                  uint16_t *residual_out, uint16_t *normed_out, hipStream_t s)
+namespace {
+
+hipError_t launch_tokens(const uint16_t *y, int64_t nrows, int H, const int32_t *token_slot, const float *w,
+                         int64_t T, int k, const uint16_t *residual, const uint16_t *gamma, float eps,
+                         uint16_t *residual_out, uint16_t *normed_out, hipStream_t s)
 {
     if (k <= 2)
         return launch_k<2>(y, nrows, H, token_slot, w, T, k, residual, gamma, eps, residual_out, normed_out, s);
@@ -225,6 +227,26 @@ hipError_t launch_combine_rmsnorm(const uint16_t *y, int64_t nrows, int H, const
     if (k <= 8)
         return launch_k<8>(y, nrows, H, token_slot, w, T, k, residual, gamma, eps, residual_out, normed_out, s);
     return launch_k<16>(y, nrows, H, token_slot, w, T, k, residual, gamma, eps, residual_out, normed_out, s);
+}
+
+}  // namespace
+
+hipError_t launch_combine_rmsnorm(const uint16_t *y, int64_t nrows, int H, const int32_t *token_slot, const float *w,
+                                  int64_t T, int k, const uint16_t *residual, const uint16_t *gamma, float eps,
+                                  uint16_t *residual_out, uint16_t *normed_out, hipStream_t s)
+{
+    // One work-group per token and at most 2^32 - 1 work-items per launch:
+    // longer batches go in launches of 2^22 tokens (256-thread groups).
+    constexpr int64_t kPiece = int64_t(1) << 22;
+    for (int64_t t0 = 0; t0 < T; t0 += kPiece) {
+        const int64_t n = T - t0 < kPiece ? T - t0 : kPiece;
+        const int64_t r = t0 * H;
+        const hipError_t e = launch_tokens(y, nrows, H, token_slot + t0 * k, w + t0 * k, n, k, residual + r, gamma,
+                                           eps, residual_out + r, normed_out + r, s);
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace moe

@@ -602,6 +602,18 @@ void choose_split(int64_t T, int nunits, int max_per_lane, int target, int *vpl,
     *segs = (nunits + v * kWave - 1) / (v * kWave);
 }
 
+// The pack grid for rows of width H: vectors (bf16) or 16-element groups
+// (fp8) per lane, and row segments per token.  False when the grid would
+// exceed the launch limit.
+bool pack_split(int64_t T, int H, int k, int dtype, int *vpl, int *segs)
+{
+    if (dtype == 0)
+        choose_split(T, H / 8, kMaxV, k >= 8 ? 1 : 8 / k, vpl, segs);
+    else
+        choose_split(T, H / 16, kMaxG, 2, vpl, segs);
+    return grid_fits((T * *segs + kWavesPerBlock - 1) / kWavesPerBlock, kBlock);
+}
+
 // The pack launch shared by every path: `masks` (router membership words of
 // 32-token chunks) or chunk_counts + local_rank (256-token chunks) give the
 // counts; offs selects the packed layout.
@@ -614,13 +626,11 @@ hipError_t launch_pack(const uint16_t *x, int64_t T, int H, const int32_t *topk_
     const size_t lds = local ? (size_t)(E * kMaskWords + (offs ? E + 1 : 0)) * 4 : 0;
     const int lpp = pair_lanes(k);
     int vpl, segs;
+    if (!pack_split(T, H, k, dtype, &vpl, &segs))
+        return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)((T * segs + kWavesPerBlock - 1) / kWavesPerBlock));
     if (dtype == 0) {
         const int nvec = H / 8;
-        choose_split(T, nvec, kMaxV, k >= 8 ? 1 : 8 / k, &vpl, &segs);
-        const int64_t blocks = (T * segs + kWavesPerBlock - 1) / kWavesPerBlock;
-        if (!grid_fits(blocks, kBlock))
-            return hipErrorInvalidConfiguration;
-        const dim3 grid((unsigned)blocks);
 #define MOE_PACK_BF16(V)                                                                                         \
     hipLaunchKernelGGL(dispatch_pack_bf16_kernel<V>, grid, dim3(kBlock), lds, s, (const u32x4 *)x, T, nvec, topk_idx, \
                        local_rank, chunk_counts, masks, offs, E, k, C, nchunks, lpp, segs, token_slot, recv_src,            \
@@ -635,11 +645,6 @@ hipError_t launch_pack(const uint16_t *x, int64_t T, int H, const int32_t *topk_
 #undef MOE_PACK_BF16
     } else {
         const int ngrp = H / 16;
-        choose_split(T, ngrp, kMaxG, 2, &vpl, &segs);
-        const int64_t blocks = (T * segs + kWavesPerBlock - 1) / kWavesPerBlock;
-        if (!grid_fits(blocks, kBlock))
-            return hipErrorInvalidConfiguration;
-        const dim3 grid((unsigned)blocks);
 #define MOE_PACK_FP8(V)                                                                                          \
     hipLaunchKernelGGL(dispatch_pack_fp8_kernel<V>, grid, dim3(kBlock), lds, s, (const u32x4 *)x, T, ngrp, topk_idx,  \
                        local_rank, chunk_counts, masks, offs, E, k, C, nchunks, lpp, segs, token_slot, recv_src,            \
@@ -656,6 +661,12 @@ hipError_t launch_pack(const uint16_t *x, int64_t T, int H, const int32_t *topk_
 }
 
 }  // namespace
+
+bool dispatch_grid_fits(int64_t T, int H, int k, int dtype)
+{
+    int vpl, segs;
+    return pack_split(T, H, k, dtype, &vpl, &segs);
+}
 
 size_t dispatch_workspace_bytes(int64_t T, int E, int k)
 {
@@ -676,6 +687,8 @@ hipError_t launch_dispatch(const uint16_t *x, int64_t T, int H, const int32_t *t
         hipLaunchKernelGGL(dispatch_zero_counts_kernel, dim3((n + kBlock - 1) / kBlock), dim3(kBlock), 0, s, zero, n);
         return hipGetLastError();
     }
+    if (!dispatch_grid_fits(T, H, k, dtype))   // before anything is enqueued
+        return hipErrorInvalidConfiguration;
     const int nchunks = (int)((T + kChunk - 1) / kChunk);
     if (nchunks == 1)   // one chunk: pack counts it itself, no count launch
         return launch_pack(x, T, H, topk_idx, nullptr, nullptr, nullptr, expert_offsets, E, k, C, 1, dtype, recv_x,
@@ -706,6 +719,8 @@ hipError_t launch_route_dispatch(const float *logits, int64_t T, int E, int k, c
                            expert_counts, E);
         return hipGetLastError();
     }
+    if (!dispatch_grid_fits(T, H, k, dtype))
+        return hipErrorInvalidConfiguration;
     // E <= 8: the router writes 32-token membership words and pack derives
     // the slots from them (two launches).  Otherwise, or when the prefix
     // over those words would exceed 64 loads per lane: route, count, pack.

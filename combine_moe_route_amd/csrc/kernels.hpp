@@ -28,6 +28,11 @@ hipError_t launch_route_topk_grouped(const float *logits, int64_t T, int E, int 
 
 size_t dispatch_workspace_bytes(int64_t T, int E, int k);
 
+// Whether the pack (dispatch) or combine launch grid for this shape stays
+// within one launch's 2^32 - 1 work-items (host-only, no HIP call).
+bool dispatch_grid_fits(int64_t T, int H, int k, int dtype);
+bool combine_grid_fits(int64_t T, int H, int k);
+
 // expert_offsets != NULL selects the packed layout (C and expert_counts
 // unused); otherwise fixed slots of C rows per expert.
 hipError_t launch_dispatch(const uint16_t *x, int64_t T, int H, const int32_t *topk_idx, int E, int k, int C,

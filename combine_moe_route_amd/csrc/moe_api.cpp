@@ -65,6 +65,8 @@ int dispatch_checked(const uint16_t *x, int64_t T, int32_t H, const int32_t *top
     const size_t need = moe::dispatch_workspace_bytes(T, E, k);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
         return MOE_ERR_WORKSPACE;
+    if (!moe::dispatch_grid_fits(T, H, k, out_dtype))
+        return MOE_ERR_UNSUPPORTED;
     (void)hipGetLastError();
     return from_hip(moe::launch_dispatch(x, T, H, topk_idx, E, k, capacity, out_dtype, recv_x, recv_scales,
                                          recv_src, expert_counts, expert_offsets, token_slot, workspace, stream));
@@ -183,6 +185,8 @@ MOE_API int moe_route_dispatch(const float *logits, int64_t T, int32_t E, int32_
     const size_t need = moe::dispatch_workspace_bytes(T, E, k);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
         return MOE_ERR_WORKSPACE;
+    if (!moe::dispatch_grid_fits(T, H, k, out_dtype))
+        return MOE_ERR_UNSUPPORTED;
     (void)hipGetLastError();
     return from_hip(moe::launch_route_dispatch(logits, T, E, k, x, H, capacity, out_dtype, topk_idx, topk_w, recv_x,
                                                recv_scales, recv_src, expert_counts, token_slot, workspace, stream));
@@ -221,6 +225,8 @@ int combine_checked(const uint16_t *y, int32_t E, int32_t capacity, int32_t H, c
     const uintptr_t o0 = (uintptr_t)out, o1 = o0 + (uintptr_t)T * H * 2;
     if (o0 < y1 && y0 < o1)
         return MOE_ERR_INVALID;  // out overlaps y
+    if (!moe::combine_grid_fits(T, H, k))
+        return MOE_ERR_UNSUPPORTED;
     (void)hipGetLastError();
     return from_hip(
         moe::launch_combine(y, (int64_t)E * capacity, H, token_slot, topk_w, T, k, out, stream, start, stop));

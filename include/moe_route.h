@@ -66,6 +66,10 @@ extern "C" {
 #define MOE_MAX_GROUPS 64         /* expert groups of moe_route_topk_grouped */
 #define MOE_MAX_NORM_HIDDEN 16384 /* H of moe_combine_residual_rmsnorm */
 #define MOE_MAX_TOKENS (1 << 24)  /* T above this is MOE_ERR_UNSUPPORTED */
+/* Also MOE_ERR_UNSUPPORTED: a dispatch or combine shape whose single kernel
+ * launch would need more than 2^32 - 1 work-items.  Each lane moves at least
+ * 128 bytes of row data per copy, so only rows wider than 32768 elements at
+ * MOE_MAX_TOKENS tokens come near it (about a terabyte of activations). */
 
 /* Text for a status code (static storage, never NULL). */
 MOE_API const char *moe_status_string(int status);

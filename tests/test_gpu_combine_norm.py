@@ -4,13 +4,13 @@ and RMSNorm right after the sum) through the C ABI, against the CPU oracle.
 
 residual_out must be bit-identical (the same fp32 operations in the same
 order as the oracle: combine's fma chain, one fp32 add, nearest-even bf16).
-normed_out within one bf16 ulp: the oracle evaluates the norm in double and
-rounds once, the kernel in fp32 with its own order for the sum of squares
-(relative error ~2^-20 before the final rounding), so an element can land on
-the other side of a rounding midpoint.  Cases: the five workloads at full
-size (fixed slots), the packed layout, in-place residual update, dropped
-pairs, row widths on every vector-count path, k from 1 to 16, eps = 0 with
-constant rows, and canaries past the outputs.
+normed_out within one bf16 ulp: both sides evaluate the norm in double and
+round once, but the kernel adds the squares in its own order, so an element
+can land on the other side of a rounding midpoint.  Cases: the five
+workloads at full size (fixed slots), the packed layout, in-place residual
+update, dropped pairs, row widths on every vector-count path, k from 1 to
+16, eps = 0 with constant rows, a batch long enough to take several
+launches, and canaries past the outputs.
 """
 import numpy as np
 import pytest
@@ -129,3 +129,28 @@ def test_empty(dev):
                                             torch.empty(0, 64, dtype=torch.bfloat16, device=dev),
                                             torch.ones(64, dtype=torch.bfloat16, device=dev))
     assert r.shape == (0, 64) and n.shape == (0, 64)
+
+
+def test_batch_longer_than_one_launch(dev):
+    """One work-group per token and at most 2^32 - 1 work-items per launch:
+    a batch of more than 2^22 tokens is run as several launches.  The tokens
+    on both sides of the piece boundary, the first and last ones and a random
+    sample are checked against the oracle; every row is checked for being
+    written."""
+    piece = 1 << 22
+    T, H, k = piece + 300, 8, 2
+    rng = np.random.default_rng(22)
+    slot = np.arange(T * k, dtype=np.int32).reshape(T, k)
+    slot[rng.random((T, k)) < 0.1] = -1
+    wt = rng.random((T, k), dtype=np.float32)
+    y_bits = _bf16(rng.standard_normal((T * k, H), dtype=np.float32))
+    res_bits = _bf16(rng.standard_normal((T, H), dtype=np.float32))
+    gamma_bits = _bf16(rng.uniform(0.5, 1.5, H))
+    say(f"[combine+norm] T={T} (two launches) H={H} k={k}")
+    res_g, normed_g = _run(dev, to_dev_bf16(y_bits, dev).view(1, T * k, H), slot, wt, res_bits, gamma_bits, 1e-6)
+    assert not (normed_g == SENT_BF16).all(axis=1).any()
+    picks = np.unique(np.concatenate([np.arange(0, 64), np.arange(piece - 200, T), rng.integers(0, T, 2000)]))
+    y_pairs = np.where((slot.reshape(-1) >= 0)[:, None], y_bits, 0).astype(np.uint16).reshape(T, k, H)
+    res_o, normed_o = oracle.combine_residual_rmsnorm(y_pairs[picks].reshape(-1, H), slot[picks], wt[picks],
+                                                      res_bits[picks], gamma_bits, 1e-6)
+    _compare(f"T={T}, {picks.size} sampled tokens", res_g[picks], normed_g[picks], res_o, normed_o)

@@ -129,3 +129,32 @@ def test_host_validation_without_device(lib):
     assert d(P, 4, 100, P, 8, 2, 4, 0, P, P, P, P, P, P, 0, P) == -2    # H % 8
     assert d(P, 4, 192, P, 8, 2, 4, 1, P, P, P, P, P, P, 0, P) == -2    # fp8 needs H % 128
     assert d(P, 4, 64, P, 8, 9, 4, 0, P, P, P, P, P, P, 0, P) == -1     # k > E
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="passes fake device addresses; host-only check")
+def test_grids_beyond_one_launch_are_unsupported(lib):
+    """A dispatch or combine whose single launch would need more than 2^32 - 1
+    work-items is refused on the host with MOE_ERR_UNSUPPORTED before
+    anything is enqueued (T = 2^24 tokens of 65536 elements)."""
+    A = 1 << 20                                  # fake, 256 B aligned addresses, never dereferenced
+    T, H, E, k = 1 << 24, 65536, 8, 2
+    ws = moe.moe_dispatch_workspace_bytes(T, E, k)
+    assert ws > 0
+    d = lib.moe_dispatch
+    for dtype, scales in ((0, None), (1, A + 3 * 256)):
+        assert d(A, T, H, A + 256, E, k, T, dtype, A + 2 * 256, scales, A + 4 * 256, A + 5 * 256, A + 6 * 256,
+                 A, ws, None) == -2
+    assert lib.moe_dispatch_packed(A, T, H, A + 256, E, k, 0, A + 2 * 256, None, A + 4 * 256, A + 5 * 256,
+                                   A + 6 * 256, A, ws, None) == -2
+    assert lib.moe_route_dispatch(A + 7 * 256, T, E, k, A, H, T, 0, A + 256, A + 8 * 256, A + 2 * 256, None,
+                                  A + 4 * 256, A + 5 * 256, A + 6 * 256, A, ws, None) == -2
+    # combine: y of E x C rows, out placed after it
+    y_bytes = E * 4 * H * 2
+    assert lib.moe_combine(A, E, 4, H, A + y_bytes, A + y_bytes + 256, T, k, A + (1 << 30), None) == -2
+    # control: at H = 4096 the same calls pass every host check and reach the
+    # launch, which fails with MOE_ERR_HIP on a host without a GPU
+    h = 4096
+    assert d(A, T, h, A + 256, E, k, T, 0, A + 2 * 256, None, A + 4 * 256, A + 5 * 256, A + 6 * 256, A, ws,
+             None) == -4
+    assert lib.moe_combine(A, E, 4, h, A + E * 4 * h * 2, A + E * 4 * h * 2 + 256, T, k, A + (1 << 30),
+                           None) == -4
