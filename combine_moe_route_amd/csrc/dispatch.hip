@@ -212,11 +212,30 @@ __device__ __forceinline__ void store_stream(float *p, float v) { __builtin_nont
 
 // A batch of at most 256 tokens is one chunk: every pack work-group then
 // rebuilds that chunk's membership masks from the ids itself (T*k ids, read
-// from L2), so no count launch is needed.  lds: [E][8] mask words, then for
-// the packed layout [E+1] offsets (the exclusive scan of the popcounts).
-// Work-group 0 publishes the totals (or offsets).  All threads must call it.
-__device__ __forceinline__ void local_chunk_counts(const int32_t *__restrict__ topk_idx, int64_t T, int E, int k,
-                                                   bool packed, uint32_t *lmask, int32_t *loffs, int32_t *wave_sums,
+// from L2), so no count launch is needed.  The ids are requested before the
+// row loads (local_ids_load): vector loads retire in order, so waiting for
+// ids issued after the rows would wait for the rows too.  lds: [E][8] mask
+// words, then for the packed layout [E+1] offsets (the exclusive scan of the
+// popcounts).  Work-group 0 publishes the totals (or offsets).  All threads
+// must call both.
+constexpr int kLocalIds = kChunk * 16 / kBlock;   // ids per thread: T*k <= 256 * MOE_MAX_TOPK
+
+// The single-chunk loads are issued unconditionally, from a clamped
+// (in-bounds) index, and unwanted values discarded afterwards: a load under a
+// branch makes the compiler wait for every outstanding load before the first
+// use, which would make the counting wait for the rows.
+__device__ __forceinline__ void local_ids_load(const int32_t *__restrict__ topk_idx, int n, int (&ids)[kLocalIds])
+{
+#pragma unroll
+    for (int q = 0; q < kLocalIds; ++q) {
+        const int p = (int)threadIdx.x + q * kBlock;
+        const int v = topk_idx[p < n ? p : n - 1];
+        ids[q] = p < n ? v : -1;
+    }
+}
+
+__device__ __forceinline__ void local_chunk_counts(const int (&ids)[kLocalIds], int E, int k, bool packed,
+                                                   uint32_t *lmask, int32_t *loffs, int32_t *wave_sums,
                                                    int32_t *__restrict__ expert_counts,
                                                    int32_t *__restrict__ expert_offsets)
 {
@@ -224,11 +243,12 @@ __device__ __forceinline__ void local_chunk_counts(const int32_t *__restrict__ t
     for (int i = tid; i < E * kMaskWords; i += kBlock)
         lmask[i] = 0u;
     __syncthreads();
-    if (tid < T) {
-        for (int j = 0; j < k; ++j) {
-            const int e = topk_idx[(int64_t)tid * k + j];
-            if ((unsigned)e < (unsigned)E)
-                atomicOr(&lmask[e * kMaskWords + (tid >> 5)], 1u << (tid & 31));
+#pragma unroll
+    for (int q = 0; q < kLocalIds; ++q) {
+        const int e = ids[q];   // pair p = tid + q*256 of token p / k; -1 past the end
+        if ((unsigned)e < (unsigned)E) {
+            const int tok = (tid + q * kBlock) / k;
+            atomicOr(&lmask[e * kMaskWords + (tok >> 5)], 1u << (tok & 31));
         }
     }
     __syncthreads();
@@ -252,12 +272,30 @@ __device__ __forceinline__ void local_chunk_counts(const int32_t *__restrict__ t
     }
 }
 
+// The expert id (and for 256-token chunks the in-chunk rank) of pair
+// (t, lane / lanes_per_pair); -1 for lanes that own no pair.
+struct PairIds {
+    int e, r;
+};
+
+__device__ __forceinline__ PairIds load_pair_ids(const int32_t *__restrict__ topk_idx,
+                                                 const int32_t *__restrict__ local_rank, bool active, int64_t t, int k,
+                                                 int lanes_per_pair)
+{
+    const int j = lane_id() / lanes_per_pair;
+    const bool own = active && j < k;
+    const int64_t q = (active ? t : 0) * k + (j < k ? j : k - 1);
+    const int e = topk_idx[q];
+    const int r = local_rank ? local_rank[q] : -1;
+    return {own ? e : -1, own ? r : -1};
+}
+
 // Slot of pair (t, j) for the lanes that own it, -1 elsewhere.  L =
 // lanes_per_pair lanes serve pair j = lane / L: they load the expert id and
-// in-chunk rank, and sum the expert's counts over all earlier 256-token
-// chunks (the exclusive prefix, read from the L2-resident chunk histograms
-// with up to 8 independent loads per lane in flight), then a butterfly
-// within the L lanes.  Fixed slots (offs == NULL): slot = e*C + prefix +
+// in-chunk rank (or take them from `pre` when PRE, the single-chunk
+// kernels), and sum the expert's counts over all earlier 256-token chunks
+// (the exclusive prefix, read from the L2-resident chunk histograms in
+// groups of eight per lane), then a butterfly within the L lanes.  Fixed slots (offs == NULL): slot = e*C + prefix +
 // rank, or -1 when that is >= C.  Packed (offs != NULL): slot = offs[e] +
 // prefix + rank.  -1 for an id out of range.  The value is valid in lane
 // j*L.
@@ -270,7 +308,9 @@ __device__ __forceinline__ void local_chunk_counts(const int32_t *__restrict__ t
 // With lmask != NULL (a single chunk, masks rebuilt in LDS) the rank comes
 // from the LDS words, there is no earlier chunk, and the packed offsets are
 // loffs (LDS).
-__device__ __forceinline__ int wave_slot(const int32_t *__restrict__ topk_idx, const int32_t *__restrict__ local_rank,
+template <bool PRE>
+__device__ __forceinline__ int wave_slot(PairIds pre, const int32_t *__restrict__ topk_idx,
+                                         const int32_t *__restrict__ local_rank,
                                          const int32_t *__restrict__ chunk_counts, const uint32_t *__restrict__ masks,
                                          const int32_t *__restrict__ offs, const uint32_t *lmask, const int32_t *loffs,
                                          int64_t t, int E, int k, int C, int nchunks, int lanes_per_pair)
@@ -281,7 +321,7 @@ __device__ __forceinline__ int wave_slot(const int32_t *__restrict__ topk_idx, c
     const int c = (int)(masks ? t / kMaskChunk : t / kChunk);
     int e = -1, r = -1, sum = 0, base = 0;
     if (j < k) {
-        e = topk_idx[t * k + j];
+        e = PRE ? pre.e : topk_idx[t * k + j];
         if ((unsigned)e < (unsigned)E) {
             if (offs)
                 base = lmask ? loffs[e] : offs[e];
@@ -305,7 +345,7 @@ __device__ __forceinline__ int wave_slot(const int32_t *__restrict__ topk_idx, c
                         sum += __popc(part[u]);
                 }
             } else {
-                r = local_rank[t * k + j];
+                r = PRE ? pre.r : local_rank[t * k + j];
                 const int32_t *row = chunk_counts + (int64_t)e * nchunks;
                 for (int b0 = sub; b0 < c; b0 += 8 * lanes_per_pair) {
                     int part[8];
@@ -371,19 +411,19 @@ constexpr int kMaxV = 16;  // most 16-byte vectors per lane in flight (bf16 rows
 // arithmetic runs while they are in flight; then every vector is stored to
 // each of the k slots.  No work-group barrier: the waves' latency chains
 // overlap freely.
-template <int VPL>
+template <int VPL, bool LOCAL>
 __global__ __launch_bounds__(kBlock) void dispatch_pack_bf16_kernel(
     const u32x4 *__restrict__ x, int64_t T, int nvec, const int32_t *__restrict__ topk_idx,
     const int32_t *__restrict__ local_rank, const int32_t *__restrict__ chunk_counts,
     const uint32_t *__restrict__ masks, int32_t *offs, int E, int k, int C, int nchunks, int lanes_per_pair,
     int segs,
     int32_t *__restrict__ token_slot, int32_t *__restrict__ recv_src, int32_t *__restrict__ expert_counts,
-    u32x4 *__restrict__ recv_x, int local)
+    u32x4 *__restrict__ recv_x)
 {
     extern __shared__ uint32_t lds_words[];  // local counting only: masks, then packed offsets
     __shared__ int32_t wave_sums[kWavesPerBlock];
-    uint32_t *lmask = local ? lds_words : nullptr;
-    int32_t *loffs = local && offs ? (int32_t *)(lds_words + E * kMaskWords) : nullptr;
+    uint32_t *lmask = LOCAL ? lds_words : nullptr;
+    int32_t *loffs = LOCAL && offs ? (int32_t *)(lds_words + E * kMaskWords) : nullptr;
     const int lane = lane_id();
     const int64_t task = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
     const int64_t t = task / segs;
@@ -391,22 +431,37 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_bf16_kernel(
     const bool active = t < T;
     const u32x4 *src = x + (active ? t : 0) * nvec;
     const int v0 = seg * VPL * kWave + lane;
+    // One chunk: the ids are requested first and the row loads carry no
+    // branch, so the LDS counting waits for the ids but not for the rows.
+    // Otherwise wave_slot loads the ids after the rows are requested (moving
+    // them ahead was measured slower there).
+    PairIds ids = {-1, -1};
+    int lids[kLocalIds];
+    if (LOCAL) {
+        ids = load_pair_ids(topk_idx, local_rank, active, t, k, lanes_per_pair);
+        local_ids_load(topk_idx, (int)T * k, lids);
+    }
     u32x4 buf[VPL];
 #pragma unroll
-    for (int i = 0; i < VPL; ++i)
-        buf[i] = active && v0 + i * kWave < nvec ? src[v0 + i * kWave] : (u32x4){0, 0, 0, 0};
+    for (int i = 0; i < VPL; ++i) {
+        const int v = v0 + i * kWave;
+        if (LOCAL)   // lanes past the row end load its last vector and store nothing
+            buf[i] = src[v < nvec ? v : nvec - 1];
+        else
+            buf[i] = active && v < nvec ? src[v] : (u32x4){0, 0, 0, 0};
+    }
     // (local counting overlaps the row loads; every thread takes part)
-    if (local)
-        local_chunk_counts(topk_idx, T, E, k, offs != nullptr, lds_words, (int32_t *)(lds_words + E * kMaskWords),
+    if (LOCAL)
+        local_chunk_counts(lids, E, k, offs != nullptr, lds_words, (int32_t *)(lds_words + E * kMaskWords),
                            wave_sums, expert_counts, offs);
     if (!active)
         return;
 
-    const int slot = wave_slot(topk_idx, local_rank, chunk_counts, masks, offs, lmask, loffs, t, E, k, C, nchunks,
-                               lanes_per_pair);
+    const int slot = wave_slot<LOCAL>(ids, topk_idx, local_rank, chunk_counts, masks, offs, lmask, loffs, t, E, k, C,
+                                      nchunks, lanes_per_pair);
     if (seg == 0)
         record_slot(slot, t, k, lanes_per_pair, token_slot, recv_src);
-    if (task < E && expert_counts && !local)
+    if (task < E && expert_counts && !LOCAL)
         wave_totals(task, T * segs, chunk_counts, masks, E, nchunks, expert_counts);
 
 #pragma unroll 1
@@ -475,14 +530,14 @@ constexpr int kMaxG = 8;   // most 16-element groups per lane in flight (fp8 row
 // amax/448 (IEEE division; 1 for an all-zero block) and each code is the
 // E4M3 encoding (round to nearest even, saturating) of x / scale, with the
 // quotient bit-identical to an IEEE division (divide_by_scale).
-template <int VPL>
+template <int VPL, bool LOCAL>
 __global__ __launch_bounds__(kBlock) void dispatch_pack_fp8_kernel(
     const u32x4 *__restrict__ x, int64_t T, int ngrp, const int32_t *__restrict__ topk_idx,
     const int32_t *__restrict__ local_rank, const int32_t *__restrict__ chunk_counts,
     const uint32_t *__restrict__ masks, int32_t *offs, int E, int k, int C, int nchunks, int lanes_per_pair,
     int segs,
     int32_t *__restrict__ token_slot, int32_t *__restrict__ recv_src, int32_t *__restrict__ expert_counts,
-    u32x4 *__restrict__ recv_x, float *__restrict__ recv_scales, int local)
+    u32x4 *__restrict__ recv_x, float *__restrict__ recv_scales)
 {
     // the wave's block scales, staged so each slot's scale segment is
     // written by one contiguous store instruction
@@ -490,8 +545,8 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_fp8_kernel(
     float *my_scale = s_scale[threadIdx.x / kWave];
     extern __shared__ uint32_t lds_words[];  // local counting only: masks, then packed offsets
     __shared__ int32_t wave_sums[kWavesPerBlock];
-    uint32_t *lmask = local ? lds_words : nullptr;
-    int32_t *loffs = local && offs ? (int32_t *)(lds_words + E * kMaskWords) : nullptr;
+    uint32_t *lmask = LOCAL ? lds_words : nullptr;
+    int32_t *loffs = LOCAL && offs ? (int32_t *)(lds_words + E * kMaskWords) : nullptr;
     const int lane = lane_id();
     const int64_t task = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
     const int64_t t = task / segs;
@@ -500,27 +555,40 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_fp8_kernel(
     const u32x4 *src = x + (active ? t : 0) * (int64_t)ngrp * 2;
     const int nblk = ngrp / 8;
     const int g0 = seg * VPL * kWave + lane;
+    PairIds ids = {-1, -1};   // the same load order as the bf16 kernel
+    int lids[kLocalIds];
+    if (LOCAL) {
+        ids = load_pair_ids(topk_idx, local_rank, active, t, k, lanes_per_pair);
+        local_ids_load(topk_idx, (int)T * k, lids);
+    }
     u32x4 lo[VPL], hi[VPL];
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
-        lo[i] = hi[i] = (u32x4){0, 0, 0, 0};
-        if (active && g0 + i * kWave < ngrp) {
-            lo[i] = src[2 * (g0 + i * kWave)];
-            hi[i] = src[2 * (g0 + i * kWave) + 1];
+        const int g = g0 + i * kWave;
+        if (LOCAL) {   // lanes past the row end load its last group and store nothing
+            const int gc = g < ngrp ? g : ngrp - 1;
+            lo[i] = src[2 * gc];
+            hi[i] = src[2 * gc + 1];
+        } else {
+            lo[i] = hi[i] = (u32x4){0, 0, 0, 0};
+            if (active && g < ngrp) {
+                lo[i] = src[2 * g];
+                hi[i] = src[2 * g + 1];
+            }
         }
     }
     // (local counting overlaps the row loads; every thread takes part)
-    if (local)
-        local_chunk_counts(topk_idx, T, E, k, offs != nullptr, lds_words, (int32_t *)(lds_words + E * kMaskWords),
+    if (LOCAL)
+        local_chunk_counts(lids, E, k, offs != nullptr, lds_words, (int32_t *)(lds_words + E * kMaskWords),
                            wave_sums, expert_counts, offs);
     if (!active)
         return;
 
-    const int slot = wave_slot(topk_idx, local_rank, chunk_counts, masks, offs, lmask, loffs, t, E, k, C, nchunks,
-                               lanes_per_pair);
+    const int slot = wave_slot<LOCAL>(ids, topk_idx, local_rank, chunk_counts, masks, offs, lmask, loffs, t, E, k, C,
+                                      nchunks, lanes_per_pair);
     if (seg == 0)
         record_slot(slot, t, k, lanes_per_pair, token_slot, recv_src);
-    if (task < E && expert_counts && !local)
+    if (task < E && expert_counts && !LOCAL)
         wave_totals(task, T * segs, chunk_counts, masks, E, nchunks, expert_counts);
 
 #pragma unroll
@@ -631,10 +699,17 @@ hipError_t launch_pack(const uint16_t *x, int64_t T, int H, const int32_t *topk_
     const dim3 grid((unsigned)((T * segs + kWavesPerBlock - 1) / kWavesPerBlock));
     if (dtype == 0) {
         const int nvec = H / 8;
+#define MOE_PACK_BF16_L(V, L)                                                                                      \
+    hipLaunchKernelGGL((dispatch_pack_bf16_kernel<V, L>), grid, dim3(kBlock), lds, s, (const u32x4 *)x, T, nvec,      \
+                       topk_idx, local_rank, chunk_counts, masks, offs, E, k, C, nchunks, lpp, segs, token_slot,           \
+                       recv_src, expert_counts, (u32x4 *)recv_x)
 #define MOE_PACK_BF16(V)                                                                                         \
-    hipLaunchKernelGGL(dispatch_pack_bf16_kernel<V>, grid, dim3(kBlock), lds, s, (const u32x4 *)x, T, nvec, topk_idx, \
-                       local_rank, chunk_counts, masks, offs, E, k, C, nchunks, lpp, segs, token_slot, recv_src,            \
-                       expert_counts, (u32x4 *)recv_x, (int)local)
+    do {                                                                                                         \
+        if (local)                                                                                               \
+            MOE_PACK_BF16_L(V, true);                                                                            \
+        else                                                                                                     \
+            MOE_PACK_BF16_L(V, false);                                                                           \
+    } while (0)
         switch (vpl) {
         case 1: MOE_PACK_BF16(1); break;
         case 2: MOE_PACK_BF16(2); break;
@@ -643,12 +718,20 @@ hipError_t launch_pack(const uint16_t *x, int64_t T, int H, const int32_t *topk_
         default: MOE_PACK_BF16(16); break;
         }
 #undef MOE_PACK_BF16
+#undef MOE_PACK_BF16_L
     } else {
         const int ngrp = H / 16;
+#define MOE_PACK_FP8_L(V, L)                                                                                       \
+    hipLaunchKernelGGL((dispatch_pack_fp8_kernel<V, L>), grid, dim3(kBlock), lds, s, (const u32x4 *)x, T, ngrp,       \
+                       topk_idx, local_rank, chunk_counts, masks, offs, E, k, C, nchunks, lpp, segs, token_slot,           \
+                       recv_src, expert_counts, (u32x4 *)recv_x, recv_scales)
 #define MOE_PACK_FP8(V)                                                                                          \
-    hipLaunchKernelGGL(dispatch_pack_fp8_kernel<V>, grid, dim3(kBlock), lds, s, (const u32x4 *)x, T, ngrp, topk_idx,  \
-                       local_rank, chunk_counts, masks, offs, E, k, C, nchunks, lpp, segs, token_slot, recv_src,            \
-                       expert_counts, (u32x4 *)recv_x, recv_scales, (int)local)
+    do {                                                                                                         \
+        if (local)                                                                                               \
+            MOE_PACK_FP8_L(V, true);                                                                             \
+        else                                                                                                     \
+            MOE_PACK_FP8_L(V, false);                                                                            \
+    } while (0)
         switch (vpl) {
         case 1: MOE_PACK_FP8(1); break;
         case 2: MOE_PACK_FP8(2); break;
@@ -656,6 +739,7 @@ hipError_t launch_pack(const uint16_t *x, int64_t T, int H, const int32_t *topk_
         default: MOE_PACK_FP8(8); break;
         }
 #undef MOE_PACK_FP8
+#undef MOE_PACK_FP8_L
     }
     return hipGetLastError();
 }
