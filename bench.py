@@ -3,7 +3,8 @@
 
 One step = moe_route_topk (or moe_route_topk_grouped with --route-groups) +
 moe_dispatch (or moe_dispatch_packed with --layout packed) + moe_combine (or
-moe_combine_residual_rmsnorm with --epilogue rmsnorm), back to back on one
+moe_combine_residual_rmsnorm with --epilogue rmsnorm, or its fp8-output form
+moe_combine_residual_rmsnorm_fp8 with --epilogue rmsnorm-fp8), back to back on one
 stream, over one batch of seeded synthetic input already resident in HBM.
 With fixed slots and plain top-k the first two are the single call
 moe_route_dispatch (identical outputs; --separate-route calls them apart).
@@ -41,22 +42,25 @@ if ROOT not in sys.path:
 import workloads as W  # noqa: E402
 
 METRIC = "dispatch+combine tokens/s and effective HBM GB/s (% of peak), 1 MI355X"
+EPILOGUE_LABEL = {None: "", "rmsnorm": "+residual+rmsnorm", "rmsnorm-fp8": "+residual+rmsnorm+fp8"}
 HBM_PEAK_GBPS = 8000.0
 LLC_BYTES = 256 * 2 ** 20
 
 
-def algorithmic_bytes(w: W.Workload, epilogue: bool = False) -> dict:
+def algorithmic_bytes(w: W.Workload, epilogue: str | None = None) -> dict:
     """Bytes each step must move: every row read once and written k times.
-    With the fused residual + RMSNorm epilogue, combine also reads the
-    residual and gamma and writes the updated residual (its normalised rows
-    take the place of the plain output)."""
+    With the fused residual + RMSNorm epilogue ("rmsnorm"), combine also
+    reads the residual and gamma and writes the updated residual (its
+    normalised rows take the place of the plain output); "rmsnorm-fp8"
+    writes the normalised rows as E4M3 codes + per-128 fp32 scales instead."""
     T, H, E, k = w.T, w.H, w.E, w.k
     row = (H + H // 32) if w.fp8 else 2 * H
+    out_row = (H + H // 32) if epilogue == "rmsnorm-fp8" else 2 * H
     b = {
         "route": T * E * 4 + T * k * 8,
         "count_scan_slot": T * k * 12 + E * 4,
         "pack": T * H * 2 + T * k * 4 + T * k * row,
-        "combine": T * k * 2 * H + T * k * 8 + T * H * 2 + ((T * H * 4 + H * 2) if epilogue else 0),
+        "combine": T * k * 2 * H + T * k * 8 + T * out_row + ((T * H * 4 + H * 2) if epilogue else 0),
     }
     b["total"] = sum(b.values())
     return b
@@ -103,10 +107,10 @@ def host_cpu() -> str:
     return "unknown"
 
 
-def cpu_baseline(w: W.Workload, seconds: float, epilogue: bool = False) -> dict:
+def cpu_baseline(w: W.Workload, seconds: float, epilogue: str | None = None) -> dict:
     """Time the CPU oracle (route, slots, pack, combine -- with the residual
-    + RMSNorm epilogue if `epilogue`) on the first min(T, 2048) tokens of the
-    workload, repeated for ~`seconds`."""
+    + RMSNorm epilogue, and its fp8 encoding, if `epilogue` says so) on the
+    first min(T, 2048) tokens of the workload, repeated for ~`seconds`."""
     import numpy as np
     import oracle
 
@@ -123,7 +127,9 @@ def cpu_baseline(w: W.Workload, seconds: float, epilogue: bool = False) -> dict:
         counts, token_slot, recv_src = oracle.assign_slots(idx, ws.E, ws.C)
         oracle.pack(x, oracle.FP8_E4M3 if w.fp8 else oracle.BF16, recv_src, counts, ws.C)
         if epilogue:
-            oracle.combine_residual_rmsnorm(y_pairs, token_slot, wt, residual, gamma, 1e-6)
+            _, normed = oracle.combine_residual_rmsnorm(y_pairs, token_slot, wt, residual, gamma, 1e-6)
+            if epilogue == "rmsnorm-fp8":
+                oracle.quantize_rows_fp8(normed)
         else:
             oracle.combine(y_pairs, token_slot, wt)
         passes += 1
@@ -133,7 +139,7 @@ def cpu_baseline(w: W.Workload, seconds: float, epilogue: bool = False) -> dict:
     tok_s = passes * ts / el
     return {
         "value": tok_s, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-        "sample": f"{passes} passes of route+slots+pack+combine{'+residual+rmsnorm' if epilogue else ''} over the "
+        "sample": f"{passes} passes of route+slots+pack+combine{EPILOGUE_LABEL[epilogue]} over the "
                   f"first {ts} of {w.T} tokens ({w.name}), {el:.1f} s",
         "gbps": algorithmic_bytes(ws, epilogue)["total"] * passes / el / 1e9,
         "host": f"{host_cpu()}, {os.cpu_count()} threads visible",
@@ -144,7 +150,7 @@ class BufferSet:
     """One complete copy of a step's inputs, outputs and fixed-slot buffers."""
 
     def __init__(self, w: W.Workload, logits_cpu, x_cpu, dev, moe, torch, route_groups=None, packed=False,
-                 epilogue=False, fuse_route=True):
+                 epilogue=None, fuse_route=True):
         self.fuse_route = fuse_route
         self.logits = logits_cpu.to(dev)
         self.x = x_cpu.to(dev)
@@ -162,6 +168,9 @@ class BufferSet:
             # residual stream (the activations stand in for it) and RMSNorm weight
             gamma = torch.linspace(0.5, 1.5, w.H, device=dev).to(torch.bfloat16)
             self.epilogue = (self.x, gamma, 1e-6, torch.empty(w.T, w.H, dtype=torch.bfloat16, device=dev))
+            if epilogue == "rmsnorm-fp8":
+                self.epilogue += (torch.empty(w.T, w.H, dtype=torch.uint8, device=dev),
+                                  torch.empty(w.T, w.H // 128, dtype=torch.float32, device=dev))
         self.route_groups = route_groups
         self.step = self.prepare(w, moe)
 
@@ -200,8 +209,9 @@ def main() -> int:
     ap.add_argument("--layout", choices=["fixed", "packed"], default="fixed",
                     help="dispatch layout: fixed slots per expert (moe_dispatch) or packed count-sized rows "
                          "(moe_dispatch_packed)")
-    ap.add_argument("--epilogue", choices=["none", "rmsnorm"], default="none",
-                    help="combine with the fused residual add + RMSNorm (moe_combine_residual_rmsnorm)")
+    ap.add_argument("--epilogue", choices=["none", "rmsnorm", "rmsnorm-fp8"], default="none",
+                    help="combine with the fused residual add + RMSNorm (moe_combine_residual_rmsnorm), or "
+                         "with its rows written as E4M3 + per-128 scales (moe_combine_residual_rmsnorm_fp8)")
     ap.add_argument("--separate-route", action="store_true",
                     help="call moe_route_topk and moe_dispatch separately instead of moe_route_dispatch")
     ap.add_argument("--route-groups", default="",
@@ -228,7 +238,7 @@ def main() -> int:
     w = W.WORKLOADS[args.workload]
     if args.steps <= 0:
         args.steps = 200 if w.T <= 4096 else 50
-    epilogue = args.epilogue == "rmsnorm"
+    epilogue = None if args.epilogue == "none" else args.epilogue
     if epilogue:
         args.timing = "marker"       # the fused kernel has no launch-attached timing entry point
     nbytes = algorithmic_bytes(w, epilogue)
@@ -385,7 +395,8 @@ def main() -> int:
             "route_groups": ({"groups": route_groups[0], "kept": route_groups[1]} if route_groups else None),
             "layout": "packed count-sized rows" if packed else "fixed slots per expert",
             "route_dispatch_call": "moe_route_dispatch" if fuse_route else "separate",
-            "combine_epilogue": "residual add + RMSNorm (fused)" if epilogue else None,
+            "combine_epilogue": {None: None, "rmsnorm": "residual add + RMSNorm (fused)",
+                                 "rmsnorm-fp8": "residual add + RMSNorm, output as E4M3 + fp32/128 (fused)"}[epilogue],
             "parallelism": "none (1 GPU)",
             "algorithmic_bytes_per_step": nbytes["total"],
             "effective_hbm_gbps": gbps,
@@ -398,7 +409,8 @@ def main() -> int:
             "graph_replay": graph,
         },
         "roofline": {
-            "kernel": f"combine_rmsnorm_kernel (k={w.k})" if epilogue else f"combine_kernel<{w.k}>",
+            "kernel": (f"combine_rmsnorm_kernel (k={w.k}{', fp8 out' if epilogue == 'rmsnorm-fp8' else ''})"
+                       if epilogue else f"combine_kernel<{w.k}>"),
             "bound": "hbm",
             "achieved": comb_gbps,
             "peak": HBM_PEAK_GBPS,

@@ -17,6 +17,7 @@ from .binding import (  # noqa: F401
     load,
     moe_combine,
     moe_combine_residual_rmsnorm,
+    moe_combine_residual_rmsnorm_fp8,
     moe_dispatch,
     moe_dispatch_packed,
     moe_dispatch_workspace_bytes,

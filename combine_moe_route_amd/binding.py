@@ -64,6 +64,9 @@ def load() -> ctypes.CDLL:
     lib.moe_combine.restype = ctypes.c_int
     lib.moe_combine_residual_rmsnorm.argtypes = [P, i32, i32, i32, P, P, i64, i32, P, P, ctypes.c_float, P, P, P]
     lib.moe_combine_residual_rmsnorm.restype = ctypes.c_int
+    lib.moe_combine_residual_rmsnorm_fp8.argtypes = [P, i32, i32, i32, P, P, i64, i32, P, P, ctypes.c_float, P, P,
+                                                     P, P, P]
+    lib.moe_combine_residual_rmsnorm_fp8.restype = ctypes.c_int
     lib.moe_combine_timed.argtypes = [P, i32, i32, i32, P, P, i64, i32, P, P, P, P]
     lib.moe_combine_timed.restype = ctypes.c_int
     _lib = lib
@@ -385,6 +388,38 @@ def moe_combine_residual_rmsnorm(y: torch.Tensor, token_slot: torch.Tensor, topk
     return residual_out, normed_out
 
 
+def moe_combine_residual_rmsnorm_fp8(y: torch.Tensor, token_slot: torch.Tensor, topk_w: torch.Tensor,
+                                     residual: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6,
+                                     residual_out: torch.Tensor | None = None, keep_bf16: bool = False,
+                                     stream=None):
+    """moe_combine_residual_rmsnorm with the normalised rows re-quantised to
+    E4M3 with one fp32 scale per 128 elements.  Returns (residual_out,
+    normed_q uint8 [T, H], normed_scales float32 [T, H/128], normed_out bf16
+    [T, H] or None unless keep_bf16)."""
+    if y.dim() == 2:
+        y = y.view(1, max(1, y.shape[0]), y.shape[1]) if y.shape[0] else y.new_empty(1, 1, y.shape[1])
+    E, C, H = y.shape
+    T, k = token_slot.shape
+    _need(y, torch.bfloat16, (E, C, H), "y")
+    _need(token_slot, torch.int32, (T, k), "token_slot")
+    _need(topk_w, torch.float32, (T, k), "topk_w")
+    _need(residual, torch.bfloat16, (T, H), "residual")
+    _need(gamma, torch.bfloat16, (H,), "gamma")
+    if residual_out is None:
+        residual_out = torch.empty(T, H, dtype=torch.bfloat16, device=y.device)
+    _need(residual_out, torch.bfloat16, (T, H), "residual_out")
+    normed_out = torch.empty(T, H, dtype=torch.bfloat16, device=y.device) if keep_bf16 else None
+    normed_q = torch.empty(T, H, dtype=torch.uint8, device=y.device)
+    normed_scales = torch.empty(T, max(H // 128, 0), dtype=torch.float32, device=y.device)
+    rc = load().moe_combine_residual_rmsnorm_fp8(_ptr(y), E, C, H, _ptr(token_slot), _ptr(topk_w), T, k,
+                                                 _ptr(residual), _ptr(gamma), float(eps), _ptr(residual_out),
+                                                 _ptr(normed_out),
+                                                 _ptr(normed_q), _ptr(normed_scales), _stream(stream))
+    if rc != MOE_OK:
+        raise MoeError("moe_combine_residual_rmsnorm_fp8", rc)
+    return residual_out, normed_q, normed_scales, normed_out
+
+
 class PreparedStep:
     """Route, dispatch and combine with their arguments marshalled once.
     `bufs` selects the layout: DispatchBuffers (fixed slots; y [E, C, H]) or
@@ -403,7 +438,10 @@ class PreparedStep:
         """route_groups = (n_groups, topk_groups) routes with
         moe_route_topk_grouped instead of moe_route_topk.  epilogue =
         (residual, gamma, eps, residual_out) combines with
-        moe_combine_residual_rmsnorm, writing the normalised rows to `out`.
+        moe_combine_residual_rmsnorm, writing the normalised rows to `out`;
+        (residual, gamma, eps, residual_out, normed_q, normed_scales) with
+        moe_combine_residual_rmsnorm_fp8, writing only their E4M3 codes and
+        block scales.
         fuse_route: route_and_dispatch() uses moe_route_dispatch (fixed slots
         and plain top-k only)."""
         T, E = logits.shape
@@ -452,13 +490,23 @@ class PreparedStep:
                                 _ptr(bufs.recv_x), scales, _ptr(bufs.recv_src), _ptr(bufs.expert_counts),
                                 _ptr(bufs.token_slot), _ptr(bufs.workspace), bufs.workspace.numel(), s)
         self._epilogue_args = None
+        self._epilogue_fn = None
         if epilogue is not None:
-            residual, gamma, eps, residual_out = epilogue
+            residual, gamma, eps, residual_out = epilogue[:4]
             _need(residual, torch.bfloat16, (T, H), "residual")
             _need(gamma, torch.bfloat16, (H,), "gamma")
             _need(residual_out, torch.bfloat16, (T, H), "residual_out")
             c = self.combine_args
-            self._epilogue_args = (*c[:8], _ptr(residual), _ptr(gamma), float(eps), _ptr(residual_out), _ptr(out), s)
+            head = (*c[:8], _ptr(residual), _ptr(gamma), float(eps), _ptr(residual_out))
+            if len(epilogue) == 6:
+                normed_q, normed_scales = epilogue[4:]
+                _need(normed_q, torch.uint8, (T, H), "normed_q")
+                _need(normed_scales, torch.float32, (T, H // 128), "normed_scales")
+                self._epilogue_fn = "moe_combine_residual_rmsnorm_fp8"
+                self._epilogue_args = (*head, None, _ptr(normed_q), _ptr(normed_scales), s)
+            else:
+                self._epilogue_fn = "moe_combine_residual_rmsnorm"
+                self._epilogue_args = (*head, _ptr(out), s)
         self._keep = (logits, x, bufs, y, out, topk_idx, topk_w, epilogue)
 
     def route_and_dispatch(self):
@@ -484,9 +532,9 @@ class PreparedStep:
 
     def combine(self):
         if self._epilogue_args is not None:
-            rc = self._lib.moe_combine_residual_rmsnorm(*self._epilogue_args)
+            rc = getattr(self._lib, self._epilogue_fn)(*self._epilogue_args)
             if rc != MOE_OK:
-                raise MoeError("moe_combine_residual_rmsnorm", rc)
+                raise MoeError(self._epilogue_fn, rc)
             return
         rc = self._lib.moe_combine(*self.combine_args)
         if rc != MOE_OK:

@@ -23,13 +23,19 @@
 // root), and every kept value is written as (r * inv) * gamma rounded from
 // double to bf16 in one step.  The only difference from an exact evaluation
 // is the order of the double sum of squares.
+//
+// With Q the normalised row is also re-quantised for an fp8 consumer: the
+// same E4M3 block encoding as dispatch's fp8 rows (handbook "NVSHMEM and
+// DeepEP", "High-throughput mode"), applied to the bf16 normalised values.
+// The 16 consecutive lanes (one DPP row) holding a 128-element block share
+// its maximum through four DPP steps; each lane stores its 8 codes (8 bytes) and the
+// block's first lane its scale.  The bf16 normalised row is then optional.
 #include "device_common.hpp"
+#include "fp8_e4m3.hpp"
 #include "kernels.hpp"
 
 namespace moe {
 namespace {
-
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ double wave_sum(double v)
 {
@@ -49,25 +55,23 @@ __device__ __forceinline__ uint32_t bf16_from_double(double v)
     const uint64_t u = (uint64_t)__double_as_longlong(v);
     const uint32_t sign = (uint32_t)(u >> 48) & 0x8000u;
     const uint64_t a = u & 0x7FFFFFFFFFFFFFFFull;
-    uint32_t mag;
-    if (a >= 0x3810000000000000ull) {           // |v| >= 2^-126
-        const uint64_t r = (a + 0x00000FFFFFFFFFFFull + ((a >> 45) & 1ull)) >> 45;   // 11-bit exp, 7-bit frac
-        const int64_t e = (int64_t)(r >> 7) - 1023 + 127;
-        mag = e >= 255 ? 0x7F80u : (uint32_t)(((uint64_t)e << 7) | (r & 0x7Full));
-        if (a > 0x7FF0000000000000ull)
-            mag = 0x7FC0u;                       // NaN
-    } else {
-        mag = (uint32_t)__builtin_rint(__longlong_as_double((long long)a) * 0x1p133);
-    }
-    return sign | mag;
+    // both forms are computed and one selected: no branch per element
+    const uint64_t r = (a + 0x00000FFFFFFFFFFFull + ((a >> 45) & 1ull)) >> 45;   // 11-bit exp, 7-bit frac
+    const int64_t e = (int64_t)(r >> 7) - 1023 + 127;
+    uint32_t mag = e >= 255 ? 0x7F80u : (uint32_t)(((uint64_t)e << 7) | (r & 0x7Full));
+    mag = a > 0x7FF0000000000000ull ? 0x7FC0u : mag;                              // NaN
+    const uint32_t sub = (uint32_t)__builtin_rint(__longlong_as_double((long long)a) * 0x1p133);
+    return sign | (a >= 0x3810000000000000ull ? mag : sub);                       // |v| >= 2^-126
 }
 
-template <int KMAX, int NV, int P, int BS>
+template <int KMAX, int NV, int P, int BS, bool Q>
 __global__ __launch_bounds__(BS) void combine_rmsnorm_kernel(
     const u32x4 *__restrict__ y, int64_t nrows, int nvec, const int32_t *__restrict__ token_slot,
     const float *__restrict__ topk_w, int k, const u32x4 *residual, const u32x4 *__restrict__ gamma, float eps,
-    int H, u32x4 *residual_out, u32x4 *__restrict__ normed_out)
+    int H, u32x4 *residual_out, u32x4 *__restrict__ normed_out, u32x2 *__restrict__ normed_q,
+    float *__restrict__ normed_scales)
 {
+    static_assert(BS % 16 == 0, "a 128-element block spans 16 consecutive threads");
     static_assert(NV % P == 0, "passes must tile the vectors");
     constexpr int kWaves = BS / kWave;
     __shared__ double part[kWaves];
@@ -169,34 +173,60 @@ __global__ __launch_bounds__(BS) void combine_rmsnorm_kernel(
             o[2 * q + 1] = bf16_from_double(((double)r[n][2 * q + 1] * inv) * (double)bf16_hi(g[q]));
         }
         const u32x4 w = {o[0] | (o[1] << 16), o[2] | (o[3] << 16), o[4] | (o[5] << 16), o[6] | (o[7] << 16)};
-        __builtin_nontemporal_store(w, out_row + v);
+        if (!Q || normed_out)
+            __builtin_nontemporal_store(w, out_row + v);
+        if (Q) {   // v < nvec holds for all 16 lanes of a block (nvec % 16 == 0, BS % 16 == 0)
+            float f[8];
+            float amax = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                f[q] = __uint_as_float(o[q] << 16);
+                amax = fmaxf(amax, fabsf(f[q]));
+            }
+            amax = group_max<16>(amax);
+            const float sc = block_scale(amax);
+            __builtin_nontemporal_store(quantize8(f, sc), normed_q + t * nvec + v);
+            if ((lane & 15) == 0)
+                __builtin_nontemporal_store(sc, normed_scales + t * (nvec / 16) + v / 16);
+        }
     }
 }
 
+// Outputs of one launch (pointers already offset to its first token).
+struct NormOut {
+    uint16_t *residual_out, *normed;   // normed may be NULL when q is set
+    uint8_t *q;                         // NULL: no fp8 output
+    float *scales;
+};
+
 template <int KMAX, int NV, int BS>
 hipError_t launch_nv(const uint16_t *y, int64_t nrows, int H, const int32_t *token_slot, const float *w, int64_t T,
-                     int k, const uint16_t *residual, const uint16_t *gamma, float eps, uint16_t *residual_out,
-                     uint16_t *normed_out, hipStream_t s)
+                     int k, const uint16_t *residual, const uint16_t *gamma, float eps, NormOut o, hipStream_t s)
 {
     // about 16 row loads in flight per lane
     constexpr int P0 = 16 / KMAX > 0 ? 16 / KMAX : 1;
     constexpr int P = P0 < NV ? P0 : NV;
     if (!grid_fits(T, BS))
         return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((combine_rmsnorm_kernel<KMAX, NV, P, BS>), dim3((unsigned)T), dim3(BS), 0, s,
-                       (const u32x4 *)y, nrows, H / 8, token_slot, w, k, (const u32x4 *)residual,
-                       (const u32x4 *)gamma, eps, H, (u32x4 *)residual_out, (u32x4 *)normed_out);
+#define MOE_NORM_LAUNCH(Q)                                                                                       \
+    hipLaunchKernelGGL((combine_rmsnorm_kernel<KMAX, NV, P, BS, Q>), dim3((unsigned)T), dim3(BS), 0, s,          \
+                       (const u32x4 *)y, nrows, H / 8, token_slot, w, k, (const u32x4 *)residual,               \
+                       (const u32x4 *)gamma, eps, H, (u32x4 *)o.residual_out, (u32x4 *)o.normed, (u32x2 *)o.q, \
+                       o.scales)
+    if (o.q)
+        MOE_NORM_LAUNCH(true);
+    else
+        MOE_NORM_LAUNCH(false);
+#undef MOE_NORM_LAUNCH
     return hipGetLastError();
 }
 
 template <int KMAX>
 hipError_t launch_k(const uint16_t *y, int64_t nrows, int H, const int32_t *token_slot, const float *w, int64_t T,
-                    int k, const uint16_t *residual, const uint16_t *gamma, float eps, uint16_t *residual_out,
-                    uint16_t *normed_out, hipStream_t s)
+                    int k, const uint16_t *residual, const uint16_t *gamma, float eps, NormOut o, hipStream_t s)
 {
     const int nvec = H / 8;
-#define MOE_NORM_NV(NV, BS) \
-    launch_nv<KMAX, NV, BS>(y, nrows, H, token_slot, w, T, k, residual, gamma, eps, residual_out, normed_out, s)
+#define MOE_NORM_NV(NV, BS) launch_nv<KMAX, NV, BS>(y, nrows, H, token_slot, w, T, k, residual, gamma, eps, o, s)
     if (T < 512) {      // fewer than 2048 waves with 4-wave groups: 16-wave groups, one pass for H <= 8192
         if (nvec <= 1024)
             return MOE_NORM_NV(1, 1024);
@@ -212,28 +242,25 @@ hipError_t launch_k(const uint16_t *y, int64_t nrows, int H, const int32_t *toke
 #undef MOE_NORM_NV
 }
 
-}  // namespace
-
-namespace {
-
 hipError_t launch_tokens(const uint16_t *y, int64_t nrows, int H, const int32_t *token_slot, const float *w,
-                         int64_t T, int k, const uint16_t *residual, const uint16_t *gamma, float eps,
-                         uint16_t *residual_out, uint16_t *normed_out, hipStream_t s)
+                         int64_t T, int k, const uint16_t *residual, const uint16_t *gamma, float eps, NormOut o,
+                         hipStream_t s)
 {
     if (k <= 2)
-        return launch_k<2>(y, nrows, H, token_slot, w, T, k, residual, gamma, eps, residual_out, normed_out, s);
+        return launch_k<2>(y, nrows, H, token_slot, w, T, k, residual, gamma, eps, o, s);
     if (k <= 4)
-        return launch_k<4>(y, nrows, H, token_slot, w, T, k, residual, gamma, eps, residual_out, normed_out, s);
+        return launch_k<4>(y, nrows, H, token_slot, w, T, k, residual, gamma, eps, o, s);
     if (k <= 8)
-        return launch_k<8>(y, nrows, H, token_slot, w, T, k, residual, gamma, eps, residual_out, normed_out, s);
-    return launch_k<16>(y, nrows, H, token_slot, w, T, k, residual, gamma, eps, residual_out, normed_out, s);
+        return launch_k<8>(y, nrows, H, token_slot, w, T, k, residual, gamma, eps, o, s);
+    return launch_k<16>(y, nrows, H, token_slot, w, T, k, residual, gamma, eps, o, s);
 }
 
 }  // namespace
 
 hipError_t launch_combine_rmsnorm(const uint16_t *y, int64_t nrows, int H, const int32_t *token_slot, const float *w,
                                   int64_t T, int k, const uint16_t *residual, const uint16_t *gamma, float eps,
-                                  uint16_t *residual_out, uint16_t *normed_out, hipStream_t s)
+                                  uint16_t *residual_out, uint16_t *normed_out, uint8_t *normed_q,
+                                  float *normed_scales, hipStream_t s)
 {
     // One work-group per token and at most 2^32 - 1 work-items per launch:
     // longer batches go in launches of 2^22 tokens (256-thread groups).
@@ -241,8 +268,10 @@ hipError_t launch_combine_rmsnorm(const uint16_t *y, int64_t nrows, int H, const
     for (int64_t t0 = 0; t0 < T; t0 += kPiece) {
         const int64_t n = T - t0 < kPiece ? T - t0 : kPiece;
         const int64_t r = t0 * H;
+        const NormOut o = {residual_out + r, normed_out ? normed_out + r : nullptr, normed_q ? normed_q + r : nullptr,
+                           normed_scales ? normed_scales + t0 * (H / 128) : nullptr};
         const hipError_t e = launch_tokens(y, nrows, H, token_slot + t0 * k, w + t0 * k, n, k, residual + r, gamma,
-                                           eps, residual_out + r, normed_out + r, s);
+                                           eps, o, s);
         if (e != hipSuccess)
             return e;
     }

@@ -38,6 +38,7 @@
 // Slot rows are written with non-temporal stores: each byte is written once
 // per call.
 #include "device_common.hpp"
+#include "fp8_e4m3.hpp"
 #include "kernels.hpp"
 
 namespace moe {
@@ -201,8 +202,6 @@ __global__ __launch_bounds__(kScanBlock) void dispatch_offsets_kernel(const int3
     if (tid == E - 1)
         offsets[E] = excl + v;
 }
-
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // Streaming stores: every slot byte is written once per call and not read
 // back by this call, so stores are non-temporal.  (Measured on MI355X: the
@@ -477,56 +476,12 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_bf16_kernel(
     }
 }
 
-// x / sc for one bf16 value, bit-identical to the IEEE division x / sc.
-// With r = 1/sc (one IEEE division per scale block), q0 = x*r is within an
-// ulp or so of the quotient; the residual x - q0*sc is exact in an FMA and
-// one correction step q0 + res*r rounds to the IEEE quotient (Markstein's
-// division scheme).  The residual underflows for tiny values, so |x| or sc
-// below 2^-100 use the IEEE division itself; copysign keeps the sign of a
-// zero quotient.  Checked bit for bit against the IEEE E4M3 codes for every
-// bf16 x with |x| <= amax and every bf16 amax.
-__device__ __forceinline__ float divide_by_scale(float x, float sc, float r, bool fast)
-{
-    const float q0 = x * r;
-    float q = __builtin_copysignf(__builtin_fmaf(__builtin_fmaf(-q0, sc, x), r, q0), x);
-    if (!(fast && (__builtin_fabsf(x) >= 0x1p-100f || x == 0.0f)))
-        q = x / sc;
-    return q;
-}
-
-// Four quotients -> four OCP E4M3 codes in one word.  v_cvt_pk_fp8_f32
-// rounds to nearest even; the clamp to +-448 makes it saturate (a magnitude
-// above 448 becomes 448), matching the E4M3 encoding the codes are defined
-// by on every fp32 input of magnitude <= 464 (checked exhaustively).
-__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d)
-{
-    a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
-    b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
-    c = __builtin_amdgcn_fmed3f(c, -448.0f, 448.0f);
-    d = __builtin_amdgcn_fmed3f(d, -448.0f, 448.0f);
-    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
-}
-
-// 16 bf16 values -> 16 E4M3 codes of x / sc.
-__device__ __forceinline__ u32x4 quantize16(const float *f, float sc)
-{
-    const float r = 1.0f / sc;
-    const bool fast = sc >= 0x1p-100f;
-    float q[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-        q[i] = divide_by_scale(f[i], sc, r, fast);
-    return (u32x4){e4m3x4(q[0], q[1], q[2], q[3]), e4m3x4(q[4], q[5], q[6], q[7]), e4m3x4(q[8], q[9], q[10], q[11]),
-                   e4m3x4(q[12], q[13], q[14], q[15])};
-}
-
 constexpr int kMaxG = 8;   // most 16-element groups per lane in flight (fp8 rows)
 
 // fp8 rows: one wave per (token, row segment); a lane owns groups of 16
 // consecutive elements (two 16-byte loads, one 16-byte code store), groups
 // seg*VPL*64 + i*64 + lane.  The 8 consecutive lanes holding one
-// 128-element block find its amax with a 3-step butterfly; the scale is
+// 128-element block find its amax with three DPP steps; the scale is
 // amax/448 (IEEE division; 1 for an all-zero block) and each code is the
 // E4M3 encoding (round to nearest even, saturating) of x / scale, with the
 // quotient bit-identical to an IEEE division (divide_by_scale).
@@ -605,12 +560,10 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_fp8_kernel(
 #pragma unroll
         for (int q = 0; q < 16; ++q)
             amax = fmaxf(amax, fabsf(f[q]));
-#pragma unroll
-        for (int o = 1; o < 8; o <<= 1)
-            amax = fmaxf(amax, __shfl_xor(amax, o));
+        amax = group_max<8>(amax);
         if (g >= ngrp)
             continue;
-        const float sc = amax == 0.0f ? 1.0f : amax / 448.0f;
+        const float sc = block_scale(amax);
         const u32x4 codes = quantize16(f, sc);
         if ((lane & 7) == 0)
             my_scale[i * 8 + lane / 8] = sc;

@@ -47,8 +47,11 @@ hipError_t launch_combine(const uint16_t *y, int64_t nrows, int H, const int32_t
                           hipEvent_t stop = nullptr);
 
 // combine + residual add + RMSNorm; residual_out may be residual (in place).
+// normed_q != NULL adds the E4M3 codes [T][H] and per-128 scales [T][H/128]
+// of the bf16 normalised rows (H % 128 == 0); normed_out may then be NULL.
 hipError_t launch_combine_rmsnorm(const uint16_t *y, int64_t nrows, int H, const int32_t *token_slot, const float *w,
                                   int64_t T, int k, const uint16_t *residual, const uint16_t *gamma, float eps,
-                                  uint16_t *residual_out, uint16_t *normed_out, hipStream_t s);
+                                  uint16_t *residual_out, uint16_t *normed_out, uint8_t *normed_q,
+                                  float *normed_scales, hipStream_t s);
 
 }  // namespace moe

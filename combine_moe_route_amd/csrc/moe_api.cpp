@@ -247,35 +247,78 @@ MOE_API int moe_combine_timed(const uint16_t *y, int32_t E, int32_t capacity, in
     return combine_checked(y, E, capacity, H, token_slot, topk_w, T, k, out, stream, start, stop);
 }
 
-MOE_API int moe_combine_residual_rmsnorm(const uint16_t *y, int32_t E, int32_t capacity, int32_t H,
-                                         const int32_t *token_slot, const float *topk_w, int64_t T, int32_t k,
-                                         const uint16_t *residual, const uint16_t *gamma, float eps,
-                                         uint16_t *residual_out, uint16_t *normed_out, hipStream_t stream)
+}  // extern "C"
+
+namespace {
+
+int norm_checked(const uint16_t *y, int32_t E, int32_t capacity, int32_t H, const int32_t *token_slot,
+                 const float *topk_w, int64_t T, int32_t k, const uint16_t *residual, const uint16_t *gamma, float eps,
+                 uint16_t *residual_out, uint16_t *normed_out, bool q, uint8_t *normed_q, float *normed_scales,
+                 hipStream_t stream)
 {
     if (T < 0 || H < 1 || capacity < 1 || E < 1 || k < 1 || !(eps >= 0.0f) || !(eps <= 3.4e38f))
         return MOE_ERR_INVALID;
-    if (k > MOE_MAX_TOPK || H % 8 != 0 || H > MOE_MAX_NORM_HIDDEN)
+    if (k > MOE_MAX_TOPK || H % 8 != 0 || H > MOE_MAX_NORM_HIDDEN || (q && H % 128 != 0))
         return MOE_ERR_UNSUPPORTED;
     if ((int64_t)E * capacity > INT32_MAX || T > MOE_MAX_TOKENS)
         return MOE_ERR_UNSUPPORTED;
     if (T == 0)
         return MOE_OK;
-    if (!y || !token_slot || !topk_w || !residual || !gamma || !residual_out || !normed_out)
+    if (!y || !token_slot || !topk_w || !residual || !gamma || !residual_out || (!q && !normed_out))
+        return MOE_ERR_INVALID;
+    if (q && (!normed_q || !normed_scales || !aligned(normed_q, 8) || !aligned(normed_scales, 4)))
         return MOE_ERR_INVALID;
     if (!aligned(y, 16) || !aligned(residual, 16) || !aligned(gamma, 16) || !aligned(residual_out, 16) ||
-        !aligned(normed_out, 16) || !aligned(token_slot, 4) || !aligned(topk_w, 4))
+        (normed_out && !aligned(normed_out, 16)) || !aligned(token_slot, 4) || !aligned(topk_w, 4))
         return MOE_ERR_INVALID;
     const uint64_t ybytes = (uint64_t)E * capacity * H * 2, row_bytes = (uint64_t)T * H * 2;
     // outputs must not overlap the inputs or each other; residual_out may be
     // residual itself (an in-place update of the residual stream)
-    if (overlaps(normed_out, row_bytes, y, ybytes) || overlaps(normed_out, row_bytes, residual, row_bytes) ||
-        overlaps(normed_out, row_bytes, residual_out, row_bytes) || overlaps(normed_out, row_bytes, gamma, 2 * H) ||
-        overlaps(residual_out, row_bytes, y, ybytes) || overlaps(residual_out, row_bytes, gamma, 2 * H) ||
-        (residual_out != residual && overlaps(residual_out, row_bytes, residual, row_bytes)))
-        return MOE_ERR_INVALID;
+    struct Region {
+        const void *p;
+        uint64_t n;
+    };
+    const Region in[] = {{y, ybytes}, {residual, row_bytes}, {gamma, 2 * (uint64_t)H},
+                         {token_slot, (uint64_t)T * k * 4}, {topk_w, (uint64_t)T * k * 4}};
+    const Region out[] = {{residual_out, row_bytes}, {normed_out, normed_out ? row_bytes : 0},
+                          {normed_q, q ? (uint64_t)T * H : 0}, {normed_scales, q ? (uint64_t)T * (H / 128) * 4 : 0}};
+    for (int i = 0; i < 4; ++i) {
+        if (!out[i].n)
+            continue;
+        for (const Region &r : in)
+            if (!(i == 0 && r.p == residual && residual_out == residual) && overlaps(out[i].p, out[i].n, r.p, r.n))
+                return MOE_ERR_INVALID;
+        for (int j = i + 1; j < 4; ++j)
+            if (out[j].n && overlaps(out[i].p, out[i].n, out[j].p, out[j].n))
+                return MOE_ERR_INVALID;
+    }
     (void)hipGetLastError();
     return from_hip(moe::launch_combine_rmsnorm(y, (int64_t)E * capacity, H, token_slot, topk_w, T, k, residual,
-                                                gamma, eps, residual_out, normed_out, stream));
+                                                gamma, eps, residual_out, normed_out, normed_q, normed_scales,
+                                                stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+MOE_API int moe_combine_residual_rmsnorm(const uint16_t *y, int32_t E, int32_t capacity, int32_t H,
+                                         const int32_t *token_slot, const float *topk_w, int64_t T, int32_t k,
+                                         const uint16_t *residual, const uint16_t *gamma, float eps,
+                                         uint16_t *residual_out, uint16_t *normed_out, hipStream_t stream)
+{
+    return norm_checked(y, E, capacity, H, token_slot, topk_w, T, k, residual, gamma, eps, residual_out,
+                        normed_out, false, nullptr, nullptr, stream);
+}
+
+MOE_API int moe_combine_residual_rmsnorm_fp8(const uint16_t *y, int32_t E, int32_t capacity, int32_t H,
+                                             const int32_t *token_slot, const float *topk_w, int64_t T, int32_t k,
+                                             const uint16_t *residual, const uint16_t *gamma, float eps,
+                                             uint16_t *residual_out, uint16_t *normed_out, uint8_t *normed_q,
+                                             float *normed_scales, hipStream_t stream)
+{
+    return norm_checked(y, E, capacity, H, token_slot, topk_w, T, k, residual, gamma, eps, residual_out,
+                        normed_out, true, normed_q, normed_scales, stream);
 }
 
 }  // extern "C"

@@ -312,12 +312,38 @@ MOE_API int moe_combine_timed(const uint16_t *y, int32_t E, int32_t capacity, in
  *                 Must not overlap any other buffer.  With eps = 0 an
  *                 all-zero row gives NaN.
  *   stream        HIP stream
- * T = 0 enqueues nothing.
+ * No output may overlap an input (y, token_slot, topk_w, residual except as
+ * above, gamma) or another output: MOE_ERR_INVALID.  T = 0 enqueues nothing.
  */
 MOE_API int moe_combine_residual_rmsnorm(const uint16_t *y, int32_t E, int32_t capacity, int32_t H,
                                          const int32_t *token_slot, const float *topk_w, int64_t T, int32_t k,
                                          const uint16_t *residual, const uint16_t *gamma, float eps,
                                          uint16_t *residual_out, uint16_t *normed_out, hipStream_t stream);
+
+/*
+ * moe_combine_residual_rmsnorm_fp8 -- the fused epilogue above, with the
+ * normalised rows also re-quantised for an fp8 consumer (the next layer's
+ * fp8 GEMM).
+ *
+ * Handbook "NVSHMEM and DeepEP", "High-throughput mode": activations travel
+ * as FP8 with one fp32 scale per 128 elements.  The encoding is
+ * moe_dispatch's MOE_DTYPE_FP8_E4M3 one, applied to the bf16 normalised
+ * values: per 128-element block sc = amax / 448 (1 for an all-zero block)
+ * and each code is the E4M3 encoding (nearest even, saturating) of x / sc.
+ *
+ *   all arguments as for moe_combine_residual_rmsnorm, except
+ *   H             also a multiple of 128 (else MOE_ERR_UNSUPPORTED)
+ *   normed_out    (device, out, may be NULL) the bf16 normalised rows; the
+ *                 codes are those of these values whether or not they are
+ *                 stored
+ *   normed_q      (device, out) uint8 [T][H] E4M3 codes, 8 B aligned
+ *   normed_scales (device, out) float [T][H/128] block scales, 4 B aligned
+ */
+MOE_API int moe_combine_residual_rmsnorm_fp8(const uint16_t *y, int32_t E, int32_t capacity, int32_t H,
+                                             const int32_t *token_slot, const float *topk_w, int64_t T, int32_t k,
+                                             const uint16_t *residual, const uint16_t *gamma, float eps,
+                                             uint16_t *residual_out, uint16_t *normed_out, uint8_t *normed_q,
+                                             float *normed_scales, hipStream_t stream);
 
 #ifdef __cplusplus
 }

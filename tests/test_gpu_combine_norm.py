@@ -154,3 +154,97 @@ def test_batch_longer_than_one_launch(dev):
     res_o, normed_o = oracle.combine_residual_rmsnorm(y_pairs[picks].reshape(-1, H), slot[picks], wt[picks],
                                                       res_bits[picks], gamma_bits, 1e-6)
     _compare(f"T={T}, {picks.size} sampled tokens", res_g[picks], normed_g[picks], res_o, normed_o)
+
+
+# ---- fp8 re-quantisation of the normalised rows (moe_combine_residual_rmsnorm_fp8) ----
+#
+# The codes are a function of the kernel's own bf16 normalised values, so
+# they are compared bit for bit with the oracle's E4M3 block encoding of
+# those values (the float decides the integer in one precision on both
+# sides); the bf16 values themselves are held to the one-ulp bar above.
+
+def _run_fp8(dev, y_dev, slot, w, res_bits, gamma_bits, eps, keep_bf16):
+    T, H = res_bits.shape
+    res = to_dev_bf16(res_bits, dev)
+    gamma = to_dev_bf16(gamma_bits, dev)
+    q = torch.full(((T + 1) * H + 64,), 0xA5, dtype=torch.uint8, device=dev)
+    sc = torch.full(((T + 1) * (H // 128) + 16,), -7.0, dtype=torch.float32, device=dev)
+    res_out = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    normed = torch.empty(T, H, dtype=torch.bfloat16, device=dev) if keep_bf16 else None
+    T_ = torch.from_numpy(slot).to(dev)
+    W_ = torch.from_numpy(w).to(dev)
+    if y_dev.dim() == 2:
+        y_dev = y_dev.view(1, y_dev.shape[0], H)
+    E, C, _ = y_dev.shape
+    lib = moe.load()
+    rc = lib.moe_combine_residual_rmsnorm_fp8(y_dev.data_ptr(), E, C, H, T_.data_ptr(), W_.data_ptr(), T,
+                                              slot.shape[1], res.data_ptr(), gamma.data_ptr(), float(eps),
+                                              res_out.data_ptr(), normed.data_ptr() if keep_bf16 else None,
+                                              q.data_ptr(), sc.data_ptr(), None)
+    assert rc == 0, moe.moe_status_string(rc)
+    torch.cuda.synchronize()
+    qh = q.cpu().numpy()
+    sch = sc.cpu().numpy()
+    assert (qh[T * H:] == 0xA5).all(), "codes written past their end"
+    assert (sch[T * (H // 128):] == -7.0).all(), "scales written past their end"
+    return (dev_bits(res_out), dev_bits(normed) if keep_bf16 else None, qh[:T * H].reshape(T, H),
+            sch[:T * (H // 128)].reshape(T, H // 128))
+
+
+def _check_fp8(label, dev, y_dev, slot, w, y_pairs, res_bits, gamma_bits, eps):
+    res_g, normed_g, q_g, sc_g = _run_fp8(dev, y_dev, slot, w, res_bits, gamma_bits, eps, True)
+    res_o, normed_o = oracle.combine_residual_rmsnorm(y_pairs, slot, w, res_bits, gamma_bits, eps)
+    _compare(label, res_g, normed_g, res_o, normed_o)
+    q_o, sc_o = oracle.quantize_rows_fp8(normed_g)
+    np.testing.assert_array_equal(q_g, q_o)
+    np.testing.assert_array_equal(sc_g.view(np.uint32), sc_o.view(np.uint32))
+    # without the bf16 rows: the same codes, scales and residual
+    res_2, _, q_2, sc_2 = _run_fp8(dev, y_dev, slot, w, res_bits, gamma_bits, eps, False)
+    np.testing.assert_array_equal(res_2, res_g)
+    np.testing.assert_array_equal(q_2, q_g)
+    np.testing.assert_array_equal(sc_2.view(np.uint32), sc_g.view(np.uint32))
+
+
+@pytest.mark.parametrize("name", W.ORDER)
+def test_fp8_output_workloads(dev, name):
+    w = W.WORKLOADS[name]
+    o = OracleRun.get(w)
+    say(f"[combine+norm fp8] {name}")
+    rng = np.random.default_rng(w.seed + 1)
+    res_bits = _bf16(rng.standard_normal((w.T, w.H)))
+    gamma_bits = _bf16(rng.uniform(0.5, 1.5, w.H))
+    y = place_rows(w, o.y_pairs, o.token_slot, dev)
+    _check_fp8(name, dev, y, o.token_slot, o.wt, o.y_pairs, res_bits, gamma_bits, 1e-6)
+    del y
+
+
+@pytest.mark.parametrize("T,H,k", [(1, 128, 1), (5, 256, 2), (300, 2048, 8), (513, 1024, 3), (40, 7168, 16),
+                                   (600, 16384, 2), (77, 6144, 5)])
+def test_fp8_output_shapes(dev, T, H, k):
+    rng = np.random.default_rng(T * 5 + H + k)
+    rows = T * k
+    slot = rng.permutation(rows).astype(np.int32).reshape(T, k)
+    slot[rng.random((T, k)) < 0.15] = -1
+    wt = rng.random((T, k)).astype(np.float32)
+    y_rows = _bf16(rng.standard_normal((rows, H)))
+    y_pairs = np.zeros((rows, H), np.uint16)
+    keep = slot.reshape(-1) >= 0
+    y_pairs[keep] = y_rows[slot.reshape(-1)[keep]]
+    # row scales from tiny to large, a zero block and a block with one spike
+    res_bits = _bf16(rng.standard_normal((T, H)) * rng.choice([1e-30, 1e-3, 1.0, 300.0], (T, 1)))
+    gamma_bits = _bf16(rng.uniform(0.25, 2.0, H))
+    gamma_bits[:128] = 0                                        # block 0 normalises to all zeros
+    gamma_bits[200 % H] = _bf16(np.array([1e4]))[0] if H > 256 else gamma_bits[200 % H]
+    say(f"[combine+norm fp8] T={T} H={H} k={k}")
+    _check_fp8(f"fp8 T={T} H={H} k={k}", dev, to_dev_bf16(y_rows, dev), slot, wt, y_pairs, res_bits, gamma_bits,
+               1e-6)
+
+
+def test_fp8_output_rejects_bad_sizes(dev):
+    y = torch.zeros(1, 8, 192, dtype=torch.bfloat16, device=dev)
+    slot = torch.zeros(2, 1, dtype=torch.int32, device=dev)
+    w = torch.ones(2, 1, device=dev)
+    r = torch.zeros(2, 192, dtype=torch.bfloat16, device=dev)
+    g = torch.ones(192, dtype=torch.bfloat16, device=dev)
+    with pytest.raises(moe.MoeError):
+        moe.moe_combine_residual_rmsnorm_fp8(y, slot, w, r, g)     # H = 192 is not a multiple of 128

@@ -34,7 +34,8 @@ def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("moe_route_topk", "moe_route_topk_grouped", "moe_dispatch", "moe_dispatch_packed", "moe_route_dispatch",
               "moe_combine",
-              "moe_combine_residual_rmsnorm", "moe_dispatch_workspace_bytes", "moe_status_string"):
+              "moe_combine_residual_rmsnorm", "moe_combine_residual_rmsnorm_fp8", "moe_dispatch_workspace_bytes",
+              "moe_status_string"):
         assert n in names
 
 
@@ -108,6 +109,21 @@ def test_host_validation_without_device(lib):
               P) == -1
     assert cn(A, 8, 4, 64, A + 8192, A + 12288, 4, 2, A + 4 * 4096, A + 5 * 4096, 1e-6, A + 4 * 4096 + 16,
               A + 7 * 4096, P) == -1
+    cq = lib.moe_combine_residual_rmsnorm_fp8
+    assert cq(P, 8, 4, 192, P, P, 4, 2, P, P, 1e-6, P, P, P, P, P) == -2   # H % 128
+    assert cq(P, 8, 4, 256, P, P, 0, 2, P, P, 1e-6, P, P, P, P, P) == 0    # empty
+    assert cq(P, 8, 4, 256, P, P, 4, 2, P, P, 1e-6, P, P, P, P, P) == -1   # null pointers
+    K = 1024                                                           # y [8][4][256] bf16 = 16 KiB at A
+    args = dict(ts=A + 16 * K, tw=A + 16 * K + 256, res=A + 20 * K, g=A + 24 * K, ro=A + 28 * K)
+    def cq_at(q, sc, normed=None):
+        return cq(A, 8, 4, 256, args["ts"], args["tw"], 4, 2, args["res"], args["g"], 1e-6, args["ro"], normed, q,
+                  sc, P)
+    assert cq_at(A + 32 * K, A + 32 * K + 512) == -1                  # scales inside the codes [4][256]
+    assert cq_at(A + 32 * K + 4, A + 34 * K) == -1                    # codes not 8 B aligned
+    assert cq_at(A + 32 * K, A + 34 * K + 2) == -1                    # scales not 4 B aligned
+    assert cq_at(A + 32 * K, A + 34 * K, normed=A + 33 * K) == -1     # bf16 rows overlapping the scales
+    assert cq_at(A + 8 * K, A + 34 * K) == -1                         # codes overlapping y
+    assert cq_at(A + 32 * K, args["ts"]) == -1                        # scales overlapping token_slot
     rd = lib.moe_route_dispatch
     assert rd(P, 4, 8, 2, P, 64, 4, 0, P, P, P, P, P, P, P, P, 0, P) == -1    # null pointers
     assert rd(P, 4, 8, 9, P, 64, 4, 0, P, P, P, P, P, P, P, P, 0, P) == -1    # k > E
