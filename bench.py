@@ -6,8 +6,9 @@ moe_dispatch (or moe_dispatch_packed with --layout packed) + moe_combine (or
 moe_combine_residual_rmsnorm with --epilogue rmsnorm, or its fp8-output form
 moe_combine_residual_rmsnorm_fp8 with --epilogue rmsnorm-fp8), back to back on one
 stream, over one batch of seeded synthetic input already resident in HBM.
-With fixed slots and plain top-k the first two are the single call
-moe_route_dispatch (identical outputs; --separate-route calls them apart).
+With plain top-k the first two are the single call moe_route_dispatch (or
+moe_route_dispatch_packed; identical outputs; --separate-route calls them
+apart).
 W untimed warm-up steps, then exactly K timed steps between device
 synchronisations.  Prints one JSON line (stdout):
 
@@ -248,7 +249,7 @@ def main() -> int:
     x_cpu = W.make_x(w)
     route_groups = tuple(int(v) for v in args.route_groups.split(":")) if args.route_groups else None
     packed = args.layout == "packed"
-    fuse_route = not args.separate_route and not packed and route_groups is None
+    fuse_route = not args.separate_route and route_groups is None
     sets = [BufferSet(w, logits_cpu, x_cpu, dev, moe, torch, route_groups, packed, epilogue, fuse_route)
             for _ in range(R)]
     gen = torch.Generator(device=dev)
@@ -394,7 +395,8 @@ def main() -> int:
             "row_dtype": "fp8-e4m3+fp32/128" if w.fp8 else "bf16", "routing": w.routing,
             "route_groups": ({"groups": route_groups[0], "kept": route_groups[1]} if route_groups else None),
             "layout": "packed count-sized rows" if packed else "fixed slots per expert",
-            "route_dispatch_call": "moe_route_dispatch" if fuse_route else "separate",
+            "route_dispatch_call": (("moe_route_dispatch_packed" if packed else "moe_route_dispatch") if fuse_route
+                                    else "separate"),
             "combine_epilogue": {None: None, "rmsnorm": "residual add + RMSNorm (fused)",
                                  "rmsnorm-fp8": "residual add + RMSNorm, output as E4M3 + fp32/128 (fused)"}[epilogue],
             "parallelism": "none (1 GPU)",

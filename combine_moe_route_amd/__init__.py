@@ -22,6 +22,7 @@ from .binding import (  # noqa: F401
     moe_dispatch_packed,
     moe_dispatch_workspace_bytes,
     moe_route_dispatch,
+    moe_route_dispatch_packed,
     moe_route_topk,
     moe_route_topk_grouped,
     moe_status_string,

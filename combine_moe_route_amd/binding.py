@@ -58,6 +58,9 @@ def load() -> ctypes.CDLL:
     lib.moe_route_dispatch.argtypes = [P, i64, i32, i32, P, i32, i32, i32, P, P, P, P, P, P, P, P,
                                        ctypes.c_size_t, P]
     lib.moe_route_dispatch.restype = ctypes.c_int
+    lib.moe_route_dispatch_packed.argtypes = [P, i64, i32, i32, P, i32, i32, P, P, P, P, P, P, P, P,
+                                              ctypes.c_size_t, P]
+    lib.moe_route_dispatch_packed.restype = ctypes.c_int
     lib.moe_dispatch_packed.argtypes = [P, i64, i32, P, i32, i32, i32, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.moe_dispatch_packed.restype = ctypes.c_int
     lib.moe_combine.argtypes = [P, i32, i32, i32, P, P, i64, i32, P, P]
@@ -332,6 +335,40 @@ def moe_dispatch_packed(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: in
     return bufs
 
 
+def moe_route_dispatch_packed(logits: torch.Tensor, x: torch.Tensor, k: int, fp8: bool = False,
+                              bufs: PackedBuffers | None = None, topk_idx: torch.Tensor | None = None,
+                              topk_w: torch.Tensor | None = None, stream=None):
+    """moe_route_topk + moe_dispatch_packed in one call (identical outputs).
+    Returns (topk_idx, topk_w, bufs)."""
+    T, E = logits.shape
+    H = x.shape[1]
+    _need(logits, torch.float32, (T, E), "logits")
+    _need(x, torch.bfloat16, (T, H), "x")
+    if topk_idx is None:
+        topk_idx = torch.empty(T, k, dtype=torch.int32, device=x.device)
+    if topk_w is None:
+        topk_w = torch.empty(T, k, dtype=torch.float32, device=x.device)
+    _need(topk_idx, torch.int32, (T, k), "topk_idx")
+    _need(topk_w, torch.float32, (T, k), "topk_w")
+    if bufs is None:
+        bufs = PackedBuffers.allocate(T, H, E, k, fp8, x.device)
+    _need(bufs.recv_x, torch.uint8 if fp8 else torch.bfloat16, (T * k, H), "recv_x")
+    if fp8:
+        _need(bufs.recv_scales, torch.float32, (T * k, H // 128), "recv_scales")
+    if bufs.recv_src.numel() < T * k:
+        raise ValueError("recv_src needs T*k entries")
+    _need(bufs.expert_offsets, torch.int32, (E + 1,), "expert_offsets")
+    _need(bufs.token_slot, torch.int32, (T, k), "token_slot")
+    rc = load().moe_route_dispatch_packed(
+        _ptr(logits), T, E, k, _ptr(x), H, MOE_DTYPE_FP8_E4M3 if fp8 else MOE_DTYPE_BF16, _ptr(topk_idx),
+        _ptr(topk_w), _ptr(bufs.recv_x), _ptr(bufs.recv_scales) if fp8 else None, _ptr(bufs.recv_src),
+        _ptr(bufs.expert_offsets), _ptr(bufs.token_slot), _ptr(bufs.workspace), bufs.workspace.numel(),
+        _stream(stream))
+    if rc != MOE_OK:
+        raise MoeError("moe_route_dispatch_packed", rc)
+    return topk_idx, topk_w, bufs
+
+
 def moe_combine(y: torch.Tensor, token_slot: torch.Tensor, topk_w: torch.Tensor, out: torch.Tensor | None = None,
                 stream=None, events: tuple[int, int] | None = None) -> torch.Tensor:
     """out[t] = bf16(sum_j w[t,j] * y[token_slot[t,j]]), fp32 FMA in top-k order.
@@ -442,8 +479,8 @@ class PreparedStep:
         (residual, gamma, eps, residual_out, normed_q, normed_scales) with
         moe_combine_residual_rmsnorm_fp8, writing only their E4M3 codes and
         block scales.
-        fuse_route: route_and_dispatch() uses moe_route_dispatch (fixed slots
-        and plain top-k only)."""
+        fuse_route: route_and_dispatch() uses moe_route_dispatch or
+        moe_route_dispatch_packed (plain top-k only)."""
         T, E = logits.shape
         H = x.shape[1]
         _need(logits, torch.float32, (T, E), "logits")
@@ -485,10 +522,17 @@ class PreparedStep:
                 _ptr(bufs.expert_counts), _ptr(bufs.token_slot), _ptr(bufs.workspace), bufs.workspace.numel(), s)
             self.combine_args = (_ptr(y), E, capacity, H, _ptr(bufs.token_slot), _ptr(topk_w), T, k, _ptr(out), s)
         self._fused_args = None
-        if not packed and route_groups is None and fuse_route:
-            self._fused_args = (_ptr(logits), T, E, k, _ptr(x), H, capacity, dt, _ptr(topk_idx), _ptr(topk_w),
-                                _ptr(bufs.recv_x), scales, _ptr(bufs.recv_src), _ptr(bufs.expert_counts),
-                                _ptr(bufs.token_slot), _ptr(bufs.workspace), bufs.workspace.numel(), s)
+        if route_groups is None and fuse_route:
+            if packed:
+                self._fused_name = "moe_route_dispatch_packed"
+                self._fused_args = (_ptr(logits), T, E, k, _ptr(x), H, dt, _ptr(topk_idx), _ptr(topk_w),
+                                    _ptr(bufs.recv_x), scales, _ptr(bufs.recv_src), _ptr(bufs.expert_offsets),
+                                    _ptr(bufs.token_slot), _ptr(bufs.workspace), bufs.workspace.numel(), s)
+            else:
+                self._fused_name = "moe_route_dispatch"
+                self._fused_args = (_ptr(logits), T, E, k, _ptr(x), H, capacity, dt, _ptr(topk_idx), _ptr(topk_w),
+                                    _ptr(bufs.recv_x), scales, _ptr(bufs.recv_src), _ptr(bufs.expert_counts),
+                                    _ptr(bufs.token_slot), _ptr(bufs.workspace), bufs.workspace.numel(), s)
         self._epilogue_args = None
         self._epilogue_fn = None
         if epilogue is not None:
@@ -510,12 +554,12 @@ class PreparedStep:
         self._keep = (logits, x, bufs, y, out, topk_idx, topk_w, epilogue)
 
     def route_and_dispatch(self):
-        """route then dispatch; one moe_route_dispatch call where it applies
-        (fixed slots, plain top-k)."""
+        """route then dispatch; one moe_route_dispatch(_packed) call where it
+        applies (plain top-k)."""
         if self._fused_args is not None:
-            rc = self._lib.moe_route_dispatch(*self._fused_args)
+            rc = getattr(self._lib, self._fused_name)(*self._fused_args)
             if rc != MOE_OK:
-                raise MoeError("moe_route_dispatch", rc)
+                raise MoeError(self._fused_name, rc)
             return
         self.route()
         self.dispatch()

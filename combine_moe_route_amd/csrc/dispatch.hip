@@ -148,6 +148,10 @@ constexpr int kScanWaves = kScanBlock / kWave;
 // expert's row, each summing every tpe-th chunk with eight loads in flight,
 // then a butterfly; then a work-group exclusive scan over the E totals (wave
 // scans, then the wave sums).
+// MASKS: the rows are the router's 32-token membership words (uint32), and
+// an expert's total is the sum of their popcounts; otherwise the rows are
+// the 256-token chunk histograms.
+template <bool MASKS>
 __global__ __launch_bounds__(kScanBlock) void dispatch_offsets_kernel(const int32_t *__restrict__ chunk_counts,
                                                                       int E, int nchunks,
                                                                       int32_t *__restrict__ offsets)
@@ -173,7 +177,7 @@ __global__ __launch_bounds__(kScanBlock) void dispatch_offsets_kernel(const int3
                     part[u] = cc + u * tpe < nchunks ? row[cc + u * tpe] : 0;
 #pragma unroll
                 for (int u = 0; u < 8; ++u)
-                    sum += part[u];
+                    sum += MASKS ? __popc((uint32_t)part[u]) : part[u];
             }
         }
         for (int o = tpe / 2; o > 0; o >>= 1)
@@ -738,8 +742,8 @@ hipError_t launch_dispatch(const uint16_t *x, int64_t T, int H, const int32_t *t
     hipLaunchKernelGGL(dispatch_count_kernel, dim3(nchunks), dim3(kBlock), (size_t)E * kMaskWords * 4, s, topk_idx,
                        T, E, k, nchunks, chunk_counts, local_rank);
     if (expert_offsets)
-        hipLaunchKernelGGL(dispatch_offsets_kernel, dim3(1), dim3(kScanBlock), 0, s, chunk_counts, E, nchunks,
-                           expert_offsets);
+        hipLaunchKernelGGL(dispatch_offsets_kernel<false>, dim3(1), dim3(kScanBlock), 0, s, chunk_counts, E,
+                           nchunks, expert_offsets);
     int32_t *offs = expert_offsets;
 
     return launch_pack(x, T, H, topk_idx, local_rank, chunk_counts, nullptr, offs, E, k, C, nchunks, dtype, recv_x,
@@ -748,35 +752,43 @@ hipError_t launch_dispatch(const uint16_t *x, int64_t T, int H, const int32_t *t
 
 hipError_t launch_route_dispatch(const float *logits, int64_t T, int E, int k, const uint16_t *x, int H, int C,
                                  int dtype, int32_t *topk_idx, float *topk_w, void *recv_x, float *recv_scales,
-                                 int32_t *recv_src, int32_t *expert_counts, int32_t *token_slot, void *workspace,
-                                 hipStream_t s)
+                                 int32_t *recv_src, int32_t *expert_counts, int32_t *expert_offsets,
+                                 int32_t *token_slot, void *workspace, hipStream_t s)
 {
     if (T == 0) {
-        hipLaunchKernelGGL(dispatch_zero_counts_kernel, dim3((E + kBlock - 1) / kBlock), dim3(kBlock), 0, s,
-                           expert_counts, E);
+        int32_t *zero = expert_offsets ? expert_offsets : expert_counts;
+        const int n = expert_offsets ? E + 1 : E;
+        hipLaunchKernelGGL(dispatch_zero_counts_kernel, dim3((n + kBlock - 1) / kBlock), dim3(kBlock), 0, s, zero, n);
         return hipGetLastError();
     }
     if (!dispatch_grid_fits(T, H, k, dtype))
         return hipErrorInvalidConfiguration;
     // E <= 8: the router writes 32-token membership words and pack derives
-    // the slots from them (two launches).  Otherwise, or when the prefix
-    // over those words would exceed 64 loads per lane: route, count, pack.
+    // the slots from them (two launches; the packed layout adds one
+    // work-group that totals the words into expert_offsets, so there it is
+    // used only past one 256-token chunk, where the alternative is four
+    // launches).  Otherwise, or when the prefix over those words would
+    // exceed 64 loads per lane: route, count (+ offsets), pack -- or for a
+    // single chunk route and a pack that counts in LDS.
     const int64_t nmask = (T + kMaskChunk - 1) / kMaskChunk;
     const int lpp = pair_lanes(k);
-    if (E <= 8 && nmask <= 64 * (int64_t)lpp &&
+    if (E <= 8 && nmask <= 64 * (int64_t)lpp && (!expert_offsets || T > kChunk) &&
         (size_t)E * nmask * 4 <= dispatch_workspace_bytes(T, E, k)) {
         uint32_t *masks = (uint32_t *)workspace;
         hipError_t e = launch_route_topk_masks(logits, T, E, k, topk_idx, topk_w, masks, s);
         if (e != hipSuccess)
             return e;
-        return launch_pack(x, T, H, topk_idx, nullptr, nullptr, masks, nullptr, E, k, C, (int)nmask, dtype, recv_x,
-                           recv_scales, recv_src, expert_counts, token_slot, s);
+        if (expert_offsets)
+            hipLaunchKernelGGL(dispatch_offsets_kernel<true>, dim3(1), dim3(kScanBlock), 0, s,
+                               (const int32_t *)masks, E, (int)nmask, expert_offsets);
+        return launch_pack(x, T, H, topk_idx, nullptr, nullptr, masks, expert_offsets, E, k, C, (int)nmask, dtype,
+                           recv_x, recv_scales, recv_src, expert_offsets ? nullptr : expert_counts, token_slot, s);
     }
     hipError_t e = launch_route_topk(logits, T, E, k, topk_idx, topk_w, s);
     if (e != hipSuccess)
         return e;
-    return launch_dispatch(x, T, H, topk_idx, E, k, C, dtype, recv_x, recv_scales, recv_src, expert_counts, nullptr,
-                           token_slot, workspace, s);
+    return launch_dispatch(x, T, H, topk_idx, E, k, C, dtype, recv_x, recv_scales, recv_src,
+                           expert_offsets ? nullptr : expert_counts, expert_offsets, token_slot, workspace, s);
 }
 
 }  // namespace moe

@@ -16,12 +16,13 @@ hipError_t launch_route_topk(const float *logits, int64_t T, int E, int k, int32
 hipError_t launch_route_topk_masks(const float *logits, int64_t T, int E, int k, int32_t *idx, float *w,
                                    uint32_t *masks, hipStream_t s);
 
-// Route + dispatch (fixed slots) in one call; the workspace is
-// dispatch_workspace_bytes(T, E, k).
+// Route + dispatch in one call; the workspace is dispatch_workspace_bytes(T,
+// E, k).  expert_offsets != NULL selects the packed layout (C and
+// expert_counts unused), otherwise fixed slots of C rows per expert.
 hipError_t launch_route_dispatch(const float *logits, int64_t T, int E, int k, const uint16_t *x, int H, int C,
                                  int dtype, int32_t *topk_idx, float *topk_w, void *recv_x, float *recv_scales,
-                                 int32_t *recv_src, int32_t *expert_counts, int32_t *token_slot, void *workspace,
-                                 hipStream_t s);
+                                 int32_t *recv_src, int32_t *expert_counts, int32_t *expert_offsets,
+                                 int32_t *token_slot, void *workspace, hipStream_t s);
 
 hipError_t launch_route_topk_grouped(const float *logits, int64_t T, int E, int k, int n_groups, int topk_groups,
                                      int32_t *idx, float *w, hipStream_t s);

@@ -153,10 +153,16 @@ MOE_API int moe_dispatch(const uint16_t *x, int64_t T, int32_t H, const int32_t 
                             expert_counts, nullptr, token_slot, workspace, workspace_bytes, stream);
 }
 
-MOE_API int moe_route_dispatch(const float *logits, int64_t T, int32_t E, int32_t k, const uint16_t *x, int32_t H,
-                               int32_t capacity, int32_t out_dtype, int32_t *topk_idx, float *topk_w, void *recv_x,
-                               float *recv_scales, int32_t *recv_src, int32_t *expert_counts, int32_t *token_slot,
-                               void *workspace, size_t workspace_bytes, hipStream_t stream)
+}  // extern "C"
+
+namespace {
+
+// Shared checks of moe_route_dispatch (expert_offsets == NULL, fixed slots)
+// and moe_route_dispatch_packed (capacity unused).
+int route_dispatch_checked(const float *logits, int64_t T, int32_t E, int32_t k, const uint16_t *x, int32_t H,
+                           int32_t capacity, int32_t out_dtype, int32_t *topk_idx, float *topk_w, void *recv_x,
+                           float *recv_scales, int32_t *recv_src, int32_t *expert_counts, int32_t *expert_offsets,
+                           int32_t *token_slot, void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
     if (T < 0 || H < 1 || capacity < 1)
         return MOE_ERR_INVALID;
@@ -167,9 +173,10 @@ MOE_API int moe_route_dispatch(const float *logits, int64_t T, int32_t E, int32_
         return MOE_ERR_INVALID;
     if (H % 8 != 0 || (out_dtype == MOE_DTYPE_FP8_E4M3 && H % 128 != 0))
         return MOE_ERR_UNSUPPORTED;
-    if ((int64_t)E * capacity > INT32_MAX || T > MOE_MAX_TOKENS)
+    if ((int64_t)E * capacity > INT32_MAX || T > MOE_MAX_TOKENS || T * (int64_t)k > INT32_MAX)
         return MOE_ERR_UNSUPPORTED;
-    if (!expert_counts || !aligned(expert_counts, 4))
+    int32_t *per_expert = expert_offsets ? expert_offsets : expert_counts;
+    if (!per_expert || !aligned(per_expert, 4))
         return MOE_ERR_INVALID;
     if (T > 0) {
         if (!logits || !x || !topk_idx || !topk_w || !recv_x || !recv_src || !token_slot)
@@ -189,7 +196,31 @@ MOE_API int moe_route_dispatch(const float *logits, int64_t T, int32_t E, int32_
         return MOE_ERR_UNSUPPORTED;
     (void)hipGetLastError();
     return from_hip(moe::launch_route_dispatch(logits, T, E, k, x, H, capacity, out_dtype, topk_idx, topk_w, recv_x,
-                                               recv_scales, recv_src, expert_counts, token_slot, workspace, stream));
+                                               recv_scales, recv_src, expert_counts, expert_offsets, token_slot,
+                                               workspace, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+MOE_API int moe_route_dispatch(const float *logits, int64_t T, int32_t E, int32_t k, const uint16_t *x, int32_t H,
+                               int32_t capacity, int32_t out_dtype, int32_t *topk_idx, float *topk_w, void *recv_x,
+                               float *recv_scales, int32_t *recv_src, int32_t *expert_counts, int32_t *token_slot,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    return route_dispatch_checked(logits, T, E, k, x, H, capacity, out_dtype, topk_idx, topk_w, recv_x, recv_scales,
+                                  recv_src, expert_counts, nullptr, token_slot, workspace, workspace_bytes, stream);
+}
+
+MOE_API int moe_route_dispatch_packed(const float *logits, int64_t T, int32_t E, int32_t k, const uint16_t *x,
+                                      int32_t H, int32_t out_dtype, int32_t *topk_idx, float *topk_w, void *recv_x,
+                                      float *recv_scales, int32_t *recv_src, int32_t *expert_offsets,
+                                      int32_t *token_slot, void *workspace, size_t workspace_bytes,
+                                      hipStream_t stream)
+{
+    return route_dispatch_checked(logits, T, E, k, x, H, 1, out_dtype, topk_idx, topk_w, recv_x, recv_scales,
+                                  recv_src, nullptr, expert_offsets, token_slot, workspace, workspace_bytes, stream);
 }
 
 MOE_API int moe_dispatch_packed(const uint16_t *x, int64_t T, int32_t H, const int32_t *topk_idx, int32_t E,

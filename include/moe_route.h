@@ -243,6 +243,31 @@ MOE_API int moe_dispatch_packed(const uint16_t *x, int64_t T, int32_t H, const i
                                 void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * moe_route_dispatch_packed -- moe_route_topk followed by
+ * moe_dispatch_packed in one call.
+ *
+ * The same steps and citations as the two calls; every output (topk_idx,
+ * topk_w, expert_offsets, token_slot, recv_src, recv_x, recv_scales) is
+ * identical to calling moe_route_topk and then moe_dispatch_packed.  For
+ * E <= 8 and more than 256 tokens the count step is folded into the
+ * router's kernel as in moe_route_dispatch, and one work-group totals the
+ * router's membership words into expert_offsets: three kernel launches
+ * instead of four.  (Up to 256 tokens the two calls are already two
+ * launches.)
+ *
+ *   logits, T, E, k, topk_idx, topk_w: as for moe_route_topk
+ *   x, H, out_dtype, recv_x, recv_scales, recv_src, expert_offsets,
+ *   token_slot, workspace (moe_dispatch_workspace_bytes(T, E, k) bytes),
+ *   workspace_bytes, stream: as for moe_dispatch_packed
+ * Buffers must not overlap.
+ */
+MOE_API int moe_route_dispatch_packed(const float *logits, int64_t T, int32_t E, int32_t k, const uint16_t *x,
+                                      int32_t H, int32_t out_dtype, int32_t *topk_idx, float *topk_w,
+                                      void *recv_x, float *recv_scales, int32_t *recv_src,
+                                      int32_t *expert_offsets, int32_t *token_slot, void *workspace,
+                                      size_t workspace_bytes, hipStream_t stream);
+
+/*
  * moe_combine -- gather each token's k expert outputs and return their
  * router-weighted sum in the original token order.
  *

@@ -8,7 +8,9 @@ to the separate moe_route_topk + moe_dispatch calls.  Cases: the five
 workloads (E = 8 on the fused path, E = 128 and 256 on the three-step path),
 token counts around the 32-token word and 256-token chunk boundaries, every
 E <= 8 with every k, capacity overflow, fp8 rows, and token counts past the
-fused path's limit.
+fused path's limit.  The same cases for moe_route_dispatch_packed against
+the oracle's packed, count-sized layout and moe_route_topk +
+moe_dispatch_packed.
 """
 import numpy as np
 import pytest
@@ -109,3 +111,79 @@ def test_empty(dev):
     x = torch.empty(0, 64, dtype=torch.bfloat16, device=dev)
     i, w, b = moe.moe_route_dispatch(lg, x, 2, 4)
     assert (b.expert_counts.cpu().numpy() == 0).all()
+
+
+
+# ---- moe_route_dispatch_packed ----
+
+def _run_both_packed(dev, logits, x_bits, k, fp8):
+    T, E = logits.shape
+    lg = torch.from_numpy(logits).to(dev)
+    xd = to_dev_bf16(x_bits, dev)
+    i1, w1, b1 = moe.moe_route_dispatch_packed(lg, xd, k, fp8=fp8)
+    i2, w2 = moe.moe_route_topk(lg, k)
+    b2 = moe.moe_dispatch_packed(xd, i2, E, fp8=fp8)
+    return (i1, w1, b1), (i2, w2, b2)
+
+
+def _check_packed(label, logits, x_bits, k, fp8, fused, separate):
+    T, E = logits.shape
+    H = x_bits.shape[1]
+    i1, w1, b1 = fused
+    i2, w2, b2 = separate
+    say(f"[route+dispatch packed] {label}: T={T} E={E} k={k} fp8={fp8}")
+    idx_o, w_o = oracle.route_topk(logits, k)
+    offs_o, slot_o, src_o = oracle.assign_packed(idx_o, E)
+    np.testing.assert_array_equal(i1.cpu().numpy(), idx_o)
+    np.testing.assert_allclose(w1.cpu().numpy(), w_o, rtol=W_RTOL, atol=0)
+    np.testing.assert_array_equal(b1.expert_offsets.cpu().numpy(), offs_o)
+    np.testing.assert_array_equal(b1.token_slot.cpu().numpy(), slot_o)
+    np.testing.assert_array_equal(b1.recv_src.cpu().numpy().reshape(-1)[:T * k], src_o)
+    if fp8:
+        c_tok, s_tok = oracle.quantize_rows_fp8(x_bits)
+        np.testing.assert_array_equal(b1.recv_x.cpu().numpy(), c_tok[src_o])
+        np.testing.assert_array_equal(b1.recv_scales.cpu().numpy(), s_tok[src_o])
+    else:
+        np.testing.assert_array_equal(dev_bits(b1.recv_x), x_bits[src_o])
+    # identical to the separate calls, bit for bit
+    assert torch.equal(i1, i2) and torch.equal(w1.view(torch.int32), w2.view(torch.int32))
+    assert torch.equal(b1.expert_offsets, b2.expert_offsets) and torch.equal(b1.token_slot, b2.token_slot)
+    assert torch.equal(b1.recv_src, b2.recv_src) and torch.equal(b1.recv_x.view(torch.uint8), b2.recv_x.view(torch.uint8))
+    if fp8:
+        assert torch.equal(b1.recv_scales.view(torch.int32), b2.recv_scales.view(torch.int32))
+
+
+@pytest.mark.parametrize("name", W.ORDER)
+def test_packed_workloads(dev, name):
+    w = W.WORKLOADS[name]
+    o = OracleRun.get(w)
+    fused, separate = _run_both_packed(dev, o.logits, o.x, w.k, w.fp8)
+    _check_packed(name, o.logits, o.x, w.k, w.fp8, fused, separate)
+
+
+@pytest.mark.parametrize("T", [1, 31, 32, 33, 255, 256, 257, 1000, 65536, 65537])
+def test_packed_token_counts(dev, T):
+    rng = np.random.default_rng(T + 7)
+    E, k, H = 8, 2, 64
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    x = W.bits(torch.from_numpy(rng.standard_normal((T, H)).astype(np.float32)).to(torch.bfloat16))
+    fused, separate = _run_both_packed(dev, logits, x, k, False)
+    _check_packed(f"T={T}", logits, x, k, False, fused, separate)
+
+
+@pytest.mark.parametrize("E", [1, 3, 8])
+def test_packed_every_k(dev, E):
+    rng = np.random.default_rng(200 + E)
+    T, H = 777, 128
+    x = W.bits(torch.from_numpy(rng.standard_normal((T, H)).astype(np.float32)).to(torch.bfloat16))
+    for k in range(1, E + 1):
+        logits = rng.integers(-2, 3, (T, E)).astype(np.float32)     # ties everywhere
+        fused, separate = _run_both_packed(dev, logits, x, k, k % 2 == 1)
+        _check_packed(f"E={E} k={k}", logits, x, k, k % 2 == 1, fused, separate)
+
+
+def test_packed_empty(dev):
+    lg = torch.empty(0, 8, device=dev)
+    x = torch.empty(0, 64, dtype=torch.bfloat16, device=dev)
+    i, w, b = moe.moe_route_dispatch_packed(lg, x, 2)
+    assert (b.expert_offsets.cpu().numpy() == 0).all()

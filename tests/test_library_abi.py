@@ -32,7 +32,7 @@ def lib():
 
 def test_header_declares_the_entry_points():
     names = _declared()
-    for n in ("moe_route_topk", "moe_route_topk_grouped", "moe_dispatch", "moe_dispatch_packed", "moe_route_dispatch",
+    for n in ("moe_route_topk", "moe_route_topk_grouped", "moe_dispatch", "moe_dispatch_packed", "moe_route_dispatch", "moe_route_dispatch_packed",
               "moe_combine",
               "moe_combine_residual_rmsnorm", "moe_combine_residual_rmsnorm_fp8", "moe_dispatch_workspace_bytes",
               "moe_status_string"):
@@ -131,6 +131,13 @@ def test_host_validation_without_device(lib):
     assert rd(P, 4, 8, 2, P, 100, 4, 0, P, P, P, P, P, P, P, P, 0, P) == -2   # H % 8
     assert rd(P, 4, 8, 2, P, 192, 4, 1, P, P, P, P, P, P, P, P, 0, P) == -2   # fp8 needs H % 128
     assert rd(P, 4, 4096, 2, P, 64, 4, 0, P, P, P, P, P, P, P, P, 0, P) == -2 # E above the limit
+    rp = lib.moe_route_dispatch_packed
+    assert rp(P, 4, 8, 2, P, 64, 0, P, P, P, P, P, P, P, P, 0, P) == -1        # null pointers
+    assert rp(P, 4, 8, 9, P, 64, 0, P, P, P, P, P, P, P, P, 0, P) == -1        # k > E
+    assert rp(P, 4, 8, 2, P, 100, 0, P, P, P, P, P, P, P, P, 0, P) == -2       # H % 8
+    assert rp(P, 4, 8, 2, P, 192, 1, P, P, P, P, P, P, P, P, 0, P) == -2       # fp8 needs H % 128
+    assert rp(P, 4, 8, 2, P, 64, 2, P, P, P, P, P, P, P, P, 0, P) == -1        # bad dtype
+    assert rp(P, 1 << 25, 8, 2, P, 64, 0, P, P, P, P, P, P, P, P, 0, P) == -2  # T above the limit
     pk = lib.moe_dispatch_packed
     assert pk(P, 4, 64, P, 8, 2, 0, P, P, P, P, P, P, 0, P) == -1        # null pointers
     assert pk(P, 4, 64, P, 8, 2, 2, P, P, P, P, P, P, 0, P) == -1        # bad dtype
