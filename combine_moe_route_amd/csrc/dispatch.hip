@@ -17,7 +17,7 @@
 //           writes the chunk's per-expert histogram and each pair's rank
 //           inside the chunk (popcount of the mask below its bit).
 //   pack:   one wave per (token, row segment) requests all of its row
-//           vectors, and while they are in flight finishes the k slots:
+//           vectors, then works out the k slots:
 //           offset = sum of the expert's counts in earlier chunks (an
 //           exclusive prefix over a few L2-resident histogram words),
 //           slot = e*C + offset + rank, dropped when >= C.  Segment 0
@@ -25,16 +25,17 @@
 //           each slot -- bf16 bit copies, or E4M3 codes with per-128 fp32
 //           scales.  The first E waves also write the true totals.
 // A batch of at most 256 tokens is a single chunk: then there is no count
-// launch, and every pack work-group rebuilds the chunk's masks in LDS.
+// launch, and every pack work-group rebuilds the chunk's masks in LDS from
+// ids it requests before the rows.
 // Route + dispatch in one call with E <= 8: the router already wrote one
 // membership word per expert and 32-token chunk, and pack takes prefixes and
 // ranks from their popcounts (no count launch either).
 // Packed, count-sized layout (handbook "High-throughput mode": count first,
 // then a receive buffer of exactly the needed size): between count and
-// pack, one work-group sums each expert's chunk counts and scans them into
-// offsets[E+1] (a single chunk's pack work-groups scan their LDS counts);
-// pack then uses slot = offsets[e] + offset + rank, with no capacity and
-// nothing dropped.
+// pack, one work-group sums each expert's chunk counts (or the popcounts of
+// the router's words) and scans them into offsets[E+1] (a single chunk's
+// pack work-groups scan their LDS counts); pack then uses slot = offsets[e]
+// + offset + rank, with no capacity and nothing dropped.
 // Slot rows are written with non-temporal stores: each byte is written once
 // per call.
 #include "device_common.hpp"
@@ -410,9 +411,11 @@ __device__ __forceinline__ void wave_totals(int64_t task, int64_t ntasks, const 
 constexpr int kMaxV = 16;  // most 16-byte vectors per lane in flight (bf16 rows)
 
 // bf16 rows: one wave per (token, row segment).  The lane's vectors
-// seg*VPL*64 + i*64 + lane (i < VPL) are all requested first; the slot
-// arithmetic runs while they are in flight; then every vector is stored to
-// each of the k slots.  No work-group barrier: the waves' latency chains
+// seg*VPL*64 + i*64 + lane (i < VPL) are all requested first, then the
+// slots are worked out, then every vector is stored to each of the k slots.
+// LOCAL (a single 256-token chunk): the work-group first rebuilds the
+// chunk's masks in LDS (two barriers) from ids requested before the rows.
+// Otherwise there is no work-group barrier and the waves' latency chains
 // overlap freely.
 template <int VPL, bool LOCAL>
 __global__ __launch_bounds__(kBlock) void dispatch_pack_bf16_kernel(
@@ -488,7 +491,8 @@ constexpr int kMaxG = 8;   // most 16-element groups per lane in flight (fp8 row
 // 128-element block find its amax with three DPP steps; the scale is
 // amax/448 (IEEE division; 1 for an all-zero block) and each code is the
 // E4M3 encoding (round to nearest even, saturating) of x / scale, with the
-// quotient bit-identical to an IEEE division (divide_by_scale).
+// quotient bit-identical to an IEEE division (divide_all).  The load order
+// and LOCAL are as in the bf16 kernel.
 template <int VPL, bool LOCAL>
 __global__ __launch_bounds__(kBlock) void dispatch_pack_fp8_kernel(
     const u32x4 *__restrict__ x, int64_t T, int ngrp, const int32_t *__restrict__ topk_idx,
