@@ -18,6 +18,30 @@ bool overlaps(const void *a, uint64_t na, const void *b, uint64_t nb)
     return a0 < b0 + nb && b0 < a0 + na;
 }
 
+// A buffer as a byte range; n == 0 marks one that is absent or unused.
+struct Region {
+    const void *p;
+    uint64_t n;
+};
+
+// Does an output overlap an input or another output?  (Inputs may share
+// memory with each other.)
+template <int NO, int NI>
+bool any_overlap(const Region (&out)[NO], const Region (&in)[NI])
+{
+    for (int i = 0; i < NO; ++i) {
+        if (!out[i].n)
+            continue;
+        for (int j = 0; j < NI; ++j)
+            if (in[j].n && overlaps(out[i].p, out[i].n, in[j].p, in[j].n))
+                return true;
+        for (int j = i + 1; j < NO; ++j)
+            if (out[j].n && overlaps(out[i].p, out[i].n, out[j].p, out[j].n))
+                return true;
+    }
+    return false;
+}
+
 int from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 // Shared checks of E and k.
@@ -65,6 +89,19 @@ int dispatch_checked(const uint16_t *x, int64_t T, int32_t H, const int32_t *top
     const size_t need = moe::dispatch_workspace_bytes(T, E, k);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
         return MOE_ERR_WORKSPACE;
+    if (T > 0) {
+        const uint64_t rows = expert_offsets ? (uint64_t)T * k : (uint64_t)E * capacity;
+        const uint64_t row_bytes = out_dtype == MOE_DTYPE_FP8_E4M3 ? (uint64_t)H : 2 * (uint64_t)H;
+        const Region in[] = {{x, (uint64_t)T * H * 2}, {topk_idx, (uint64_t)T * k * 4}};
+        const Region out[] = {{recv_x, rows * row_bytes},
+                              {recv_scales, recv_scales ? rows * (H / 128) * 4 : 0},
+                              {recv_src, rows * 4},
+                              {per_expert, (uint64_t)(expert_offsets ? E + 1 : E) * 4},
+                              {token_slot, (uint64_t)T * k * 4},
+                              {workspace, need}};
+        if (any_overlap(out, in))
+            return MOE_ERR_INVALID;
+    }
     if (!moe::dispatch_grid_fits(T, H, k, out_dtype))
         return MOE_ERR_UNSUPPORTED;
     (void)hipGetLastError();
@@ -104,6 +141,10 @@ MOE_API int moe_route_topk(const float *logits, int64_t T, int32_t E, int32_t k,
         return MOE_ERR_INVALID;
     if (T > MOE_MAX_TOKENS)
         return MOE_ERR_UNSUPPORTED;
+    const Region in[] = {{logits, (uint64_t)T * E * 4}};
+    const Region out[] = {{topk_idx, (uint64_t)T * k * 4}, {topk_w, (uint64_t)T * k * 4}};
+    if (any_overlap(out, in))
+        return MOE_ERR_INVALID;
     (void)hipGetLastError();
     return from_hip(moe::launch_route_topk(logits, T, E, k, topk_idx, topk_w, stream));
 }
@@ -129,6 +170,10 @@ MOE_API int moe_route_topk_grouped(const float *logits, int64_t T, int32_t E, in
         return MOE_ERR_INVALID;
     if (T > MOE_MAX_TOKENS)
         return MOE_ERR_UNSUPPORTED;
+    const Region in[] = {{logits, (uint64_t)T * E * 4}};
+    const Region out[] = {{topk_idx, (uint64_t)T * k * 4}, {topk_w, (uint64_t)T * k * 4}};
+    if (any_overlap(out, in))
+        return MOE_ERR_INVALID;
     (void)hipGetLastError();
     return from_hip(moe::launch_route_topk_grouped(logits, T, E, k, n_groups, topk_groups, topk_idx, topk_w, stream));
 }
@@ -192,6 +237,21 @@ int route_dispatch_checked(const float *logits, int64_t T, int32_t E, int32_t k,
     const size_t need = moe::dispatch_workspace_bytes(T, E, k);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
         return MOE_ERR_WORKSPACE;
+    if (T > 0) {
+        const uint64_t rows = expert_offsets ? (uint64_t)T * k : (uint64_t)E * capacity;
+        const uint64_t row_bytes = out_dtype == MOE_DTYPE_FP8_E4M3 ? (uint64_t)H : 2 * (uint64_t)H;
+        const Region in[] = {{logits, (uint64_t)T * E * 4}, {x, (uint64_t)T * H * 2}};
+        const Region out[] = {{topk_idx, (uint64_t)T * k * 4},
+                              {topk_w, (uint64_t)T * k * 4},
+                              {recv_x, rows * row_bytes},
+                              {recv_scales, recv_scales ? rows * (H / 128) * 4 : 0},
+                              {recv_src, rows * 4},
+                              {per_expert, (uint64_t)(expert_offsets ? E + 1 : E) * 4},
+                              {token_slot, (uint64_t)T * k * 4},
+                              {workspace, need}};
+        if (any_overlap(out, in))
+            return MOE_ERR_INVALID;
+    }
     if (!moe::dispatch_grid_fits(T, H, k, out_dtype))
         return MOE_ERR_UNSUPPORTED;
     (void)hipGetLastError();
@@ -252,10 +312,12 @@ int combine_checked(const uint16_t *y, int32_t E, int32_t capacity, int32_t H, c
         return MOE_ERR_INVALID;
     if (!aligned(y, 16) || !aligned(out, 16) || !aligned(token_slot, 4) || !aligned(topk_w, 4))
         return MOE_ERR_INVALID;
-    const uintptr_t y0 = (uintptr_t)y, y1 = y0 + (uintptr_t)E * capacity * H * 2;
-    const uintptr_t o0 = (uintptr_t)out, o1 = o0 + (uintptr_t)T * H * 2;
-    if (o0 < y1 && y0 < o1)
-        return MOE_ERR_INVALID;  // out overlaps y
+    const Region in[] = {{y, (uint64_t)E * capacity * H * 2},
+                         {token_slot, (uint64_t)T * k * 4},
+                         {topk_w, (uint64_t)T * k * 4}};
+    const Region out_r[] = {{out, (uint64_t)T * H * 2}};
+    if (any_overlap(out_r, in))
+        return MOE_ERR_INVALID;
     if (!moe::combine_grid_fits(T, H, k))
         return MOE_ERR_UNSUPPORTED;
     (void)hipGetLastError();
@@ -305,24 +367,17 @@ int norm_checked(const uint16_t *y, int32_t E, int32_t capacity, int32_t H, cons
     const uint64_t ybytes = (uint64_t)E * capacity * H * 2, row_bytes = (uint64_t)T * H * 2;
     // outputs must not overlap the inputs or each other; residual_out may be
     // residual itself (an in-place update of the residual stream)
-    struct Region {
-        const void *p;
-        uint64_t n;
-    };
-    const Region in[] = {{y, ybytes}, {residual, row_bytes}, {gamma, 2 * (uint64_t)H},
-                         {token_slot, (uint64_t)T * k * 4}, {topk_w, (uint64_t)T * k * 4}};
-    const Region out[] = {{residual_out, row_bytes}, {normed_out, normed_out ? row_bytes : 0},
-                          {normed_q, q ? (uint64_t)T * H : 0}, {normed_scales, q ? (uint64_t)T * (H / 128) * 4 : 0}};
-    for (int i = 0; i < 4; ++i) {
-        if (!out[i].n)
-            continue;
-        for (const Region &r : in)
-            if (!(i == 0 && r.p == residual && residual_out == residual) && overlaps(out[i].p, out[i].n, r.p, r.n))
-                return MOE_ERR_INVALID;
-        for (int j = i + 1; j < 4; ++j)
-            if (out[j].n && overlaps(out[i].p, out[i].n, out[j].p, out[j].n))
-                return MOE_ERR_INVALID;
-    }
+    const Region in[] = {{y, ybytes},
+                         {residual, residual_out == residual ? 0 : row_bytes},
+                         {gamma, 2 * (uint64_t)H},
+                         {token_slot, (uint64_t)T * k * 4},
+                         {topk_w, (uint64_t)T * k * 4}};
+    const Region out[] = {{residual_out, row_bytes},
+                          {normed_out, normed_out ? row_bytes : 0},
+                          {normed_q, q ? (uint64_t)T * H : 0},
+                          {normed_scales, q ? (uint64_t)T * (H / 128) * 4 : 0}};
+    if (any_overlap(out, in))
+        return MOE_ERR_INVALID;
     (void)hipGetLastError();
     return from_hip(moe::launch_combine_rmsnorm(y, (int64_t)E * capacity, H, token_slot, topk_w, T, k, residual,
                                                 gamma, eps, residual_out, normed_out, normed_q, normed_scales,

@@ -29,6 +29,9 @@
  *   - Arguments are checked on the host before anything is enqueued.  The
  *     return value is MOE_OK or a negative MOE_ERR_* code; on error nothing
  *     was enqueued.  MOE_ERR_HIP reports a failed kernel launch.
+ *   - No output (workspace included) may overlap an input or another output
+ *     over the bytes the call touches: MOE_ERR_INVALID.  Inputs may share
+ *     memory.  The one exception is documented where it applies.
  *   - Arrays are dense and row-major.  bf16 values are passed as their
  *     16-bit patterns (uint16_t).  Buffers read or written in 16-byte
  *     vectors (x, recv_x, y, out) must be 16-byte aligned.

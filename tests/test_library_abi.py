@@ -154,30 +154,81 @@ def test_host_validation_without_device(lib):
     assert d(P, 4, 64, P, 8, 9, 4, 0, P, P, P, P, P, P, 0, P) == -1     # k > E
 
 
+def _fake_layout(*sizes):
+    """Fake, 256 B aligned, non-overlapping device addresses for buffers of
+    the given byte sizes (never dereferenced)."""
+    addr, out = 1 << 20, []
+    for n in sizes:
+        out.append(addr)
+        addr += (n + 255) // 256 * 256 + 256
+    return out
+
+
 @pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="passes fake device addresses; host-only check")
 def test_grids_beyond_one_launch_are_unsupported(lib):
     """A dispatch or combine whose single launch would need more than 2^32 - 1
     work-items is refused on the host with MOE_ERR_UNSUPPORTED before
     anything is enqueued (T = 2^24 tokens of 65536 elements)."""
-    A = 1 << 20                                  # fake, 256 B aligned addresses, never dereferenced
-    T, H, E, k = 1 << 24, 65536, 8, 2
+    T, E, k = 1 << 24, 8, 2
     ws = moe.moe_dispatch_workspace_bytes(T, E, k)
     assert ws > 0
     d = lib.moe_dispatch
-    for dtype, scales in ((0, None), (1, A + 3 * 256)):
-        assert d(A, T, H, A + 256, E, k, T, dtype, A + 2 * 256, scales, A + 4 * 256, A + 5 * 256, A + 6 * 256,
-                 A, ws, None) == -2
-    assert lib.moe_dispatch_packed(A, T, H, A + 256, E, k, 0, A + 2 * 256, None, A + 4 * 256, A + 5 * 256,
-                                   A + 6 * 256, A, ws, None) == -2
-    assert lib.moe_route_dispatch(A + 7 * 256, T, E, k, A, H, T, 0, A + 256, A + 8 * 256, A + 2 * 256, None,
-                                  A + 4 * 256, A + 5 * 256, A + 6 * 256, A, ws, None) == -2
+
+    def dispatch(H, dtype, packed=False):
+        rows = T * k if packed else E * T
+        row = H if dtype else 2 * H
+        x, idx, rx, sc, src, cnt, slot, w = _fake_layout(T * H * 2, T * k * 4, rows * row, rows * (H // 128) * 4,
+                                                         rows * 4, (E + 1) * 4, T * k * 4, ws)
+        if packed:
+            return lib.moe_dispatch_packed(x, T, H, idx, E, k, dtype, rx, sc if dtype else None, src, cnt, slot, w,
+                                           ws, None)
+        return d(x, T, H, idx, E, k, T, dtype, rx, sc if dtype else None, src, cnt, slot, w, ws, None)
+
+    H = 65536
+    assert dispatch(H, 0) == -2
+    assert dispatch(H, 1) == -2
+    assert dispatch(H, 0, packed=True) == -2
+    lg, x, idx, tw, rx, src, cnt, slot, w = _fake_layout(T * E * 4, T * H * 2, T * k * 4, T * k * 4, E * T * 2 * H,
+                                                         E * T * 4, E * 4, T * k * 4, ws)
+    assert lib.moe_route_dispatch(lg, T, E, k, x, H, T, 0, idx, tw, rx, None, src, cnt, slot, w, ws, None) == -2
     # combine: y of E x C rows, out placed after it
-    y_bytes = E * 4 * H * 2
-    assert lib.moe_combine(A, E, 4, H, A + y_bytes, A + y_bytes + 256, T, k, A + (1 << 30), None) == -2
+    y, ts, tw, out = _fake_layout(E * 4 * H * 2, T * k * 4, T * k * 4, T * H * 2)
+    assert lib.moe_combine(y, E, 4, H, ts, tw, T, k, out, None) == -2
     # control: at H = 4096 the same calls pass every host check and reach the
     # launch, which fails with MOE_ERR_HIP on a host without a GPU
-    h = 4096
-    assert d(A, T, h, A + 256, E, k, T, 0, A + 2 * 256, None, A + 4 * 256, A + 5 * 256, A + 6 * 256, A, ws,
-             None) == -4
-    assert lib.moe_combine(A, E, 4, h, A + E * 4 * h * 2, A + E * 4 * h * 2 + 256, T, k, A + (1 << 30),
-                           None) == -4
+    assert dispatch(4096, 0) == -4
+    y, ts, tw, out = _fake_layout(E * 4 * 4096 * 2, T * k * 4, T * k * 4, T * 4096 * 2)
+    assert lib.moe_combine(y, E, 4, 4096, ts, tw, T, k, out, None) == -4
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="passes fake device addresses; host-only check")
+def test_overlapping_buffers_are_rejected(lib):
+    """Every entry point refuses an output that overlaps an input or another
+    output, on the host, before anything is enqueued."""
+    T, E, k, H = 64, 8, 2, 256
+    ws = moe.moe_dispatch_workspace_bytes(T, E, k)
+    lg, x, idx, tw, rx, sc, src, cnt, slot, w = _fake_layout(T * E * 4, T * H * 2, T * k * 4, T * k * 4,
+                                                             E * T * H * 2, E * T * (H // 128) * 4, E * T * 4,
+                                                             (E + 1) * 4, T * k * 4, ws)
+    r = lib.moe_route_topk
+    assert r(lg, T, E, k, lg + 64, tw, None) == -1                       # ids inside the logits
+    assert r(lg, T, E, k, idx, idx + 64, None) == -1                     # weights inside the ids
+    assert lib.moe_route_topk_grouped(lg, T, E, k, 2, 1, idx, lg, None) == -1
+    d = lib.moe_dispatch
+    assert d(x, T, H, idx, E, k, T, 0, rx, None, src, cnt, slot, w, ws, None) == -4    # control (no GPU)
+    assert d(x, T, H, idx, E, k, T, 0, x + 512, None, src, cnt, slot, w, ws, None) == -1  # rows over x
+    assert d(x, T, H, idx, E, k, T, 0, rx, None, src, cnt, idx, w, ws, None) == -1        # slots over ids
+    assert d(x, T, H, idx, E, k, T, 0, rx, None, src, cnt, slot, src, ws, None) == -1     # workspace over src
+    assert d(x, T, H, idx, E, k, T, 1, rx, rx + 4096, src, cnt, slot, w, ws, None) == -1  # scales inside codes
+    pk = lib.moe_dispatch_packed
+    assert pk(x, T, H, idx, E, k, 0, rx, None, src, src + 8, slot, w, ws, None) == -1     # offsets inside src
+    rd = lib.moe_route_dispatch
+    assert rd(lg, T, E, k, x, H, T, 0, idx, tw, rx, None, src, cnt, slot, w, ws, None) == -4  # control
+    assert rd(lg, T, E, k, x, H, T, 0, idx, lg, rx, None, src, cnt, slot, w, ws, None) == -1  # weights over logits
+    assert rd(lg, T, E, k, x, H, T, 0, idx, tw, rx, None, src, cnt, tw, w, ws, None) == -1   # slots over weights
+    rp = lib.moe_route_dispatch_packed
+    assert rp(lg, T, E, k, x, H, 0, idx, tw, rx, None, src, rx + 1024, slot, w, ws, None) == -1
+    c = lib.moe_combine
+    y, out = rx, x
+    assert c(y, E, T, H, slot, tw, T, k, out, None) == -4                # control
+    assert c(y, E, T, H, slot, tw, T, k, slot, None) == -1               # out over the slots
