@@ -153,6 +153,12 @@ def test_empty_combine_and_route(dev):
     (200, 640, 8, 2, 200, False, "equal"),        # all-equal logits
     (129, 7168, 256, 8, 129, True, "normal"),
     (4100, 64, 64, 8, 4100, False, "normal"),     # many chunks
+    # grids large enough to keep each pack split (bf16 aims at 8/k vectors per lane)
+    (4096, 4096, 8, 1, 4096, False, "normal"),    # 8 vectors per lane
+    (4096, 2056, 16, 2, 4096, False, "normal"),   # 4, ragged last segment
+    (3000, 2056, 16, 3, 3000, False, "ties"),     # 2, ragged
+    (2500, 1024, 64, 4, 2500, False, "normal"),   # 2
+    (2300, 1024, 32, 1, 2300, True, "normal"),    # fp8: 2 groups per lane
 ])
 def test_shapes(dev, T, H, E, k, C, fp8, kind):
     run_case(dev, T, H, E, k, C, fp8, kind)
