@@ -329,6 +329,33 @@ def main() -> int:
     # the same steps without timing events, for comparison
     plain_ms = timed(Wm + K, K, S)
 
+    # each call alone: events recorded around route + dispatch and around
+    # combine for ~K/4 steps, a pass of its own outside the timed region
+    per_call = None
+    if S == 1:
+        n = max(8, K // 4)
+        marks = [(hip_events.create(), hip_events.create(), hip_events.create()) for _ in range(n)]
+        torch.cuda.synchronize()
+        for i, (a, b, c) in enumerate(marks):
+            st = sets[(Wm + 2 * K + i) % R].step
+            hip_events.record(a, main)
+            st.route_and_dispatch()
+            hip_events.record(b, main)
+            st.combine()
+            hip_events.record(c, main)
+        torch.cuda.synchronize()
+
+        def stats(v):
+            v = sorted(x * 1e3 for x in v)
+            return {"median": v[len(v) // 2], "min": v[0], "max": v[-1]}
+        per_call = {"steps": n,
+                    "route_dispatch_us": stats([hip_events.elapsed_ms(a, b) for a, b, _ in marks]),
+                    "combine_us": stats([hip_events.elapsed_ms(b, c) for _, b, c in marks]),
+                    "timing": "device-release HIP events recorded around each call, one step at a time"}
+        for trio in marks:
+            for e in trio:
+                hip_events.destroy(e)
+
     # the same steps replayed from HIP graphs (one captured step per buffer
     # set): no host launch cost, so small batches show their GPU time
     graph = None
@@ -409,6 +436,7 @@ def main() -> int:
             "ms_per_step_without_timing_events": plain_ms,
             "two_batches_in_flight": overlap,
             "graph_replay": graph,
+            "per_call": per_call,
         },
         "roofline": {
             "kernel": (f"combine_rmsnorm_kernel (k={w.k}{', fp8 out' if epilogue == 'rmsnorm-fp8' else ''})"
@@ -422,6 +450,7 @@ def main() -> int:
             "traffic_source": f"profiles/{w.name}_hbm_traffic.md (bytes per launch)",
             "algorithmic_bytes_per_launch": nbytes["combine"],
             "mean_launch_us": combine_ms * 1e3,
+            "median_launch_us": sorted(combine_times)[len(combine_times) // 2] * 1e3,
             "timed_launches": len(combine_times),
             "min_launch_us": min(combine_times) * 1e3,
             "max_launch_us": max(combine_times) * 1e3,
