@@ -148,6 +148,9 @@ def _need(t: torch.Tensor, dtype, shape, name: str):
         raise ValueError(f"{name}: must be contiguous")
     if t.device.type != "cuda":
         raise ValueError(f"{name}: must be a device tensor")
+    if t.device.index is not None and t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name}: on {t.device}, but the current device (where the kernels run) is "
+                         f"cuda:{torch.cuda.current_device()}")
 
 
 def moe_route_topk(logits: torch.Tensor, k: int, topk_idx: torch.Tensor | None = None,
