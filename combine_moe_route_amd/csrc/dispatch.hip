@@ -41,6 +41,7 @@
 #include "device_common.hpp"
 #include "fp8_e4m3.hpp"
 #include "kernels.hpp"
+#include "route_core.hpp"
 
 namespace moe {
 namespace {
@@ -238,24 +239,14 @@ __device__ __forceinline__ void local_ids_load(const int32_t *__restrict__ topk_
     }
 }
 
-__device__ __forceinline__ void local_chunk_counts(const int (&ids)[kLocalIds], int E, int k, bool packed,
-                                                   uint32_t *lmask, int32_t *loffs, int32_t *wave_sums,
-                                                   int32_t *__restrict__ expert_counts,
-                                                   int32_t *__restrict__ expert_offsets)
+// The chunk's per-expert totals from its complete LDS masks: work-group 0
+// writes them (fixed slots), or every work-group scans them into loffs and
+// work-group 0 writes the offsets (packed layout).  All threads call it.
+__device__ __forceinline__ void local_totals(int E, bool packed, const uint32_t *lmask, int32_t *loffs,
+                                             int32_t *wave_sums, int32_t *__restrict__ expert_counts,
+                                             int32_t *__restrict__ expert_offsets)
 {
     const int tid = threadIdx.x;
-    for (int i = tid; i < E * kMaskWords; i += kBlock)
-        lmask[i] = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < kLocalIds; ++q) {
-        const int e = ids[q];   // pair p = tid + q*256 of token p / k; -1 past the end
-        if ((unsigned)e < (unsigned)E) {
-            const int tok = (tid + q * kBlock) / k;
-            atomicOr(&lmask[e * kMaskWords + (tok >> 5)], 1u << (tok & 31));
-        }
-    }
-    __syncthreads();
     for (int e = tid; e < E; e += kBlock) {
         int n = 0;
 #pragma unroll
@@ -274,6 +265,90 @@ __device__ __forceinline__ void local_chunk_counts(const int (&ids)[kLocalIds], 
             for (int e = tid; e <= E; e += kBlock)
                 expert_offsets[e] = loffs[e];
     }
+}
+
+__device__ __forceinline__ void local_chunk_counts(const int (&ids)[kLocalIds], int E, int k, bool packed,
+                                                   uint32_t *lmask, int32_t *loffs, int32_t *wave_sums,
+                                                   int32_t *__restrict__ expert_counts,
+                                                   int32_t *__restrict__ expert_offsets)
+{
+    const int tid = threadIdx.x;
+    for (int i = tid; i < E * kMaskWords; i += kBlock)
+        lmask[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kLocalIds; ++q) {
+        const int e = ids[q];   // pair p = tid + q*256 of token p / k; -1 past the end
+        if ((unsigned)e < (unsigned)E) {
+            const int tok = (tid + q * kBlock) / k;
+            atomicOr(&lmask[e * kMaskWords + (tok >> 5)], 1u << (tok & 31));
+        }
+    }
+    __syncthreads();
+    local_totals(E, packed, lmask, loffs, wave_sums, expert_counts, expert_offsets);
+}
+
+// Route + dispatch of a batch of at most 256 tokens with E <= 8 in one
+// launch: every pack work-group routes the whole batch itself -- 8-lane
+// groups, 32 tokens per pass, the router's own selection and softmax code,
+// so the choices and weights are those of moe_route_topk bit for bit --
+// keeping the choices in LDS (ids and membership masks); work-group 0 also
+// stores ids, weights and totals.  A lane's logits for all passes are
+// requested before the row loads, for the reason given at local_ids_load.
+constexpr int kRoutePasses = kChunk / kMaskChunk;   // 8 passes of 32 tokens
+
+// Pack kernel modes: slots from chunk histograms or router membership words
+// (several chunks); a single chunk counted in LDS from the ids; a single
+// chunk routed in LDS by every work-group.
+constexpr int kPackChunks = 0;
+constexpr int kPackLocalIds = 1;
+constexpr int kPackLocalRoute = 2;
+
+__device__ __forceinline__ void route_logits_load(const float *__restrict__ logits, int64_t T, int E,
+                                                  float (&v)[kRoutePasses], uint32_t (&key)[kRoutePasses])
+{
+    const int gl = lane_id() % 8;
+#pragma unroll
+    for (int p = 0; p < kRoutePasses; ++p) {
+        const int64_t tt = p * kMaskChunk + (int)threadIdx.x / 8;
+        float vv[1];
+        uint32_t kk[1];
+        route_core::load_logits<1, false>(logits, tt, tt < T, E, gl, vv, kk);
+        v[p] = vv[0];
+        key[p] = kk[0];
+    }
+}
+
+__device__ __forceinline__ void route_local_counts(const float (&v)[kRoutePasses], const uint32_t (&key)[kRoutePasses],
+                                                   int64_t T, int E, int k, bool packed, int32_t *__restrict__ out_idx,
+                                                   float *__restrict__ out_w, uint32_t *lmask, int32_t *lids,
+                                                   int32_t *loffs, int32_t *wave_sums,
+                                                   int32_t *__restrict__ expert_counts,
+                                                   int32_t *__restrict__ expert_offsets)
+{
+    const int tid = threadIdx.x;
+    const int gl = lane_id() % 8;
+    for (int i = tid; i < E * kMaskWords; i += kBlock)
+        lmask[i] = 0u;
+    __syncthreads();
+    const bool store = blockIdx.x == 0;
+#pragma unroll
+    for (int p = 0; p < kRoutePasses; ++p) {
+        if (p * kMaskChunk >= T)   // uniform: T is the same for the whole work-group
+            break;
+        const int64_t tt = p * kMaskChunk + tid / 8;
+        const bool active = tt < T;
+        const float vv[1] = {v[p]};
+        uint32_t kk[1] = {key[p]};
+        const int e = route_core::select_and_store<8, 1>(vv, kk, active, tt, E, k, store ? out_idx : nullptr,
+                                                         store ? out_w : nullptr);
+        if (active && gl < k) {
+            lids[tt * k + gl] = e;
+            atomicOr(&lmask[e * kMaskWords + ((int)tt >> 5)], 1u << ((int)tt & 31));
+        }
+    }
+    __syncthreads();
+    local_totals(E, packed, lmask, loffs, wave_sums, expert_counts, expert_offsets);
 }
 
 // The expert id (and for 256-token chunks the in-chunk rank) of pair
@@ -417,16 +492,18 @@ constexpr int kMaxV = 16;  // most 16-byte vectors per lane in flight (bf16 rows
 // chunk's masks in LDS (two barriers) from ids requested before the rows.
 // Otherwise there is no work-group barrier and the waves' latency chains
 // overlap freely.
-template <int VPL, bool LOCAL>
+template <int VPL, int MODE>
 __global__ __launch_bounds__(kBlock) void dispatch_pack_bf16_kernel(
     const u32x4 *__restrict__ x, int64_t T, int nvec, const int32_t *__restrict__ topk_idx,
     const int32_t *__restrict__ local_rank, const int32_t *__restrict__ chunk_counts,
     const uint32_t *__restrict__ masks, int32_t *offs, int E, int k, int C, int nchunks, int lanes_per_pair,
     int segs,
     int32_t *__restrict__ token_slot, int32_t *__restrict__ recv_src, int32_t *__restrict__ expert_counts,
-    u32x4 *__restrict__ recv_x)
+    u32x4 *__restrict__ recv_x, const float *__restrict__ logits, int32_t *__restrict__ route_idx,
+    float *__restrict__ route_w)
 {
-    extern __shared__ uint32_t lds_words[];  // local counting only: masks, then packed offsets
+    constexpr bool LOCAL = MODE != kPackChunks;
+    extern __shared__ uint32_t lds_words[];  // local counting only: masks, packed offsets, routed ids
     __shared__ int32_t wave_sums[kWavesPerBlock];
     uint32_t *lmask = LOCAL ? lds_words : nullptr;
     int32_t *loffs = LOCAL && offs ? (int32_t *)(lds_words + E * kMaskWords) : nullptr;
@@ -443,10 +520,14 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_bf16_kernel(
     // them ahead was measured slower there).
     PairIds ids = {-1, -1};
     int lids[kLocalIds];
-    if (LOCAL) {
+    float rv[kRoutePasses];
+    uint32_t rkey[kRoutePasses];
+    if (MODE == kPackLocalIds) {
         ids = load_pair_ids(topk_idx, local_rank, active, t, k, lanes_per_pair);
         local_ids_load(topk_idx, (int)T * k, lids);
     }
+    if (MODE == kPackLocalRoute)
+        route_logits_load(logits, T, E, rv, rkey);
     u32x4 buf[VPL];
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
@@ -457,9 +538,16 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_bf16_kernel(
             buf[i] = active && v < nvec ? src[v] : (u32x4){0, 0, 0, 0};
     }
     // (local counting overlaps the row loads; every thread takes part)
-    if (LOCAL)
+    int32_t *lroute = (int32_t *)(lds_words + E * kMaskWords + E + 1);   // routed ids [T][k]
+    if (MODE == kPackLocalIds)
         local_chunk_counts(lids, E, k, offs != nullptr, lds_words, (int32_t *)(lds_words + E * kMaskWords),
                            wave_sums, expert_counts, offs);
+    if (MODE == kPackLocalRoute) {
+        route_local_counts(rv, rkey, T, E, k, offs != nullptr, route_idx, route_w, lds_words, lroute,
+                           (int32_t *)(lds_words + E * kMaskWords), wave_sums, expert_counts, offs);
+        const int j = lane / lanes_per_pair;
+        ids.e = active && j < k ? lroute[t * k + j] : -1;
+    }
     if (!active)
         return;
 
@@ -493,15 +581,17 @@ constexpr int kMaxG = 8;   // most 16-element groups per lane in flight (fp8 row
 // E4M3 encoding (round to nearest even, saturating) of x / scale, with the
 // quotient bit-identical to an IEEE division (divide_all).  The load order
 // and LOCAL are as in the bf16 kernel.
-template <int VPL, bool LOCAL>
+template <int VPL, int MODE>
 __global__ __launch_bounds__(kBlock) void dispatch_pack_fp8_kernel(
     const u32x4 *__restrict__ x, int64_t T, int ngrp, const int32_t *__restrict__ topk_idx,
     const int32_t *__restrict__ local_rank, const int32_t *__restrict__ chunk_counts,
     const uint32_t *__restrict__ masks, int32_t *offs, int E, int k, int C, int nchunks, int lanes_per_pair,
     int segs,
     int32_t *__restrict__ token_slot, int32_t *__restrict__ recv_src, int32_t *__restrict__ expert_counts,
-    u32x4 *__restrict__ recv_x, float *__restrict__ recv_scales)
+    u32x4 *__restrict__ recv_x, float *__restrict__ recv_scales, const float *__restrict__ logits,
+    int32_t *__restrict__ route_idx, float *__restrict__ route_w)
 {
+    constexpr bool LOCAL = MODE != kPackChunks;
     // the wave's block scales, staged so each slot's scale segment is
     // written by one contiguous store instruction
     __shared__ float s_scale[kWavesPerBlock][VPL * 8];
@@ -520,10 +610,14 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_fp8_kernel(
     const int g0 = seg * VPL * kWave + lane;
     PairIds ids = {-1, -1};   // the same load order as the bf16 kernel
     int lids[kLocalIds];
-    if (LOCAL) {
+    float rv[kRoutePasses];
+    uint32_t rkey[kRoutePasses];
+    if (MODE == kPackLocalIds) {
         ids = load_pair_ids(topk_idx, local_rank, active, t, k, lanes_per_pair);
         local_ids_load(topk_idx, (int)T * k, lids);
     }
+    if (MODE == kPackLocalRoute)
+        route_logits_load(logits, T, E, rv, rkey);
     u32x4 lo[VPL], hi[VPL];
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
@@ -541,9 +635,16 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_fp8_kernel(
         }
     }
     // (local counting overlaps the row loads; every thread takes part)
-    if (LOCAL)
+    int32_t *lroute = (int32_t *)(lds_words + E * kMaskWords + E + 1);   // routed ids [T][k]
+    if (MODE == kPackLocalIds)
         local_chunk_counts(lids, E, k, offs != nullptr, lds_words, (int32_t *)(lds_words + E * kMaskWords),
                            wave_sums, expert_counts, offs);
+    if (MODE == kPackLocalRoute) {
+        route_local_counts(rv, rkey, T, E, k, offs != nullptr, route_idx, route_w, lds_words, lroute,
+                           (int32_t *)(lds_words + E * kMaskWords), wave_sums, expert_counts, offs);
+        const int j = lane / lanes_per_pair;
+        ids.e = active && j < k ? lroute[t * k + j] : -1;
+    }
     if (!active)
         return;
 
@@ -649,10 +750,12 @@ bool pack_split(int64_t T, int H, int k, int dtype, int *vpl, int *segs)
 hipError_t launch_pack(const uint16_t *x, int64_t T, int H, const int32_t *topk_idx, const int32_t *local_rank,
                        const int32_t *chunk_counts, const uint32_t *masks, int32_t *offs, int E, int k, int C,
                        int nchunks, int dtype, void *recv_x, float *recv_scales, int32_t *recv_src,
-                       int32_t *expert_counts, int32_t *token_slot, hipStream_t s, bool local = false)
+                       int32_t *expert_counts, int32_t *token_slot, hipStream_t s, int mode = kPackChunks,
+                       const float *logits = nullptr, int32_t *route_idx = nullptr, float *route_w = nullptr)
 {
-    // local: a single chunk whose masks every work-group rebuilds in LDS
-    const size_t lds = local ? (size_t)(E * kMaskWords + (offs ? E + 1 : 0)) * 4 : 0;
+    // single chunk: masks [E][8] and offsets [E+1] in LDS (+ routed ids [T][k])
+    const size_t lds = mode == kPackChunks ? 0
+                     : (size_t)(E * kMaskWords + E + 1 + (mode == kPackLocalRoute ? T * k : 0)) * 4;
     const int lpp = pair_lanes(k);
     int vpl, segs;
     if (!pack_split(T, H, k, dtype, &vpl, &segs))
@@ -660,16 +763,18 @@ hipError_t launch_pack(const uint16_t *x, int64_t T, int H, const int32_t *topk_
     const dim3 grid((unsigned)((T * segs + kWavesPerBlock - 1) / kWavesPerBlock));
     if (dtype == 0) {
         const int nvec = H / 8;
-#define MOE_PACK_BF16_L(V, L)                                                                                      \
-    hipLaunchKernelGGL((dispatch_pack_bf16_kernel<V, L>), grid, dim3(kBlock), lds, s, (const u32x4 *)x, T, nvec,      \
+#define MOE_PACK_BF16_L(V, M)                                                                                      \
+    hipLaunchKernelGGL((dispatch_pack_bf16_kernel<V, M>), grid, dim3(kBlock), lds, s, (const u32x4 *)x, T, nvec,      \
                        topk_idx, local_rank, chunk_counts, masks, offs, E, k, C, nchunks, lpp, segs, token_slot,           \
-                       recv_src, expert_counts, (u32x4 *)recv_x)
+                       recv_src, expert_counts, (u32x4 *)recv_x, logits, route_idx, route_w)
 #define MOE_PACK_BF16(V)                                                                                         \
     do {                                                                                                         \
-        if (local)                                                                                               \
-            MOE_PACK_BF16_L(V, true);                                                                            \
+        if (mode == kPackLocalRoute)                                                                             \
+            MOE_PACK_BF16_L(V, kPackLocalRoute);                                                                 \
+        else if (mode == kPackLocalIds)                                                                          \
+            MOE_PACK_BF16_L(V, kPackLocalIds);                                                                   \
         else                                                                                                     \
-            MOE_PACK_BF16_L(V, false);                                                                           \
+            MOE_PACK_BF16_L(V, kPackChunks);                                                                     \
     } while (0)
         switch (vpl) {
         case 1: MOE_PACK_BF16(1); break;
@@ -682,16 +787,18 @@ hipError_t launch_pack(const uint16_t *x, int64_t T, int H, const int32_t *topk_
 #undef MOE_PACK_BF16_L
     } else {
         const int ngrp = H / 16;
-#define MOE_PACK_FP8_L(V, L)                                                                                       \
-    hipLaunchKernelGGL((dispatch_pack_fp8_kernel<V, L>), grid, dim3(kBlock), lds, s, (const u32x4 *)x, T, ngrp,       \
+#define MOE_PACK_FP8_L(V, M)                                                                                       \
+    hipLaunchKernelGGL((dispatch_pack_fp8_kernel<V, M>), grid, dim3(kBlock), lds, s, (const u32x4 *)x, T, ngrp,       \
                        topk_idx, local_rank, chunk_counts, masks, offs, E, k, C, nchunks, lpp, segs, token_slot,           \
-                       recv_src, expert_counts, (u32x4 *)recv_x, recv_scales)
+                       recv_src, expert_counts, (u32x4 *)recv_x, recv_scales, logits, route_idx, route_w)
 #define MOE_PACK_FP8(V)                                                                                          \
     do {                                                                                                         \
-        if (local)                                                                                               \
-            MOE_PACK_FP8_L(V, true);                                                                             \
+        if (mode == kPackLocalRoute)                                                                             \
+            MOE_PACK_FP8_L(V, kPackLocalRoute);                                                                  \
+        else if (mode == kPackLocalIds)                                                                          \
+            MOE_PACK_FP8_L(V, kPackLocalIds);                                                                    \
         else                                                                                                     \
-            MOE_PACK_FP8_L(V, false);                                                                            \
+            MOE_PACK_FP8_L(V, kPackChunks);                                                                      \
     } while (0)
         switch (vpl) {
         case 1: MOE_PACK_FP8(1); break;
@@ -737,7 +844,7 @@ hipError_t launch_dispatch(const uint16_t *x, int64_t T, int H, const int32_t *t
     const int nchunks = (int)((T + kChunk - 1) / kChunk);
     if (nchunks == 1)   // one chunk: pack counts it itself, no count launch
         return launch_pack(x, T, H, topk_idx, nullptr, nullptr, nullptr, expert_offsets, E, k, C, 1, dtype, recv_x,
-                           recv_scales, recv_src, expert_counts, token_slot, s, true);
+                           recv_scales, recv_src, expert_counts, token_slot, s, kPackLocalIds);
     int32_t *chunk_counts = (int32_t *)workspace;
     int32_t *local_rank =
         (int32_t *)((char *)workspace + ((int64_t)E * nchunks * 4 + 255) / 256 * 256);
@@ -767,16 +874,21 @@ hipError_t launch_route_dispatch(const float *logits, int64_t T, int E, int k, c
     }
     if (!dispatch_grid_fits(T, H, k, dtype))
         return hipErrorInvalidConfiguration;
-    // E <= 8: the router writes 32-token membership words and pack derives
-    // the slots from them (two launches; the packed layout adds one
-    // work-group that totals the words into expert_offsets, so there it is
-    // used only past one 256-token chunk, where the alternative is four
-    // launches).  Otherwise, or when the prefix over those words would
-    // exceed 64 loads per lane: route, count (+ offsets), pack -- or for a
-    // single chunk route and a pack that counts in LDS.
+    // E <= 8 and one 256-token chunk: one launch, every pack work-group
+    // routes the whole batch itself (route_local_counts).
+    // E <= 8 beyond that: the router writes 32-token membership words and
+    // pack derives the slots from them (two launches; the packed layout adds
+    // one work-group that totals the words into expert_offsets).
+    // Otherwise, or when the prefix over those words would exceed 64 loads
+    // per lane: route, count (+ offsets), pack -- or for a single chunk route
+    // and a pack that counts in LDS.
+    if (E <= 8 && T <= kChunk)
+        return launch_pack(x, T, H, nullptr, nullptr, nullptr, nullptr, expert_offsets, E, k, C, 1, dtype, recv_x,
+                           recv_scales, recv_src, expert_offsets ? nullptr : expert_counts, token_slot, s,
+                           kPackLocalRoute, logits, topk_idx, topk_w);
     const int64_t nmask = (T + kMaskChunk - 1) / kMaskChunk;
     const int lpp = pair_lanes(k);
-    if (E <= 8 && nmask <= 64 * (int64_t)lpp && (!expert_offsets || T > kChunk) &&
+    if (E <= 8 && nmask <= 64 * (int64_t)lpp &&
         (size_t)E * nmask * 4 <= dispatch_workspace_bytes(T, E, k)) {
         uint32_t *masks = (uint32_t *)workspace;
         hipError_t e = launch_route_topk_masks(logits, T, E, k, topk_idx, topk_w, masks, s);

@@ -193,8 +193,10 @@ MOE_API int moe_dispatch(const uint16_t *x, int64_t T, int32_t H, const int32_t 
  * the count step is folded into the router's kernel: a work-group that
  * routes 32 tokens also records which of them chose each expert, and the
  * pack derives counts, prefixes and ranks from those words, so the call is
- * two kernel launches instead of three.  Larger E (or more than 64·2048
- * tokens per pair lane group) use the three-step path.
+ * two kernel launches instead of three.  With E <= 8 and at most 256 tokens
+ * it is one launch: every pack work-group routes the whole batch itself with
+ * the router's own code.  Larger E (or more than 64·2048 tokens per pair
+ * lane group) use the three-step path.
  *
  *   logits, T, E, k, topk_idx, topk_w: as for moe_route_topk
  *   x, H, capacity, out_dtype, recv_x, recv_scales, recv_src, expert_counts,
@@ -255,8 +257,8 @@ MOE_API int moe_dispatch_packed(const uint16_t *x, int64_t T, int32_t H, const i
  * E <= 8 and more than 256 tokens the count step is folded into the
  * router's kernel as in moe_route_dispatch, and one work-group totals the
  * router's membership words into expert_offsets: three kernel launches
- * instead of four.  (Up to 256 tokens the two calls are already two
- * launches.)
+ * instead of four.  With E <= 8 and at most 256 tokens it is one launch, as
+ * for moe_route_dispatch.
  *
  *   logits, T, E, k, topk_idx, topk_w: as for moe_route_topk
  *   x, H, out_dtype, recv_x, recv_scales, recv_src, expert_offsets,

@@ -8,7 +8,9 @@ to the separate moe_route_topk + moe_dispatch calls.  Cases: the five
 workloads (E = 8 on the fused path, E = 128 and 256 on the three-step path),
 token counts around the 32-token word and 256-token chunk boundaries, every
 E <= 8 with every k, capacity overflow, fp8 rows, and token counts past the
-fused path's limit.  The same cases for moe_route_dispatch_packed against
+fused path's limit; batches of at most 256 tokens with E <= 8 take a single
+launch in which every pack work-group routes the batch itself.  The same
+cases for moe_route_dispatch_packed against
 the oracle's packed, count-sized layout and moe_route_topk +
 moe_dispatch_packed.
 """
@@ -84,10 +86,11 @@ def test_token_counts(dev, T):
     _check(f"T={T}", logits, x, k, T, False, fused, separate)
 
 
+@pytest.mark.parametrize("T", [777, 200])       # router words + pack; one launch routing in every work-group
 @pytest.mark.parametrize("E", [1, 2, 3, 5, 8])
-def test_every_k(dev, E):
-    rng = np.random.default_rng(100 + E)
-    T, H = 777, 128
+def test_every_k(dev, E, T):
+    rng = np.random.default_rng(100 + E + T)
+    H = 128
     x = W.bits(torch.from_numpy(rng.standard_normal((T, H)).astype(np.float32)).to(torch.bfloat16))
     for k in range(1, E + 1):
         logits = rng.integers(-2, 3, (T, E)).astype(np.float32)     # ties everywhere
@@ -171,10 +174,11 @@ def test_packed_token_counts(dev, T):
     _check_packed(f"T={T}", logits, x, k, False, fused, separate)
 
 
+@pytest.mark.parametrize("T", [777, 200])
 @pytest.mark.parametrize("E", [1, 3, 8])
-def test_packed_every_k(dev, E):
-    rng = np.random.default_rng(200 + E)
-    T, H = 777, 128
+def test_packed_every_k(dev, E, T):
+    rng = np.random.default_rng(200 + E + T)
+    H = 128
     x = W.bits(torch.from_numpy(rng.standard_normal((T, H)).astype(np.float32)).to(torch.bfloat16))
     for k in range(1, E + 1):
         logits = rng.integers(-2, 3, (T, E)).astype(np.float32)     # ties everywhere
