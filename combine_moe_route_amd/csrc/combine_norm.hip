@@ -9,16 +9,17 @@
 // sum is combine's router-weighted sum (pplx blog, Combine), so one kernel
 // replaces combine + add + norm and the token's row makes one trip.
 //
-// One work-group per token: 256 threads, or 1024 when there are too few
-// tokens to fill the chip with 4-wave groups.  Thread i owns the row's
-// 16-byte vectors i, i + BS, ... (NV of them).  In passes of P vectors it requests
-// the k expert rows (non-temporal) and the residual, forms combine's fp32
-// accumulator exactly as combine_kernel does (fma per expert in top-k order
-// from +0, dropped pairs skipped), adds the residual in fp32, stores the
-// updated residual (bf16, nearest even) and keeps the fp32 sums in
-// registers.  The norm is evaluated in double: the squares are summed in
+// One work-group per token: 256 threads (512 for rows of 4097 to 8192
+// elements, so each lane requests its whole share in one pass), or 1024 when
+// there are too few tokens to fill the chip with 4-wave groups.  Thread i
+// owns the row's 16-byte vectors i, i + BS, ... (NV of them).  In passes of
+// P vectors it requests the k expert rows (non-temporal) and the residual,
+// forms combine's fp32 accumulator exactly as combine_kernel does (fma per
+// expert in top-k order from +0, dropped pairs skipped), adds the residual
+// in fp32, stores the updated residual (bf16, nearest even) and keeps the
+// fp32 sums in registers.  The norm is evaluated in double: the squares are summed in
 // double (no fp32 underflow or overflow for any row: r^2 of a float spans
-// 2^-298 .. 2^256), the work-group adds its four wave totals in a fixed
+// 2^-298 .. 2^256), the work-group adds its wave totals in a fixed
 // order, inv = 1 / sqrt(sum / H + eps) (IEEE double division and square
 // root), and every kept value is written as (r * inv) * gamma rounded from
 // double to bf16 in one step.  The only difference from an exact evaluation
@@ -236,8 +237,8 @@ hipError_t launch_k(const uint16_t *y, int64_t nrows, int H, const int32_t *toke
         return MOE_NORM_NV(1, kBlock);
     if (nvec <= 2 * kBlock)
         return MOE_NORM_NV(2, kBlock);
-    if (nvec <= 4 * kBlock)
-        return MOE_NORM_NV(4, kBlock);
+    if (nvec <= 4 * kBlock)     // H <= 8192: 8-wave groups with all loads in one pass beat 4 vectors per lane
+        return MOE_NORM_NV(2, 2 * kBlock);
     return MOE_NORM_NV(8, kBlock);
 #undef MOE_NORM_NV
 }
@@ -263,7 +264,8 @@ hipError_t launch_combine_rmsnorm(const uint16_t *y, int64_t nrows, int H, const
                                   float *normed_scales, hipStream_t s)
 {
     // One work-group per token and at most 2^32 - 1 work-items per launch:
-    // longer batches go in launches of 2^22 tokens (256-thread groups).
+    // longer batches go in launches of 2^22 tokens (groups of at most 512
+    // threads there).
     constexpr int64_t kPiece = int64_t(1) << 22;
     for (int64_t t0 = 0; t0 < T; t0 += kPiece) {
         const int64_t n = T - t0 < kPiece ? T - t0 : kPiece;
