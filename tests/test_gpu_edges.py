@@ -275,6 +275,40 @@ def test_combine_timed_matches_combine(dev):
     assert bf16_ulp_distance(dev_bits(got), want).max() <= 1
 
 
+@pytest.mark.parametrize("T,H,k", [
+    (4096, 2056, 3),    # one work-group per token, 320 threads for a ragged 257-vector row
+    (2048, 8192, 2),    # one work-group per token, 1024 threads
+    (4100, 8, 5),       # one-vector rows: 64-thread groups with 63 idle lanes
+    (16384, 4096, 1),   # 512-vector segments tile the row and there are many waves: segmented launch
+    (100, 7168, 8),     # few tokens: one vector per lane, segmented launch
+])
+def test_combine_launch_shapes_with_dropped_pairs(dev, T, H, k):
+    """Each of combine's launch shapes with dropped pairs mixed in: slot -1,
+    slots at or past E*C (both skipped), and a token whose pairs are all
+    dropped (its output is +0)."""
+    say(f"combine launch shape T={T} H={H} k={k}")
+    rng = np.random.default_rng(T + H + k)
+    R = T * k
+    slot = rng.permutation(R).astype(np.int32).reshape(T, k)
+    drop = rng.random((T, k)) < 0.03
+    past = rng.random((T, k)) < 0.01
+    slot[drop] = -1
+    slot[past] = (R + rng.integers(0, 1 << 30, int(past.sum()))).astype(np.int32)
+    slot[T // 2, :] = -1
+    w = rng.uniform(-1, 1, (T, k)).astype(np.float32)
+    y = torch.randn(1, R, H, device=dev).to(torch.bfloat16)
+    out = torch.empty(T + 1, H, dtype=torch.bfloat16, device=dev)
+    out.view(torch.int16).fill_(SENT_BF16)
+    moe.moe_combine(y, torch.from_numpy(slot).to(dev), torch.from_numpy(w).to(dev), out=out[:T])
+    got = dev_bits(out)
+    kept = np.where((slot >= 0) & (slot < R), slot, -1).astype(np.int32)
+    rows = dev_bits(y.view(R, H))[np.clip(kept, 0, R - 1).reshape(-1)]
+    want = oracle.combine(rows, kept, w)
+    assert bf16_ulp_distance(got[:T], want).max() <= 1
+    assert (got[T // 2] == 0).all()
+    assert (got[T] == SENT_BF16).all(), "combine wrote past its output"
+
+
 def test_combine_rejects_overlapping_output(dev):
     y = torch.zeros(2, 4, 64, dtype=torch.bfloat16, device=dev)
     ts = torch.zeros(4, 1, dtype=torch.int32, device=dev)
