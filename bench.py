@@ -440,7 +440,7 @@ def main() -> int:
         },
         "roofline": {
             "kernel": (f"combine_rmsnorm_kernel (k={w.k}{', fp8 out' if epilogue == 'rmsnorm-fp8' else ''})"
-                       if epilogue else f"combine_kernel<{w.k}>"),
+                       if epilogue else f"moe_combine (k={w.k}); profiles/{w.name}_kernel_trace.md names the kernel"),
             "bound": "hbm",
             "achieved": comb_gbps,
             "peak": HBM_PEAK_GBPS,
