@@ -280,6 +280,7 @@ def test_combine_timed_matches_combine(dev):
     (2048, 8192, 2),    # one work-group per token, 1024 threads
     (4100, 8, 5),       # one-vector rows: 64-thread groups with 63 idle lanes
     (16384, 4096, 1),   # 512-vector segments tile the row and there are many waves: segmented launch
+    (2500, 16392, 2),   # rows past 1024 vectors: segmented launch, last segment one vector long
     (100, 7168, 8),     # few tokens: one vector per lane, segmented launch
 ])
 def test_combine_launch_shapes_with_dropped_pairs(dev, T, H, k):
