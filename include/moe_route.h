@@ -282,10 +282,12 @@ MOE_API int moe_route_dispatch_packed(const float *logits, int64_t T, int32_t E,
  * section 7: the k weighted outputs are added at the token's origin.
  *
  *   y          (device, in)  bf16 [E][C][H] expert outputs, same row layout
- *              as moe_dispatch's recv_x; 16 B aligned
+ *              as moe_dispatch's recv_x; 16 B aligned.  All E*C rows must
+ *              be readable memory (unfilled rows may hold anything): the
+ *              kernel may load row 0 in place of a skipped pair
  *   E, capacity, H   as for moe_dispatch (H multiple of 8)
  *   token_slot (device, in)  int32 [T][k] from moe_dispatch; entries < 0
- *              or >= E*C are skipped
+ *              or >= E*C are skipped (left out of the sum)
  *   topk_w     (device, in)  float [T][k] router weights
  *   T, k       tokens (0..MOE_MAX_TOKENS) and experts per token
  *              (1..MOE_MAX_TOPK)
