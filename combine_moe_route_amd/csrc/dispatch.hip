@@ -33,9 +33,10 @@
 // Packed, count-sized layout (handbook "High-throughput mode": count first,
 // then a receive buffer of exactly the needed size): between count and
 // pack, one work-group sums each expert's chunk counts (or the popcounts of
-// the router's words) and scans them into offsets[E+1] (a single chunk's
-// pack work-groups scan their LDS counts); pack then uses slot = offsets[e]
-// + offset + rank, with no capacity and nothing dropped.
+// the router's words) and scans them into offsets[E+1]; a single chunk's
+// pack work-groups scan their LDS counts, and with at most 2048 router words
+// every pack work-group totals and scans them itself.  Pack then uses slot =
+// offsets[e] + offset + rank, with no capacity and nothing dropped.
 // Slot rows are written with non-temporal stores: each byte is written once
 // per call.
 #include "device_common.hpp"
@@ -303,6 +304,78 @@ constexpr int kRoutePasses = kChunk / kMaskChunk;   // 8 passes of 32 tokens
 constexpr int kPackChunks = 0;
 constexpr int kPackLocalIds = 1;
 constexpr int kPackLocalRoute = 2;
+// Packed layout from router membership words (E <= 8, several chunks): every
+// pack work-group totals the words itself and scans the totals into LDS
+// offsets, in place of a separate one-work-group offsets launch.
+constexpr int kPackMaskOffsets = 3;
+constexpr int kOffWords = 8;   // membership words per thread in that mode: E * words <= 8 * 256
+
+// The membership words [E][nwords] as kOffWords words per thread, requested
+// before the row loads from a clamped index (see local_ids_load); words past
+// the end read as 0.
+__device__ __forceinline__ void mask_words_load(const uint32_t *__restrict__ masks, int n, uint32_t (&w)[kOffWords])
+{
+#pragma unroll
+    for (int q = 0; q < kOffWords; ++q) {
+        const int p = (int)threadIdx.x + q * kBlock;
+        const uint32_t v = masks[p < n ? p : n - 1];
+        w[q] = p < n ? v : 0u;
+    }
+}
+
+// Popcounts of those words, taken right after the row loads are requested
+// and before any branch, so that the compiler waits for the words alone.
+__device__ __forceinline__ void mask_words_count(uint32_t (&w)[kOffWords])
+{
+#pragma unroll
+    for (int q = 0; q < kOffWords; ++q)
+        w[q] = __popc(w[q]);
+}
+
+// Expert totals (the words' popcounts, pc) and their exclusive scan into
+// loffs[0..E] (LDS); work-group 0 also stores them to expert_offsets.  E <= 8.
+// All threads call it.
+__device__ __forceinline__ void mask_offsets(const uint32_t (&pc)[kOffWords], int E, int nwords, int32_t *ltot,
+                                             int32_t *loffs, int32_t *__restrict__ expert_offsets)
+{
+    const int tid = threadIdx.x;
+    if (tid < E)
+        ltot[tid] = 0;
+    int cnt[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        cnt[e] = 0;
+#pragma unroll
+    for (int q = 0; q < kOffWords; ++q) {
+        const int ex = (tid + q * kBlock) / nwords;   // >= E past the end, where the word is 0
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            cnt[e] += ex == e ? (int)pc[q] : 0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        if (e >= E)
+            break;
+        int v = cnt[e];
+        for (int o = kWave / 2; o > 0; o >>= 1)
+            v += __shfl_xor(v, o);
+        if (lane_id() == 0)
+            atomicAdd(&ltot[e], v);
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int run = 0;
+        for (int e = 0; e < E; ++e) {
+            loffs[e] = run;
+            run += ltot[e];
+        }
+        loffs[E] = run;
+    }
+    __syncthreads();
+    if (blockIdx.x == 0 && tid <= E)
+        expert_offsets[tid] = loffs[tid];
+}
 
 __device__ __forceinline__ void route_logits_load(const float *__restrict__ logits, int64_t T, int E,
                                                   float (&v)[kRoutePasses], uint32_t (&key)[kRoutePasses])
@@ -385,8 +458,8 @@ __device__ __forceinline__ PairIds load_pair_ids(const int32_t *__restrict__ top
 // popcount of its own word below the token's bit.
 //
 // With lmask != NULL (a single chunk, masks rebuilt in LDS) the rank comes
-// from the LDS words, there is no earlier chunk, and the packed offsets are
-// loffs (LDS).
+// from the LDS words and there is no earlier chunk.  With loffs != NULL the
+// packed offsets are read from LDS instead of offs.
 template <bool PRE>
 __device__ __forceinline__ int wave_slot(PairIds pre, const int32_t *__restrict__ topk_idx,
                                          const int32_t *__restrict__ local_rank,
@@ -403,7 +476,7 @@ __device__ __forceinline__ int wave_slot(PairIds pre, const int32_t *__restrict_
         e = PRE ? pre.e : topk_idx[t * k + j];
         if ((unsigned)e < (unsigned)E) {
             if (offs)
-                base = lmask ? loffs[e] : offs[e];
+                base = loffs ? loffs[e] : offs[e];
             if (lmask) {
                 const int word = (int)t >> 5;
                 r = __popc(lmask[e * kMaskWords + word] & ((1u << ((int)t & 31)) - 1u));
@@ -502,11 +575,12 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_bf16_kernel(
     u32x4 *__restrict__ recv_x, const float *__restrict__ logits, int32_t *__restrict__ route_idx,
     float *__restrict__ route_w)
 {
-    constexpr bool LOCAL = MODE != kPackChunks;
+    constexpr bool LOCAL = MODE == kPackLocalIds || MODE == kPackLocalRoute;
     extern __shared__ uint32_t lds_words[];  // local counting only: masks, packed offsets, routed ids
     __shared__ int32_t wave_sums[kWavesPerBlock];
     uint32_t *lmask = LOCAL ? lds_words : nullptr;
-    int32_t *loffs = LOCAL && offs ? (int32_t *)(lds_words + E * kMaskWords) : nullptr;
+    int32_t *loffs = LOCAL && offs ? (int32_t *)(lds_words + E * kMaskWords)
+                     : MODE == kPackMaskOffsets ? (int32_t *)(lds_words + E) : nullptr;
     const int lane = lane_id();
     const int64_t task = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
     const int64_t t = task / segs;
@@ -528,15 +602,20 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_bf16_kernel(
     }
     if (MODE == kPackLocalRoute)
         route_logits_load(logits, T, E, rv, rkey);
+    uint32_t mw[kOffWords];
+    if (MODE == kPackMaskOffsets)
+        mask_words_load(masks, E * nchunks, mw);
     u32x4 buf[VPL];
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
         const int v = v0 + i * kWave;
-        if (LOCAL)   // lanes past the row end load its last vector and store nothing
+        if (LOCAL || MODE == kPackMaskOffsets)   // lanes past the row end load its last vector, store nothing
             buf[i] = src[v < nvec ? v : nvec - 1];
         else
             buf[i] = active && v < nvec ? src[v] : (u32x4){0, 0, 0, 0};
     }
+    if (MODE == kPackMaskOffsets)
+        mask_words_count(mw);
     // (local counting overlaps the row loads; every thread takes part)
     int32_t *lroute = (int32_t *)(lds_words + E * kMaskWords + E + 1);   // routed ids [T][k]
     if (MODE == kPackLocalIds)
@@ -548,6 +627,8 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_bf16_kernel(
         const int j = lane / lanes_per_pair;
         ids.e = active && j < k ? lroute[t * k + j] : -1;
     }
+    if (MODE == kPackMaskOffsets)
+        mask_offsets(mw, E, nchunks, (int32_t *)lds_words, loffs, offs);
     if (!active)
         return;
 
@@ -591,7 +672,7 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_fp8_kernel(
     u32x4 *__restrict__ recv_x, float *__restrict__ recv_scales, const float *__restrict__ logits,
     int32_t *__restrict__ route_idx, float *__restrict__ route_w)
 {
-    constexpr bool LOCAL = MODE != kPackChunks;
+    constexpr bool LOCAL = MODE == kPackLocalIds || MODE == kPackLocalRoute;
     // the wave's block scales, staged so each slot's scale segment is
     // written by one contiguous store instruction
     __shared__ float s_scale[kWavesPerBlock][VPL * 8];
@@ -599,7 +680,8 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_fp8_kernel(
     extern __shared__ uint32_t lds_words[];  // local counting only: masks, then packed offsets
     __shared__ int32_t wave_sums[kWavesPerBlock];
     uint32_t *lmask = LOCAL ? lds_words : nullptr;
-    int32_t *loffs = LOCAL && offs ? (int32_t *)(lds_words + E * kMaskWords) : nullptr;
+    int32_t *loffs = LOCAL && offs ? (int32_t *)(lds_words + E * kMaskWords)
+                     : MODE == kPackMaskOffsets ? (int32_t *)(lds_words + E) : nullptr;
     const int lane = lane_id();
     const int64_t task = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
     const int64_t t = task / segs;
@@ -618,11 +700,14 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_fp8_kernel(
     }
     if (MODE == kPackLocalRoute)
         route_logits_load(logits, T, E, rv, rkey);
+    uint32_t mw[kOffWords];
+    if (MODE == kPackMaskOffsets)
+        mask_words_load(masks, E * nchunks, mw);
     u32x4 lo[VPL], hi[VPL];
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
         const int g = g0 + i * kWave;
-        if (LOCAL) {   // lanes past the row end load its last group and store nothing
+        if (LOCAL || MODE == kPackMaskOffsets) {   // lanes past the row end load its last group, store nothing
             const int gc = g < ngrp ? g : ngrp - 1;
             lo[i] = src[2 * gc];
             hi[i] = src[2 * gc + 1];
@@ -634,6 +719,8 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_fp8_kernel(
             }
         }
     }
+    if (MODE == kPackMaskOffsets)
+        mask_words_count(mw);
     // (local counting overlaps the row loads; every thread takes part)
     int32_t *lroute = (int32_t *)(lds_words + E * kMaskWords + E + 1);   // routed ids [T][k]
     if (MODE == kPackLocalIds)
@@ -645,6 +732,8 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_fp8_kernel(
         const int j = lane / lanes_per_pair;
         ids.e = active && j < k ? lroute[t * k + j] : -1;
     }
+    if (MODE == kPackMaskOffsets)
+        mask_offsets(mw, E, nchunks, (int32_t *)lds_words, loffs, offs);
     if (!active)
         return;
 
@@ -753,8 +842,10 @@ hipError_t launch_pack(const uint16_t *x, int64_t T, int H, const int32_t *topk_
                        int32_t *expert_counts, int32_t *token_slot, hipStream_t s, int mode = kPackChunks,
                        const float *logits = nullptr, int32_t *route_idx = nullptr, float *route_w = nullptr)
 {
-    // single chunk: masks [E][8] and offsets [E+1] in LDS (+ routed ids [T][k])
-    const size_t lds = mode == kPackChunks ? 0
+    // single chunk: masks [E][8] and offsets [E+1] in LDS (+ routed ids [T][k]);
+    // totals from membership words: totals [E] and offsets [E+1]
+    const size_t lds = mode == kPackChunks        ? 0
+                     : mode == kPackMaskOffsets ? (size_t)(2 * E + 1) * 4
                      : (size_t)(E * kMaskWords + E + 1 + (mode == kPackLocalRoute ? T * k : 0)) * 4;
     const int lpp = pair_lanes(k);
     int vpl, segs;
@@ -773,6 +864,8 @@ hipError_t launch_pack(const uint16_t *x, int64_t T, int H, const int32_t *topk_
             MOE_PACK_BF16_L(V, kPackLocalRoute);                                                                 \
         else if (mode == kPackLocalIds)                                                                          \
             MOE_PACK_BF16_L(V, kPackLocalIds);                                                                   \
+        else if (mode == kPackMaskOffsets)                                                                       \
+            MOE_PACK_BF16_L(V, kPackMaskOffsets);                                                                \
         else                                                                                                     \
             MOE_PACK_BF16_L(V, kPackChunks);                                                                     \
     } while (0)
@@ -797,6 +890,8 @@ hipError_t launch_pack(const uint16_t *x, int64_t T, int H, const int32_t *topk_
             MOE_PACK_FP8_L(V, kPackLocalRoute);                                                                  \
         else if (mode == kPackLocalIds)                                                                          \
             MOE_PACK_FP8_L(V, kPackLocalIds);                                                                    \
+        else if (mode == kPackMaskOffsets)                                                                       \
+            MOE_PACK_FP8_L(V, kPackMaskOffsets);                                                                 \
         else                                                                                                     \
             MOE_PACK_FP8_L(V, kPackChunks);                                                                      \
     } while (0)
@@ -877,8 +972,9 @@ hipError_t launch_route_dispatch(const float *logits, int64_t T, int E, int k, c
     // E <= 8 and one 256-token chunk: one launch, every pack work-group
     // routes the whole batch itself (route_local_counts).
     // E <= 8 beyond that: the router writes 32-token membership words and
-    // pack derives the slots from them (two launches; the packed layout adds
-    // one work-group that totals the words into expert_offsets).
+    // pack derives the slots from them (two launches; for the packed layout
+    // every pack work-group also totals the words into the offsets, or for
+    // more than 2048 words one added work-group does it first).
     // Otherwise, or when the prefix over those words would exceed 64 loads
     // per lane: route, count (+ offsets), pack -- or for a single chunk route
     // and a pack that counts in LDS.
@@ -894,11 +990,15 @@ hipError_t launch_route_dispatch(const float *logits, int64_t T, int E, int k, c
         hipError_t e = launch_route_topk_masks(logits, T, E, k, topk_idx, topk_w, masks, s);
         if (e != hipSuccess)
             return e;
-        if (expert_offsets)
+        // packed: each pack work-group totals the words itself while they fit
+        // kOffWords per thread, else one work-group does it first
+        const bool own_offsets = expert_offsets && E * nmask <= (int64_t)kOffWords * kBlock;
+        if (expert_offsets && !own_offsets)
             hipLaunchKernelGGL(dispatch_offsets_kernel<true>, dim3(1), dim3(kScanBlock), 0, s,
                                (const int32_t *)masks, E, (int)nmask, expert_offsets);
         return launch_pack(x, T, H, topk_idx, nullptr, nullptr, masks, expert_offsets, E, k, C, (int)nmask, dtype,
-                           recv_x, recv_scales, recv_src, expert_offsets ? nullptr : expert_counts, token_slot, s);
+                           recv_x, recv_scales, recv_src, expert_offsets ? nullptr : expert_counts, token_slot, s,
+                           own_offsets ? kPackMaskOffsets : kPackChunks);
     }
     hipError_t e = launch_route_topk(logits, T, E, k, topk_idx, topk_w, s);
     if (e != hipSuccess)

@@ -175,6 +175,20 @@ def test_packed_token_counts(dev, T):
     _check_packed(f"T={T}", logits, x, k, False, fused, separate)
 
 
+@pytest.mark.parametrize("T,E", [(8192, 8), (8193, 8), (20000, 3), (21856, 3), (4000, 5)])
+def test_packed_router_word_limit(dev, T, E):
+    """E <= 8 past one chunk: each pack work-group totals the router's
+    32-token membership words itself while there are at most 2048 of them
+    (E * ceil(T/32)), else one work-group does it first.  Both sides of the
+    limit, and words of several experts in one thread when E < 8."""
+    rng = np.random.default_rng(T * 10 + E)
+    k, H = 2, 64
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    x = W.bits(torch.from_numpy(rng.standard_normal((T, H)).astype(np.float32)).to(torch.bfloat16))
+    fused, separate = _run_both_packed(dev, logits, x, k, False)
+    _check_packed(f"T={T} E={E}", logits, x, k, False, fused, separate)
+
+
 @pytest.mark.parametrize("T", [777, 200])
 @pytest.mark.parametrize("E", [1, 3, 8])
 def test_packed_every_k(dev, E, T):
