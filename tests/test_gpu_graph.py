@@ -5,15 +5,17 @@ graph-capturable).  No call synchronises, allocates, or records a memset.
 
 Each test captures a step on a side stream, replays the graph several times
 with the program's own eager work and synchronisations in between, and
-checks every replay bit for bit against the eager results of the same calls
-(which the other GPU tests pin to the oracle)."""
+checks every replay bit for bit against the eager results of the same calls;
+the eager results of the prepared calls (the ones bench.py times) are
+checked against the oracle first."""
 import numpy as np
 import pytest
 import torch
 
 import combine_moe_route_amd as moe
+import oracle
 import workloads as W
-from gpu_common import OracleRun, place_rows, require_gpu, say
+from gpu_common import W_RTOL, OracleRun, bf16_ulp_distance, dev_bits, place_rows, require_gpu, say
 
 pytestmark = pytest.mark.gpu
 
@@ -54,6 +56,13 @@ def test_step_graph_replays_match_eager(dev, name, fused):
         step.combine()
     side.synchronize()
     ref = _outputs(bufs, idx, wt, out)
+    # the prepared calls (what bench.py times) against the oracle
+    np.testing.assert_array_equal(idx.cpu().numpy(), o.idx)
+    np.testing.assert_allclose(wt.cpu().numpy(), o.wt, rtol=W_RTOL, atol=0)
+    np.testing.assert_array_equal(bufs.token_slot.cpu().numpy(), o.token_slot)
+    np.testing.assert_array_equal(bufs.expert_counts.cpu().numpy(), o.counts)
+    want = oracle.combine(o.y_pairs, o.token_slot, wt.cpu().numpy())
+    assert bf16_ulp_distance(dev_bits(out), want).max(initial=0) <= 1
 
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=side):
