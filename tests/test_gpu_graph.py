@@ -104,6 +104,18 @@ def test_packed_and_epilogue_graph(dev):
         step.combine()
     side.synchronize()
     ref = _outputs(bufs, idx, wt, out, (bufs.expert_offsets, res_out))
+    # against the oracle: grouped routing, packed slots, combine + residual + RMSNorm
+    idx_o, w_o = oracle.route_topk_grouped(o.logits, w.k, 8, 4)
+    np.testing.assert_array_equal(idx.cpu().numpy(), idx_o)
+    np.testing.assert_allclose(wt.cpu().numpy(), w_o, rtol=W_RTOL, atol=0)
+    offs_o, pslot_o, _ = oracle.assign_packed(idx_o, w.E)
+    np.testing.assert_array_equal(bufs.expert_offsets.cpu().numpy(), offs_o)
+    np.testing.assert_array_equal(bufs.token_slot.cpu().numpy(), pslot_o)
+    y_pairs = dev_bits(y)[pslot_o.reshape(-1)]
+    res_o, normed_o = oracle.combine_residual_rmsnorm(y_pairs, pslot_o, wt.cpu().numpy(), W.bits(x.cpu()),
+                                                      dev_bits(gamma), 1e-6)
+    assert (dev_bits(res_out) == res_o).all()
+    assert (dev_bits(out) == normed_o).all()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=side):
         step.route_and_dispatch()
