@@ -255,10 +255,12 @@ MOE_API int moe_dispatch_packed(const uint16_t *x, int64_t T, int32_t H, const i
  * topk_w, expert_offsets, token_slot, recv_src, recv_x, recv_scales) is
  * identical to calling moe_route_topk and then moe_dispatch_packed.  For
  * E <= 8 and more than 256 tokens the count step is folded into the
- * router's kernel as in moe_route_dispatch, and one work-group totals the
- * router's membership words into expert_offsets: three kernel launches
- * instead of four.  With E <= 8 and at most 256 tokens it is one launch, as
- * for moe_route_dispatch.
+ * router's kernel as in moe_route_dispatch, and the pack kernel's
+ * work-groups total the router's membership words into the offsets
+ * themselves: two kernel launches instead of four (three when there are more
+ * than 2048 such words, E * ceil(T/32), and one work-group totals them
+ * first).  With E <= 8 and at most 256 tokens it is one launch, as for
+ * moe_route_dispatch.
  *
  *   logits, T, E, k, topk_idx, topk_w: as for moe_route_topk
  *   x, H, out_dtype, recv_x, recv_scales, recv_src, expert_offsets,
