@@ -86,22 +86,28 @@ def test_packed_layout_in_place(dev):
 
 
 @pytest.mark.parametrize("T,H,k", [(1, 8, 1), (3, 64, 2), (50, 2048, 3), (37, 2056, 8), (20, 4104, 4),
-                                   (64, 7168, 8), (9, 16384, 16), (17, 8192, 5), (300, 1024, 16), (129, 6144, 2)])
+                                   (64, 7168, 8), (9, 16384, 16), (17, 8192, 5), (300, 1024, 16), (129, 6144, 2),
+                                   # 512 tokens and more: 256-thread groups with 1, 2 and 8 vectors per lane,
+                                   # and 512-thread groups with 2 (rows of 4097 to 8192 elements)
+                                   (600, 1024, 3), (700, 4096, 2), (520, 6152, 8), (513, 8192, 4), (512, 9000, 4)])
 def test_shapes(dev, T, H, k):
     rng = np.random.default_rng(T * 7 + H + k)
     rows = T * k
     slot = rng.permutation(rows).astype(np.int32).reshape(T, k)
     slot[rng.random((T, k)) < 0.15] = -1                       # dropped pairs are skipped
+    past = rng.random((T, k)) < 0.02                           # so are slots at or past E*C
+    slot[past] = rows + rng.integers(0, 1 << 20, int(past.sum()))
     wt = rng.random((T, k)).astype(np.float32)
     y_rows = _bf16(rng.standard_normal((rows, H)))
     y_pairs = np.zeros((rows, H), np.uint16)
-    keep = slot.reshape(-1) >= 0
+    keep = (slot.reshape(-1) >= 0) & (slot.reshape(-1) < rows)
     y_pairs[keep] = y_rows[slot.reshape(-1)[keep]]
     res_bits = _bf16(rng.standard_normal((T, H)) * rng.choice([1e-3, 1.0, 50.0], (T, 1)))
     gamma_bits = _bf16(rng.uniform(0.25, 2.0, H))
     say(f"[combine+norm] T={T} H={H} k={k}")
     res_g, normed_g = _run(dev, to_dev_bf16(y_rows, dev).view(1, rows, H), slot, wt, res_bits, gamma_bits, 1e-6)
-    res_o, normed_o = oracle.combine_residual_rmsnorm(y_pairs, slot, wt, res_bits, gamma_bits, 1e-6)
+    kept = np.where(keep.reshape(T, k), slot, -1).astype(np.int32)
+    res_o, normed_o = oracle.combine_residual_rmsnorm(y_pairs, kept, wt, res_bits, gamma_bits, 1e-6)
     _compare(f"T={T} H={H} k={k}", res_g, normed_g, res_o, normed_o)
 
 
@@ -219,7 +225,7 @@ def test_fp8_output_workloads(dev, name):
 
 
 @pytest.mark.parametrize("T,H,k", [(1, 128, 1), (5, 256, 2), (300, 2048, 8), (513, 1024, 3), (40, 7168, 16),
-                                   (600, 16384, 2), (77, 6144, 5)])
+                                   (600, 16384, 2), (77, 6144, 5), (640, 4096, 2), (520, 6144, 8)])
 def test_fp8_output_shapes(dev, T, H, k):
     rng = np.random.default_rng(T * 5 + H + k)
     rows = T * k
