@@ -118,9 +118,9 @@ def main() -> int:
         jobs += [(f"norm_{n}", m, NORM_TESTS, tmp) for n, m in NORM.items()]
         bad = 0
         with ThreadPoolExecutor(4) as ex:
-            for name, verdict, detail in ex.map(run, jobs):
-                print(f"{name:36s} {verdict:10s} {detail[:100]}", flush=True)
-                bad += verdict != "killed"
+            for name, outcome, detail in ex.map(run, jobs):
+                print(f"{name:36s} {outcome:10s} {detail[:100]}", flush=True)
+                bad += outcome != "killed"
     print(f"{len(jobs) - bad} of {len(jobs)} planted mistakes fail a pin")
     return 1 if bad else 0
 
