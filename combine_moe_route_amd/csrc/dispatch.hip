@@ -24,6 +24,10 @@
 //           records token_slot and recv_src; then the row is stored to
 //           each slot -- bf16 bit copies, or E4M3 codes with per-128 fp32
 //           scales.  The first E waves also write the true totals.
+//   scan:   past 256 chunks that prefix would grow with the batch, so one
+//           work-group per expert first rewrites the expert's chunk counts
+//           as exclusive prefixes (and writes its total); pack then reads
+//           the prefix with one load.
 // A batch of at most 256 tokens is a single chunk: then there is no count
 // launch, and every pack work-group rebuilds the chunk's masks in LDS from
 // ids it requests before the rows.
@@ -140,6 +144,61 @@ __global__ __launch_bounds__(kBlock) void dispatch_zero_counts_kernel(int32_t *_
 {
     for (int e = blockIdx.x * kBlock + threadIdx.x; e < E; e += gridDim.x * kBlock)
         expert_counts[e] = 0;
+}
+
+// Beyond this many 256-token chunks the pack's per-pair prefix (a sum over
+// every earlier chunk) would grow with the batch, so the chunk counts are
+// scanned first.
+constexpr int kScanChunks = 256;
+
+// One work-group per expert e: chunk_counts[e][c] is replaced by the exclusive
+// prefix sum over chunks 0 .. c-1 (in place, in pieces of 1024 chunks) and
+// totals[e] (if given) receives the expert's total.
+__global__ __launch_bounds__(kBlock) void dispatch_chunk_scan_kernel(int32_t *__restrict__ chunk_counts,
+                                                                     int nchunks, int32_t *__restrict__ totals)
+{
+    __shared__ int32_t wave_sums[kWavesPerBlock];
+    const int tid = threadIdx.x;
+    const int lane = lane_id();
+    const int wv = tid / kWave;
+    int32_t *row = chunk_counts + (int64_t)blockIdx.x * nchunks;
+    int run = 0;   // total of the earlier pieces
+    for (int c0 = 0; c0 < nchunks; c0 += 4 * kBlock) {
+        int v[4];
+        int own = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int c = c0 + 4 * tid + u;
+            v[u] = c < nchunks ? row[c] : 0;
+            own += v[u];
+        }
+        int incl = own;
+        for (int o = 1; o < kWave; o <<= 1) {
+            const int up = __shfl_up(incl, o);
+            if (lane >= o)
+                incl += up;
+        }
+        if (lane == kWave - 1)
+            wave_sums[wv] = incl;
+        __syncthreads();
+        int base = run + incl - own;
+        int piece = 0;
+        for (int w = 0; w < kWavesPerBlock; ++w) {
+            base += w < wv ? wave_sums[w] : 0;
+            piece += wave_sums[w];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int c = c0 + 4 * tid + u;
+            if (c < nchunks)
+                row[c] = base;
+            base += v[u];
+        }
+        run += piece;
+        __syncthreads();   // wave_sums is rewritten by the next piece
+    }
+    if (tid == 0 && totals)
+        totals[blockIdx.x] = run;
 }
 
 constexpr int kScanBlock = 1024;                      // >= the largest E
@@ -308,6 +367,9 @@ constexpr int kPackLocalRoute = 2;
 // pack work-group totals the words itself and scans the totals into LDS
 // offsets, in place of a separate one-work-group offsets launch.
 constexpr int kPackMaskOffsets = 3;
+// Several chunks whose counts dispatch_chunk_scan_kernel has already turned
+// into per-expert exclusive prefixes: one load per pair instead of a sum.
+constexpr int kPackScanned = 4;
 constexpr int kOffWords = 8;   // membership words per thread in that mode: E * words <= 8 * 256
 
 // The membership words [E][nwords] as kOffWords words per thread, requested
@@ -457,10 +519,13 @@ __device__ __forceinline__ PairIds load_pair_ids(const int32_t *__restrict__ top
 // sums the popcounts of the expert's earlier words and the rank is the
 // popcount of its own word below the token's bit.
 //
+// SCANNED: chunk_counts already holds each expert's exclusive prefix over
+// chunks, so the prefix is one load.
+//
 // With lmask != NULL (a single chunk, masks rebuilt in LDS) the rank comes
 // from the LDS words and there is no earlier chunk.  With loffs != NULL the
 // packed offsets are read from LDS instead of offs.
-template <bool PRE>
+template <bool PRE, bool SCANNED = false>
 __device__ __forceinline__ int wave_slot(PairIds pre, const int32_t *__restrict__ topk_idx,
                                          const int32_t *__restrict__ local_rank,
                                          const int32_t *__restrict__ chunk_counts, const uint32_t *__restrict__ masks,
@@ -499,16 +564,21 @@ __device__ __forceinline__ int wave_slot(PairIds pre, const int32_t *__restrict_
             } else {
                 r = PRE ? pre.r : local_rank[t * k + j];
                 const int32_t *row = chunk_counts + (int64_t)e * nchunks;
-                for (int b0 = sub; b0 < c; b0 += 8 * lanes_per_pair) {
-                    int part[8];
+                if (SCANNED) {
+                    if (sub == 0)
+                        sum = row[c];   // already the prefix over chunks 0 .. c-1
+                } else {
+                    for (int b0 = sub; b0 < c; b0 += 8 * lanes_per_pair) {
+                        int part[8];
 #pragma unroll
-                    for (int u = 0; u < 8; ++u) {
-                        const int cc = b0 + u * lanes_per_pair;
-                        part[u] = cc < c ? row[cc] : 0;
+                        for (int u = 0; u < 8; ++u) {
+                            const int cc = b0 + u * lanes_per_pair;
+                            part[u] = cc < c ? row[cc] : 0;
+                        }
+#pragma unroll
+                        for (int u = 0; u < 8; ++u)
+                            sum += part[u];
                     }
-#pragma unroll
-                    for (int u = 0; u < 8; ++u)
-                        sum += part[u];
                 }
             }
         }
@@ -632,11 +702,12 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_bf16_kernel(
     if (!active)
         return;
 
-    const int slot = wave_slot<LOCAL>(ids, topk_idx, local_rank, chunk_counts, masks, offs, lmask, loffs, t, E, k, C,
+    const int slot = wave_slot<LOCAL, MODE == kPackScanned>(ids, topk_idx, local_rank, chunk_counts, masks, offs,
+                                                             lmask, loffs, t, E, k, C,
                                       nchunks, lanes_per_pair);
     if (seg == 0)
         record_slot(slot, t, k, lanes_per_pair, token_slot, recv_src);
-    if (task < E && expert_counts && !LOCAL)
+    if (task < E && expert_counts && !LOCAL && MODE != kPackScanned)
         wave_totals(task, T * segs, chunk_counts, masks, E, nchunks, expert_counts);
 
 #pragma unroll 1
@@ -737,11 +808,12 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_fp8_kernel(
     if (!active)
         return;
 
-    const int slot = wave_slot<LOCAL>(ids, topk_idx, local_rank, chunk_counts, masks, offs, lmask, loffs, t, E, k, C,
+    const int slot = wave_slot<LOCAL, MODE == kPackScanned>(ids, topk_idx, local_rank, chunk_counts, masks, offs,
+                                                             lmask, loffs, t, E, k, C,
                                       nchunks, lanes_per_pair);
     if (seg == 0)
         record_slot(slot, t, k, lanes_per_pair, token_slot, recv_src);
-    if (task < E && expert_counts && !LOCAL)
+    if (task < E && expert_counts && !LOCAL && MODE != kPackScanned)
         wave_totals(task, T * segs, chunk_counts, masks, E, nchunks, expert_counts);
 
 #pragma unroll
@@ -844,7 +916,7 @@ hipError_t launch_pack(const uint16_t *x, int64_t T, int H, const int32_t *topk_
 {
     // single chunk: masks [E][8] and offsets [E+1] in LDS (+ routed ids [T][k]);
     // totals from membership words: totals [E] and offsets [E+1]
-    const size_t lds = mode == kPackChunks        ? 0
+    const size_t lds = mode == kPackChunks || mode == kPackScanned ? 0
                      : mode == kPackMaskOffsets ? (size_t)(2 * E + 1) * 4
                      : (size_t)(E * kMaskWords + E + 1 + (mode == kPackLocalRoute ? T * k : 0)) * 4;
     const int lpp = pair_lanes(k);
@@ -866,6 +938,8 @@ hipError_t launch_pack(const uint16_t *x, int64_t T, int H, const int32_t *topk_
             MOE_PACK_BF16_L(V, kPackLocalIds);                                                                   \
         else if (mode == kPackMaskOffsets)                                                                       \
             MOE_PACK_BF16_L(V, kPackMaskOffsets);                                                                \
+        else if (mode == kPackScanned)                                                                           \
+            MOE_PACK_BF16_L(V, kPackScanned);                                                                    \
         else                                                                                                     \
             MOE_PACK_BF16_L(V, kPackChunks);                                                                     \
     } while (0)
@@ -892,6 +966,8 @@ hipError_t launch_pack(const uint16_t *x, int64_t T, int H, const int32_t *topk_
             MOE_PACK_FP8_L(V, kPackLocalIds);                                                                    \
         else if (mode == kPackMaskOffsets)                                                                       \
             MOE_PACK_FP8_L(V, kPackMaskOffsets);                                                                 \
+        else if (mode == kPackScanned)                                                                           \
+            MOE_PACK_FP8_L(V, kPackScanned);                                                                     \
         else                                                                                                     \
             MOE_PACK_FP8_L(V, kPackChunks);                                                                      \
     } while (0)
@@ -951,6 +1027,12 @@ hipError_t launch_dispatch(const uint16_t *x, int64_t T, int H, const int32_t *t
         hipLaunchKernelGGL(dispatch_offsets_kernel<false>, dim3(1), dim3(kScanBlock), 0, s, chunk_counts, E,
                            nchunks, expert_offsets);
     int32_t *offs = expert_offsets;
+    if (nchunks > kScanChunks) {   // prefixes scanned once; the scan also writes the totals
+        hipLaunchKernelGGL(dispatch_chunk_scan_kernel, dim3(E), dim3(kBlock), 0, s, chunk_counts, nchunks,
+                           expert_counts);
+        return launch_pack(x, T, H, topk_idx, local_rank, chunk_counts, nullptr, offs, E, k, C, nchunks, dtype,
+                           recv_x, recv_scales, recv_src, nullptr, token_slot, s, kPackScanned);
+    }
 
     return launch_pack(x, T, H, topk_idx, local_rank, chunk_counts, nullptr, offs, E, k, C, nchunks, dtype, recv_x,
                        recv_scales, recv_src, expert_counts, token_slot, s);

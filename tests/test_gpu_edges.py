@@ -159,6 +159,10 @@ def test_empty_combine_and_route(dev):
     (3000, 2056, 16, 3, 3000, False, "ties"),     # 2, ragged
     (2500, 1024, 64, 4, 2500, False, "normal"),   # 2
     (2300, 1024, 32, 1, 2300, True, "normal"),    # fp8: 2 groups per lane
+    # more than 256 chunks: the chunk counts are scanned into prefixes first
+    (66000, 64, 16, 4, 66000, False, "normal"),
+    (65800, 128, 24, 2, 65800, True, "ties"),
+    (70000, 8, 4, 2, 20000, False, "normal"),     # and capacity overflow on that path
 ])
 def test_shapes(dev, T, H, E, k, C, fp8, kind):
     run_case(dev, T, H, E, k, C, fp8, kind)

@@ -21,7 +21,7 @@ import torch
 import combine_moe_route_amd as moe
 import oracle
 import workloads as W
-from gpu_common import OracleRun, W_RTOL, dev_bits, require_gpu, say, to_dev_bf16
+from gpu_common import OracleRun, W_RTOL, bf16_ulp_distance, dev_bits, require_gpu, say, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -116,6 +116,38 @@ def test_empty(dev):
     i, w, b = moe.moe_route_dispatch(lg, x, 2, 4)
     assert (b.expert_counts.cpu().numpy() == 0).all()
 
+
+
+def test_largest_batch(dev):
+    """MOE_MAX_TOKENS (2^24) tokens through route + dispatch + combine: ids,
+    weights, counts, every slot and every filled source against the oracle;
+    rows and combined sums on a sample.  Past 256 chunks the chunk counts are
+    scanned into prefixes once, so each pair's slot costs one load whatever
+    the batch."""
+    T, E, k, H = 1 << 24, 8, 2, 8
+    C = T // 2                     # about 2^22 tokens per expert: nothing dropped
+    rng = np.random.default_rng(24)
+    logits = rng.standard_normal((T, E), dtype=np.float32)
+    x = W.bits(torch.from_numpy(rng.standard_normal((T, H), dtype=np.float32)).to(torch.bfloat16))
+    say(f"[route+dispatch] largest batch T={T} E={E} k={k} H={H} C={C}")
+    idx, wt, b = moe.moe_route_dispatch(torch.from_numpy(logits).to(dev), to_dev_bf16(x, dev), k, C)
+    idx_o, w_o = oracle.route_topk(logits, k)
+    np.testing.assert_array_equal(idx.cpu().numpy(), idx_o)
+    wt_h = wt.cpu().numpy()
+    np.testing.assert_allclose(wt_h, w_o, rtol=W_RTOL, atol=0)
+    counts_o, slot_o, src_o = oracle.assign_slots(idx_o, E, C)
+    np.testing.assert_array_equal(b.expert_counts.cpu().numpy(), counts_o)
+    np.testing.assert_array_equal(b.token_slot.cpu().numpy(), slot_o)
+    filled = np.nonzero(src_o >= 0)[0]
+    np.testing.assert_array_equal(b.recv_src.cpu().numpy().reshape(-1)[filled], src_o[filled])
+    pick = filled[rng.integers(0, filled.size, 4096)]
+    rows = dev_bits(b.recv_x.view(E * C, H)[torch.from_numpy(pick).to(dev)])
+    np.testing.assert_array_equal(rows, x[src_o[pick]])
+    out = moe.moe_combine(b.recv_x, b.token_slot, wt)    # identity experts
+    tp = np.unique(np.concatenate([np.arange(64), np.arange(T - 64, T), rng.integers(0, T, 4096)]))
+    want = oracle.combine(np.repeat(x[tp], k, axis=0), slot_o[tp], wt_h[tp])
+    got = dev_bits(out[torch.from_numpy(tp).to(dev)])
+    assert bf16_ulp_distance(got, want).max() <= 1
 
 
 # ---- moe_route_dispatch_packed ----
