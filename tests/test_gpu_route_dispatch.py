@@ -150,6 +150,30 @@ def test_largest_batch(dev):
     assert bf16_ulp_distance(got, want).max() <= 1
 
 
+def test_largest_batch_packed(dev):
+    """MOE_MAX_TOKENS tokens into the packed layout: offsets, every slot and
+    source against the oracle; rows and combined sums on a sample."""
+    T, E, k, H = 1 << 24, 8, 2, 8
+    rng = np.random.default_rng(25)
+    logits = rng.standard_normal((T, E), dtype=np.float32)
+    x = W.bits(torch.from_numpy(rng.standard_normal((T, H), dtype=np.float32)).to(torch.bfloat16))
+    say(f"[route+dispatch packed] largest batch T={T} E={E} k={k} H={H}")
+    idx, wt, p = moe.moe_route_dispatch_packed(torch.from_numpy(logits).to(dev), to_dev_bf16(x, dev), k)
+    idx_o, _ = oracle.route_topk(logits, k)
+    np.testing.assert_array_equal(idx.cpu().numpy(), idx_o)
+    offs_o, slot_o, src_o = oracle.assign_packed(idx_o, E)
+    np.testing.assert_array_equal(p.expert_offsets.cpu().numpy(), offs_o)
+    np.testing.assert_array_equal(p.token_slot.cpu().numpy(), slot_o)
+    np.testing.assert_array_equal(p.recv_src.cpu().numpy().reshape(-1)[:T * k], src_o)
+    pick = rng.integers(0, T * k, 4096)
+    rows = dev_bits(p.recv_x[torch.from_numpy(pick).to(dev)])
+    np.testing.assert_array_equal(rows, x[src_o[pick]])
+    out = moe.moe_combine(p.recv_x, p.token_slot, wt)
+    tp = np.unique(np.concatenate([np.arange(64), np.arange(T - 64, T), rng.integers(0, T, 4096)]))
+    want = oracle.combine(np.repeat(x[tp], k, axis=0), slot_o[tp], wt.cpu().numpy()[tp])
+    assert bf16_ulp_distance(dev_bits(out[torch.from_numpy(tp).to(dev)]), want).max() <= 1
+
+
 # ---- moe_route_dispatch_packed ----
 
 def _run_both_packed(dev, logits, x_bits, k, fp8):
