@@ -197,9 +197,11 @@ def _run_fp8(dev, y_dev, slot, w, res_bits, gamma_bits, eps, keep_bf16):
             sch[:T * (H // 128)].reshape(T, H // 128))
 
 
-def _check_fp8(label, dev, y_dev, slot, w, y_pairs, res_bits, gamma_bits, eps):
+def _check_fp8(label, dev, y_dev, slot, w, y_pairs, res_bits, gamma_bits, eps, slot_o=None):
+    """slot_o: the oracle's view of the slots (out-of-range ones as -1), if it differs."""
     res_g, normed_g, q_g, sc_g = _run_fp8(dev, y_dev, slot, w, res_bits, gamma_bits, eps, True)
-    res_o, normed_o = oracle.combine_residual_rmsnorm(y_pairs, slot, w, res_bits, gamma_bits, eps)
+    res_o, normed_o = oracle.combine_residual_rmsnorm(y_pairs, slot if slot_o is None else slot_o, w, res_bits,
+                                                      gamma_bits, eps)
     _compare(label, res_g, normed_g, res_o, normed_o)
     q_o, sc_o = oracle.quantize_rows_fp8(normed_g)
     np.testing.assert_array_equal(q_g, q_o)
@@ -244,6 +246,41 @@ def test_fp8_output_shapes(dev, T, H, k):
     say(f"[combine+norm fp8] T={T} H={H} k={k}")
     _check_fp8(f"fp8 T={T} H={H} k={k}", dev, to_dev_bf16(y_rows, dev), slot, wt, y_pairs, res_bits, gamma_bits,
                1e-6)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_shapes(dev, seed):
+    """Seeded random shapes through both epilogue entry points: T from 1 to
+    3000 (both sides of the 512-token switch), H up to the largest supported
+    (a multiple of 128 for the fp8 output), k from 1 to 16, eps from 0 to
+    1e-2, dropped and out-of-range slots, rows of very different scales."""
+    rng = np.random.default_rng(90_000 + seed)
+    fp8 = bool(seed % 2)
+    T = int(rng.choice([rng.integers(1, 512), rng.integers(512, 3001)]))
+    H = 128 * int(rng.integers(1, 129)) if fp8 else 8 * int(rng.integers(1, 2049))
+    k = int(rng.integers(1, 17))
+    eps = float(rng.choice([0.0, 1e-6, 1e-2]))
+    rows = T * k
+    slot = rng.permutation(rows).astype(np.int32).reshape(T, k)
+    slot[rng.random((T, k)) < rng.uniform(0, 0.3)] = -1
+    past = rng.random((T, k)) < 0.02
+    slot[past] = rows + rng.integers(0, 1 << 20, int(past.sum()))
+    wt = rng.uniform(-1, 1, (T, k)).astype(np.float32)
+    y_rows = _bf16(rng.standard_normal((rows, H)))
+    keep = (slot.reshape(-1) >= 0) & (slot.reshape(-1) < rows)
+    y_pairs = np.zeros((rows, H), np.uint16)
+    y_pairs[keep] = y_rows[slot.reshape(-1)[keep]]
+    kept = np.where(keep.reshape(T, k), slot, -1).astype(np.int32)
+    res_bits = _bf16(rng.standard_normal((T, H)) * rng.choice([1e-20, 1e-3, 1.0, 300.0], (T, 1)))
+    gamma_bits = _bf16(rng.uniform(0.25, 2.0, H))
+    say(f"[combine+norm random] seed={seed} T={T} H={H} k={k} eps={eps} fp8={fp8}")
+    y_dev = to_dev_bf16(y_rows, dev).view(1, rows, H)
+    if fp8:
+        _check_fp8(f"seed {seed}", dev, y_dev, slot, wt, y_pairs, res_bits, gamma_bits, eps, slot_o=kept)
+    else:
+        res_g, normed_g = _run(dev, y_dev, slot, wt, res_bits, gamma_bits, eps)
+        res_o, normed_o = oracle.combine_residual_rmsnorm(y_pairs, kept, wt, res_bits, gamma_bits, eps)
+        _compare(f"seed {seed}", res_g, normed_g, res_o, normed_o)
 
 
 def test_fp8_output_rejects_bad_sizes(dev):
