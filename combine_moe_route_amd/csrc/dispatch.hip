@@ -367,10 +367,10 @@ constexpr int kPackLocalRoute = 2;
 // pack work-group totals the words itself and scans the totals into LDS
 // offsets, in place of a separate one-work-group offsets launch.
 constexpr int kPackMaskOffsets = 3;
+constexpr int kOffWords = 8;   // membership words per thread in that mode: E * words <= 8 * 256
 // Several chunks whose counts dispatch_chunk_scan_kernel has already turned
 // into per-expert exclusive prefixes: one load per pair instead of a sum.
 constexpr int kPackScanned = 4;
-constexpr int kOffWords = 8;   // membership words per thread in that mode: E * words <= 8 * 256
 
 // The membership words [E][nwords] as kOffWords words per thread, requested
 // before the row loads from a clamped index (see local_ids_load); words past
