@@ -30,7 +30,8 @@
 //           the prefix with one load.
 // A batch of at most 256 tokens is a single chunk: then there is no count
 // launch, and every pack work-group rebuilds the chunk's masks in LDS from
-// ids it requests before the rows.
+// ids it requests before the rows.  Up to 512 tokens whose ids fit 16 per
+// thread (and whose masks fit 32 KiB of LDS) are counted the same way.
 // Route + dispatch in one call with E <= 8: the router already wrote one
 // membership word per expert and 32-token chunk, and pack takes prefixes and
 // ranks from their popcounts (no count launch either).
@@ -54,6 +55,14 @@ namespace {
 constexpr int kChunk = 256;          // tokens per count work-group (one mask bit each)
 constexpr int kMaskWords = kChunk / 32;
 constexpr int kMaskChunk = 32;       // tokens per router membership word
+constexpr int kLocalTokens = 2 * kChunk;   // pack counts the batch itself up to this many tokens
+
+// Membership words per expert kept in LDS by the pack modes that count the
+// batch themselves: one 256-token chunk's 8, or ceil(T/32) for larger batches.
+__host__ __device__ constexpr int local_words(int64_t T)
+{
+    return T <= kChunk ? kMaskWords : (int)((T + 31) / 32);
+}
 
 // Exclusive scan of the work-group's n <= 4*256 values in LDS (thread i owns
 // values 4i .. 4i+3): out[i] = sum of in[0 .. i-1] for i < n, out[n] = total.
@@ -277,9 +286,10 @@ __device__ __forceinline__ void store_stream(float *p, float v) { __builtin_nont
 
 // A batch of at most 256 tokens is one chunk: every pack work-group then
 // rebuilds that chunk's membership masks from the ids itself (T*k ids, read
-// from L2), so no count launch is needed.  The ids are requested before the
+// from L2), so no count launch is needed; up to 512 tokens are counted the
+// same way, with ceil(T/32) words per expert (local_words).  The ids are requested before the
 // row loads (local_ids_load): vector loads retire in order, so waiting for
-// ids issued after the rows would wait for the rows too.  lds: [E][8] mask
+// ids issued after the rows would wait for the rows too.  lds: [E][nw] mask
 // words, then for the packed layout [E+1] offsets (the exclusive scan of the
 // popcounts).  Work-group 0 publishes the totals (or offsets).  All threads
 // must call both.
@@ -302,7 +312,7 @@ __device__ __forceinline__ void local_ids_load(const int32_t *__restrict__ topk_
 // The chunk's per-expert totals from its complete LDS masks: work-group 0
 // writes them (fixed slots), or every work-group scans them into loffs and
 // work-group 0 writes the offsets (packed layout).  All threads call it.
-__device__ __forceinline__ void local_totals(int E, bool packed, const uint32_t *lmask, int32_t *loffs,
+__device__ __forceinline__ void local_totals(int E, int nw, bool packed, const uint32_t *lmask, int32_t *loffs,
                                              int32_t *wave_sums, int32_t *__restrict__ expert_counts,
                                              int32_t *__restrict__ expert_offsets)
 {
@@ -310,8 +320,8 @@ __device__ __forceinline__ void local_totals(int E, bool packed, const uint32_t 
     for (int e = tid; e < E; e += kBlock) {
         int n = 0;
 #pragma unroll
-        for (int w = 0; w < kMaskWords; ++w)
-            n += __popc(lmask[e * kMaskWords + w]);
+        for (int w = 0; w < nw; ++w)
+            n += __popc(lmask[e * nw + w]);
         if (packed)
             loffs[e] = n;
         else if (blockIdx.x == 0)
@@ -327,13 +337,13 @@ __device__ __forceinline__ void local_totals(int E, bool packed, const uint32_t 
     }
 }
 
-__device__ __forceinline__ void local_chunk_counts(const int (&ids)[kLocalIds], int E, int k, bool packed,
+__device__ __forceinline__ void local_chunk_counts(const int (&ids)[kLocalIds], int E, int k, int nw, bool packed,
                                                    uint32_t *lmask, int32_t *loffs, int32_t *wave_sums,
                                                    int32_t *__restrict__ expert_counts,
                                                    int32_t *__restrict__ expert_offsets)
 {
     const int tid = threadIdx.x;
-    for (int i = tid; i < E * kMaskWords; i += kBlock)
+    for (int i = tid; i < E * nw; i += kBlock)
         lmask[i] = 0u;
     __syncthreads();
 #pragma unroll
@@ -341,11 +351,11 @@ __device__ __forceinline__ void local_chunk_counts(const int (&ids)[kLocalIds], 
         const int e = ids[q];   // pair p = tid + q*256 of token p / k; -1 past the end
         if ((unsigned)e < (unsigned)E) {
             const int tok = (tid + q * kBlock) / k;
-            atomicOr(&lmask[e * kMaskWords + (tok >> 5)], 1u << (tok & 31));
+            atomicOr(&lmask[e * nw + (tok >> 5)], 1u << (tok & 31));
         }
     }
     __syncthreads();
-    local_totals(E, packed, lmask, loffs, wave_sums, expert_counts, expert_offsets);
+    local_totals(E, nw, packed, lmask, loffs, wave_sums, expert_counts, expert_offsets);
 }
 
 // Route + dispatch of a batch of at most 256 tokens with E <= 8 in one
@@ -483,7 +493,7 @@ __device__ __forceinline__ void route_local_counts(const float (&v)[kRoutePasses
         }
     }
     __syncthreads();
-    local_totals(E, packed, lmask, loffs, wave_sums, expert_counts, expert_offsets);
+    local_totals(E, kMaskWords, packed, lmask, loffs, wave_sums, expert_counts, expert_offsets);
 }
 
 // The expert id (and for 256-token chunks the in-chunk rank) of pair
@@ -530,7 +540,7 @@ __device__ __forceinline__ int wave_slot(PairIds pre, const int32_t *__restrict_
                                          const int32_t *__restrict__ local_rank,
                                          const int32_t *__restrict__ chunk_counts, const uint32_t *__restrict__ masks,
                                          const int32_t *__restrict__ offs, const uint32_t *lmask, const int32_t *loffs,
-                                         int64_t t, int E, int k, int C, int nchunks, int lanes_per_pair)
+                                         int64_t t, int E, int k, int C, int nchunks, int lanes_per_pair, int nw)
 {
     const int lane = lane_id();
     const int j = lane / lanes_per_pair;
@@ -544,9 +554,9 @@ __device__ __forceinline__ int wave_slot(PairIds pre, const int32_t *__restrict_
                 base = loffs ? loffs[e] : offs[e];
             if (lmask) {
                 const int word = (int)t >> 5;
-                r = __popc(lmask[e * kMaskWords + word] & ((1u << ((int)t & 31)) - 1u));
+                r = __popc(lmask[e * nw + word] & ((1u << ((int)t & 31)) - 1u));
                 for (int w = 0; w < word; ++w)
-                    r += __popc(lmask[e * kMaskWords + w]);
+                    r += __popc(lmask[e * nw + w]);
             } else if (masks) {
                 const uint32_t *row = masks + (int64_t)e * nchunks;
                 r = __popc(row[c] & ((1u << (int)(t % kMaskChunk)) - 1u));
@@ -649,7 +659,8 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_bf16_kernel(
     extern __shared__ uint32_t lds_words[];  // local counting only: masks, packed offsets, routed ids
     __shared__ int32_t wave_sums[kWavesPerBlock];
     uint32_t *lmask = LOCAL ? lds_words : nullptr;
-    int32_t *loffs = LOCAL && offs ? (int32_t *)(lds_words + E * kMaskWords)
+    const int nw = local_words(T);   // LDS membership words per expert (local modes)
+    int32_t *loffs = LOCAL && offs ? (int32_t *)(lds_words + E * nw)
                      : MODE == kPackMaskOffsets ? (int32_t *)(lds_words + E) : nullptr;
     const int lane = lane_id();
     const int64_t task = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
@@ -687,13 +698,13 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_bf16_kernel(
     if (MODE == kPackMaskOffsets)
         mask_words_count(mw);
     // (local counting overlaps the row loads; every thread takes part)
-    int32_t *lroute = (int32_t *)(lds_words + E * kMaskWords + E + 1);   // routed ids [T][k]
+    int32_t *lroute = (int32_t *)(lds_words + E * nw + E + 1);   // routed ids [T][k]
     if (MODE == kPackLocalIds)
-        local_chunk_counts(lids, E, k, offs != nullptr, lds_words, (int32_t *)(lds_words + E * kMaskWords),
+        local_chunk_counts(lids, E, k, nw, offs != nullptr, lds_words, (int32_t *)(lds_words + E * nw),
                            wave_sums, expert_counts, offs);
     if (MODE == kPackLocalRoute) {
         route_local_counts(rv, rkey, T, E, k, offs != nullptr, route_idx, route_w, lds_words, lroute,
-                           (int32_t *)(lds_words + E * kMaskWords), wave_sums, expert_counts, offs);
+                           (int32_t *)(lds_words + E * nw), wave_sums, expert_counts, offs);
         const int j = lane / lanes_per_pair;
         ids.e = active && j < k ? lroute[t * k + j] : -1;
     }
@@ -703,8 +714,8 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_bf16_kernel(
         return;
 
     const int slot = wave_slot<LOCAL, MODE == kPackScanned>(ids, topk_idx, local_rank, chunk_counts, masks, offs,
-                                                             lmask, loffs, t, E, k, C,
-                                      nchunks, lanes_per_pair);
+                                                             lmask, loffs, t, E, k, C, nchunks, lanes_per_pair,
+                                                             nw);
     if (seg == 0)
         record_slot(slot, t, k, lanes_per_pair, token_slot, recv_src);
     if (task < E && expert_counts && !LOCAL && MODE != kPackScanned)
@@ -751,7 +762,8 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_fp8_kernel(
     extern __shared__ uint32_t lds_words[];  // local counting only: masks, then packed offsets
     __shared__ int32_t wave_sums[kWavesPerBlock];
     uint32_t *lmask = LOCAL ? lds_words : nullptr;
-    int32_t *loffs = LOCAL && offs ? (int32_t *)(lds_words + E * kMaskWords)
+    const int nw = local_words(T);   // LDS membership words per expert (local modes)
+    int32_t *loffs = LOCAL && offs ? (int32_t *)(lds_words + E * nw)
                      : MODE == kPackMaskOffsets ? (int32_t *)(lds_words + E) : nullptr;
     const int lane = lane_id();
     const int64_t task = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
@@ -793,13 +805,13 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_fp8_kernel(
     if (MODE == kPackMaskOffsets)
         mask_words_count(mw);
     // (local counting overlaps the row loads; every thread takes part)
-    int32_t *lroute = (int32_t *)(lds_words + E * kMaskWords + E + 1);   // routed ids [T][k]
+    int32_t *lroute = (int32_t *)(lds_words + E * nw + E + 1);   // routed ids [T][k]
     if (MODE == kPackLocalIds)
-        local_chunk_counts(lids, E, k, offs != nullptr, lds_words, (int32_t *)(lds_words + E * kMaskWords),
+        local_chunk_counts(lids, E, k, nw, offs != nullptr, lds_words, (int32_t *)(lds_words + E * nw),
                            wave_sums, expert_counts, offs);
     if (MODE == kPackLocalRoute) {
         route_local_counts(rv, rkey, T, E, k, offs != nullptr, route_idx, route_w, lds_words, lroute,
-                           (int32_t *)(lds_words + E * kMaskWords), wave_sums, expert_counts, offs);
+                           (int32_t *)(lds_words + E * nw), wave_sums, expert_counts, offs);
         const int j = lane / lanes_per_pair;
         ids.e = active && j < k ? lroute[t * k + j] : -1;
     }
@@ -809,8 +821,8 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_fp8_kernel(
         return;
 
     const int slot = wave_slot<LOCAL, MODE == kPackScanned>(ids, topk_idx, local_rank, chunk_counts, masks, offs,
-                                                             lmask, loffs, t, E, k, C,
-                                      nchunks, lanes_per_pair);
+                                                             lmask, loffs, t, E, k, C, nchunks, lanes_per_pair,
+                                                             nw);
     if (seg == 0)
         record_slot(slot, t, k, lanes_per_pair, token_slot, recv_src);
     if (task < E && expert_counts && !LOCAL && MODE != kPackScanned)
@@ -918,7 +930,7 @@ hipError_t launch_pack(const uint16_t *x, int64_t T, int H, const int32_t *topk_
     // totals from membership words: totals [E] and offsets [E+1]
     const size_t lds = mode == kPackChunks || mode == kPackScanned ? 0
                      : mode == kPackMaskOffsets ? (size_t)(2 * E + 1) * 4
-                     : (size_t)(E * kMaskWords + E + 1 + (mode == kPackLocalRoute ? T * k : 0)) * 4;
+                     : (size_t)(E * local_words(T) + E + 1 + (mode == kPackLocalRoute ? T * k : 0)) * 4;
     const int lpp = pair_lanes(k);
     int vpl, segs;
     if (!pack_split(T, H, k, dtype, &vpl, &segs))
@@ -1013,7 +1025,9 @@ hipError_t launch_dispatch(const uint16_t *x, int64_t T, int H, const int32_t *t
     if (!dispatch_grid_fits(T, H, k, dtype))   // before anything is enqueued
         return hipErrorInvalidConfiguration;
     const int nchunks = (int)((T + kChunk - 1) / kChunk);
-    if (nchunks == 1)   // one chunk: pack counts it itself, no count launch
+    // up to 512 tokens whose ids fit kLocalIds per thread and whose masks fit
+    // 32 KiB of LDS: pack counts the whole batch itself, no count launch
+    if (T <= kLocalTokens && T * k <= (int64_t)kLocalIds * kBlock && (int64_t)E * local_words(T) <= 8 * 1024)
         return launch_pack(x, T, H, topk_idx, nullptr, nullptr, nullptr, expert_offsets, E, k, C, 1, dtype, recv_x,
                            recv_scales, recv_src, expert_counts, token_slot, s, kPackLocalIds);
     int32_t *chunk_counts = (int32_t *)workspace;

@@ -159,6 +159,14 @@ def test_empty_combine_and_route(dev):
     (3000, 2056, 16, 3, 3000, False, "ties"),     # 2, ragged
     (2500, 1024, 64, 4, 2500, False, "normal"),   # 2
     (2300, 1024, 32, 1, 2300, True, "normal"),    # fp8: 2 groups per lane
+    # 257-512 tokens counted inside pack (ids <= 4096, masks <= 8192 words), and past each limit
+    (300, 7168, 256, 8, 300, True, "normal"),
+    (512, 2048, 64, 8, 512, False, "ties"),
+    (500, 256, 512, 8, 500, False, "normal"),     # 512 experts x 16 words: the largest local mask
+    (400, 128, 1024, 8, 400, False, "zeros"),     # 1024 experts: count launch
+    (512, 64, 32, 16, 512, False, "normal"),      # 8192 ids: count launch
+    (257, 64, 16, 16, 257, False, "normal"),      # 4112 ids: count launch
+    (480, 136, 20, 3, 37, False, "normal"),       # counted inside pack, with capacity overflow
     # more than 256 chunks: the chunk counts are scanned into prefixes first
     (66000, 64, 16, 4, 66000, False, "normal"),
     (65800, 128, 24, 2, 65800, True, "ties"),

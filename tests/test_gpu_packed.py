@@ -107,6 +107,7 @@ def test_workloads_full_size(dev, name):
     (1, 128, 8, 2, False), (1, 128, 8, 2, True), (255, 256, 16, 4, False), (257, 384, 16, 4, True),
     (1000, 64, 1, 1, False), (700, 128, 6, 6, True), (3000, 1024, 128, 8, False), (513, 8, 1024, 16, False),
     (5000, 2048, 256, 8, True), (70000, 64, 8, 2, False), (66000, 128, 16, 3, True),
+    (400, 256, 64, 8, True), (511, 512, 300, 6, False),
 ])
 def test_shapes(dev, T, H, E, k, fp8):
     rng = np.random.default_rng(T + H + E + k + fp8)
