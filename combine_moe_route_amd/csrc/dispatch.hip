@@ -31,7 +31,7 @@
 // A batch of at most 256 tokens is a single chunk: then there is no count
 // launch, and every pack work-group rebuilds the chunk's masks in LDS from
 // ids it requests before the rows.  Up to 512 tokens whose ids fit 16 per
-// thread (and whose masks fit 32 KiB of LDS) are counted the same way.
+// thread (and whose masks are at most 4096 words) are counted the same way.
 // Route + dispatch in one call with E <= 8: the router already wrote one
 // membership word per expert and 32-token chunk, and pack takes prefixes and
 // ranks from their popcounts (no count launch either).
@@ -1025,9 +1025,12 @@ hipError_t launch_dispatch(const uint16_t *x, int64_t T, int H, const int32_t *t
     if (!dispatch_grid_fits(T, H, k, dtype))   // before anything is enqueued
         return hipErrorInvalidConfiguration;
     const int nchunks = (int)((T + kChunk - 1) / kChunk);
-    // up to 512 tokens whose ids fit kLocalIds per thread and whose masks fit
-    // 32 KiB of LDS: pack counts the whole batch itself, no count launch
-    if (T <= kLocalTokens && T * k <= (int64_t)kLocalIds * kBlock && (int64_t)E * local_words(T) <= 8 * 1024)
+    // one chunk, or up to 512 tokens whose ids fit kLocalIds per thread and
+    // whose masks are at most 4096 words: pack counts the whole batch itself,
+    // no count launch (every work-group clears, fills and popcounts the
+    // masks, which past that costs more than the launch it saves)
+    if (T <= kChunk ||
+        (T <= kLocalTokens && T * k <= (int64_t)kLocalIds * kBlock && (int64_t)E * local_words(T) <= 4096))
         return launch_pack(x, T, H, topk_idx, nullptr, nullptr, nullptr, expert_offsets, E, k, C, 1, dtype, recv_x,
                            recv_scales, recv_src, expert_counts, token_slot, s, kPackLocalIds);
     int32_t *chunk_counts = (int32_t *)workspace;

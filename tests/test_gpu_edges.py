@@ -162,7 +162,8 @@ def test_empty_combine_and_route(dev):
     # 257-512 tokens counted inside pack (ids <= 4096, masks <= 8192 words), and past each limit
     (300, 7168, 256, 8, 300, True, "normal"),
     (512, 2048, 64, 8, 512, False, "ties"),
-    (500, 256, 512, 8, 500, False, "normal"),     # 512 experts x 16 words: the largest local mask
+    (500, 256, 256, 8, 500, False, "normal"),     # 256 experts x 16 words: the largest local mask
+    (500, 256, 512, 8, 500, False, "normal"),     # 512 experts x 16 words: count launch
     (400, 128, 1024, 8, 400, False, "zeros"),     # 1024 experts: count launch
     (512, 64, 32, 16, 512, False, "normal"),      # 8192 ids: count launch
     (257, 64, 16, 16, 257, False, "normal"),      # 4112 ids: count launch
