@@ -9,18 +9,27 @@ stream, over one batch of seeded synthetic input already resident in HBM.
 With plain top-k the first two are the single call moe_route_dispatch (or
 moe_route_dispatch_packed; identical outputs; --separate-route calls them
 apart).
-W untimed warm-up steps, then exactly K timed steps between device
-synchronisations.  Prints one JSON line (stdout):
 
-  value     tokens/s of the whole job (one GPU)
+The headline workload is the largest that fits one GPU: GLM-style prefill
+(32768 tokens, hidden 6144, 128 experts, top-8, fp8 dispatch).  W untimed
+warm-up steps, then exactly K timed steps between device synchronisations,
+with nothing else in the stream: no timing events inside the timed region.
+Prints one JSON line (stdout):
+
+  value     tokens/s of the whole job (one GPU), from the host clock around
+            the K timed steps
   config    the workload plus effective HBM GB/s and fraction of the 8 TB/s
             peak, from the algorithmic byte model (each row read once and
-            written k times, unfilled slots not counted)
+            written k times, unfilled slots not counted); per-call kernel
+            times from a separate timing pass; the copy floors (--floor);
+            and, by default, the Mixtral-like and DeepSeek-R1-like prefill
+            workloads measured the same way (other_workloads)
   roofline  the dominant kernel (combine): algorithmic bytes per launch over
-            its mean launch time from HIP events recorded around each launch
-            in the timed region, against the 8 TB/s HBM peak
-  cpu_baseline  the CPU oracle (single-threaded, plain C) on a bounded
-            sample of the same workload
+            its mean launch time, from HIP events recorded on the launch
+            stream around every combine call of the timing pass
+  cpu_baseline  the CPU oracle on a bounded sample of the same workload, on
+            the host's cores (threads over tokens for route, pack and
+            combine; slot assignment serial) and on one thread
 
 Consecutive steps cycle through several copies of every buffer (inputs,
 outputs and the fixed-slot buffers) so that each step's data was last touched
@@ -33,6 +42,7 @@ import argparse
 import json
 import math
 import os
+import subprocess
 import sys
 import time
 
@@ -45,7 +55,10 @@ import workloads as W  # noqa: E402
 METRIC = "dispatch+combine tokens/s and effective HBM GB/s (% of peak), 1 MI355X"
 EPILOGUE_LABEL = {None: "", "rmsnorm": "+residual+rmsnorm", "rmsnorm-fp8": "+residual+rmsnorm+fp8"}
 HBM_PEAK_GBPS = 8000.0
-LLC_BYTES = 256 * 2 ** 20
+DEFAULT_WORKLOAD = "glm_prefill"
+SECONDARY = ["mixtral_prefill", "dsr1_prefill"]
+FLOOR_SRC = os.path.join(ROOT, "bench_floor.hip")
+FLOOR_LIB = os.path.join(ROOT, "bench_floor.so")
 
 
 def algorithmic_bytes(w: W.Workload, epilogue: str | None = None) -> dict:
@@ -108,43 +121,142 @@ def host_cpu() -> str:
     return "unknown"
 
 
+def host_threads() -> int:
+    """Threads for the host-cores baseline: the cores this process may run
+    on, at most 16 (a one-GPU share of the machine's host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _balanced_expert_ranges(filled, parts: int):
+    """Split experts into at most `parts` consecutive ranges with about the
+    same number of filled rows each; returns (e0, e1, first row) triples."""
+    total = int(sum(filled))
+    out, e0, row0, acc = [], 0, 0, 0
+    for e, n in enumerate(filled):
+        acc += int(n)
+        if acc * parts >= total * (len(out) + 1) and len(out) < parts - 1:
+            out.append((e0, e + 1, row0))
+            e0, row0 = e + 1, acc
+    out.append((e0, len(filled), row0))
+    return [r for r in out if r[1] > r[0]]
+
+
 def cpu_baseline(w: W.Workload, seconds: float, epilogue: str | None = None) -> dict:
-    """Time the CPU oracle (route, slots, pack, combine -- with the residual
-    + RMSNorm epilogue, and its fp8 encoding, if `epilogue` says so) on the
-    first min(T, 2048) tokens of the workload, repeated for ~`seconds`."""
+    """Time the CPU oracle, unchanged, on the first min(T, 2048) tokens of
+    the workload: route, slots, pack, combine (with the residual + RMSNorm
+    epilogue and its fp8 encoding if `epilogue` says so), repeated for about
+    `seconds` per leg.  The host-cores leg runs the oracle's own functions on
+    disjoint token ranges (route, combine) and expert ranges (pack) in
+    threads; slot assignment stays one serial call.  The one-thread leg runs
+    each function once over the whole sample."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
     import oracle
 
     ts = min(w.T, 2048)
     ws = w.with_(T=ts, C=min(w.C, ts))
-    logits = W.make_logits(w)[:ts].numpy()
-    x = W.bits(W.make_x(w)[:ts])
-    y_pairs = W.bits(W.make_y_pairs(w, rows=ts * w.k))
+    logits = np.ascontiguousarray(W.make_logits(w)[:ts].numpy())
+    x = np.ascontiguousarray(W.bits(W.make_x(w)[:ts]))
+    y_pairs = np.ascontiguousarray(W.bits(W.make_y_pairs(w, rows=ts * w.k)))
     residual = x                     # any bf16 rows of the right shape
-    gamma = x[0]
-    passes, t0 = 0, time.perf_counter()
-    while True:
+    gamma = np.ascontiguousarray(x[0])
+    dtype = oracle.FP8_E4M3 if w.fp8 else oracle.BF16
+
+    def one_thread():
         idx, wt = oracle.route_topk(logits, ws.k)
         counts, token_slot, recv_src = oracle.assign_slots(idx, ws.E, ws.C)
-        oracle.pack(x, oracle.FP8_E4M3 if w.fp8 else oracle.BF16, recv_src, counts, ws.C)
+        oracle.pack(x, dtype, recv_src, counts, ws.C)
         if epilogue:
             _, normed = oracle.combine_residual_rmsnorm(y_pairs, token_slot, wt, residual, gamma, 1e-6)
             if epilogue == "rmsnorm-fp8":
                 oracle.quantize_rows_fp8(normed)
         else:
             oracle.combine(y_pairs, token_slot, wt)
-        passes += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    tok_s = passes * ts / el
+
+    nthr = host_threads()
+    pool = ThreadPoolExecutor(nthr)
+    bounds = [(ts * i // nthr, ts * (i + 1) // nthr) for i in range(nthr)]
+
+    def threaded():
+        idx = np.empty((ts, ws.k), np.int32)
+        wt = np.empty((ts, ws.k), np.float32)
+        list(pool.map(lambda b: oracle.route_topk_range(logits, ws.k, idx, wt, *b), bounds))
+        counts, token_slot, recv_src = oracle.assign_slots(idx, ws.E, ws.C)
+        filled = np.minimum(counts, ws.C)
+        R = int(filled.sum())
+        rows = np.empty((R, ws.H), np.uint16 if dtype == oracle.BF16 else np.uint8)
+        scales = None if dtype == oracle.BF16 else np.empty((R, ws.H // 128), np.float32)
+        slot_of_row = np.empty(R, np.int32)
+        ranges = _balanced_expert_ranges(filled, nthr)
+        list(pool.map(lambda r: oracle.pack_range(x, dtype, recv_src, counts, ws.C, rows, scales, slot_of_row,
+                                                  *r), ranges))
+        if epilogue:
+            res_out = np.empty((ts, ws.H), np.uint16)
+            normed = np.empty((ts, ws.H), np.uint16)
+            list(pool.map(lambda b: oracle.combine_residual_rmsnorm_range(
+                y_pairs, token_slot, wt, residual, gamma, 1e-6, res_out, normed, *b), bounds))
+            if epilogue == "rmsnorm-fp8":
+                q = np.empty((ts, ws.H), np.uint8)
+                sc = np.empty((ts, ws.H // 128), np.float32)
+                list(pool.map(lambda b: oracle.quantize_rows_fp8_range(normed, q, sc, *b), bounds))
+        else:
+            out = np.empty((ts, ws.H), np.uint16)
+            list(pool.map(lambda b: oracle.combine_range(y_pairs, token_slot, wt, out, *b), bounds))
+
+    def timed(fn):
+        passes, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            passes += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                return passes, el
+
+    p1, e1 = timed(one_thread)
+    pn, en = timed(threaded)
+    pool.shutdown()
+    nbytes = algorithmic_bytes(ws, epilogue)["total"]
+    what = f"route+slots+pack+combine{EPILOGUE_LABEL[epilogue]} over the first {ts} of {w.T} tokens ({w.name})"
     return {
-        "value": tok_s, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-        "sample": f"{passes} passes of route+slots+pack+combine{EPILOGUE_LABEL[epilogue]} over the "
-                  f"first {ts} of {w.T} tokens ({w.name}), {el:.1f} s",
-        "gbps": algorithmic_bytes(ws, epilogue)["total"] * passes / el / 1e9,
-        "host": f"{host_cpu()}, {os.cpu_count()} threads visible",
+        "value": pn * ts / en, "unit": "tokens/s", "cores": nthr, "kind": "oracle",
+        "sample": f"{pn} passes of {what} in {en:.1f} s on {nthr} threads (tokens and experts split over threads, "
+                  f"slot assignment serial)",
+        "gbps": nbytes * pn / en / 1e9,
+        "single_thread": {"value": p1 * ts / e1, "unit": "tokens/s", "cores": 1, "gbps": nbytes * p1 / e1 / 1e9,
+                          "sample": f"{p1} passes of {what} in {e1:.1f} s on one thread"},
+        "host": f"{host_cpu()}, {os.cpu_count()} threads visible, {nthr} used",
     }
+
+
+def floor_lib():
+    """The copy-floor kernels (bench_floor.hip), built next to this file on
+    first use."""
+    import ctypes
+    if not os.path.exists(FLOOR_LIB):
+        build_floor()
+    lib = ctypes.CDLL(FLOOR_LIB)
+    P, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.floor_scatter_rows.argtypes = [P, i64, i32, i32, P, i32, P, P, P]
+    lib.floor_scatter_rows.restype = ctypes.c_int
+    lib.floor_gather_rows.argtypes = [P, i64, i32, P, P, i64, i32, P, P]
+    lib.floor_gather_rows.restype = ctypes.c_int
+    return lib
+
+
+def build_floor() -> str:
+    """Compile bench_floor.hip for gfx950 into bench_floor.so."""
+    hipcc = "hipcc" if subprocess.run(["which", "hipcc"], capture_output=True).returncode == 0 else "/opt/rocm/bin/hipcc"
+    tmp = FLOOR_LIB + ".tmp%d" % os.getpid()
+    subprocess.run([hipcc, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-fvisibility=hidden",
+                    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", FLOOR_SRC, "-o", tmp],
+                   check=True, capture_output=True)
+    os.replace(tmp, FLOOR_LIB)
+    return FLOOR_LIB
 
 
 class BufferSet:
@@ -153,6 +265,7 @@ class BufferSet:
     def __init__(self, w: W.Workload, logits_cpu, x_cpu, dev, moe, torch, route_groups=None, packed=False,
                  epilogue=None, fuse_route=True):
         self.fuse_route = fuse_route
+        self.packed = packed
         self.logits = logits_cpu.to(dev)
         self.x = x_cpu.to(dev)
         self.idx = torch.empty(w.T, w.k, dtype=torch.int32, device=dev)
@@ -188,25 +301,253 @@ class BufferSet:
         self.y.view(-1, w.H).index_copy_(0, slots, rows.to(torch.bfloat16))
 
 
+def _stats_us(v_ms):
+    v = sorted(x * 1e3 for x in v_ms)
+    return {"mean_us": sum(v) / len(v), "median_us": v[len(v) // 2], "min_us": v[0], "max_us": v[-1],
+            "launches": len(v)}
+
+
+def run_workload(w: W.Workload, args, moe, torch, dev, primary: bool) -> dict:
+    """Headline timing, kernel timing pass, copy floors (and for the primary
+    workload the graph-replay and two-stream extras) of one workload."""
+    epilogue = None if args.epilogue == "none" else args.epilogue
+    nbytes = algorithmic_bytes(w, epilogue)
+    K = args.steps if args.steps > 0 else (200 if w.T <= 4096 else 50)
+    Wm = args.warmup
+    R = args.rotate or max(1, min(32, math.ceil(2 * 2 ** 30 / nbytes["total"])))
+    S = max(1, args.streams) if primary else 1
+    if R % S:
+        R += S - R % S
+
+    logits_cpu = W.make_logits(w)
+    x_cpu = W.make_x(w)
+    route_groups = tuple(int(v) for v in args.route_groups.split(":")) if args.route_groups else None
+    packed = args.layout == "packed"
+    fuse_route = not args.separate_route and route_groups is None
+    sets = [BufferSet(w, logits_cpu, x_cpu, dev, moe, torch, route_groups, packed, epilogue, fuse_route)
+            for _ in range(R)]
+    del logits_cpu, x_cpu
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed * 16 + 3)
+    for s in sets:
+        s.step.route_and_dispatch()
+        s.fill_expert_outputs(w, torch, gen)
+    torch.cuda.synchronize()
+
+    main = torch.cuda.current_stream()
+    streams = [main] + [torch.cuda.Stream() for _ in range(max(S, 2) - 1)]
+    hip_events = moe.HipEvents()
+
+    def bind(nstreams):
+        """Bind buffer set i to stream i % nstreams (a set never changes stream
+        while steps are queued)."""
+        torch.cuda.synchronize()
+        for si, st in enumerate(sets):
+            st.step = st.prepare(w, moe, stream=streams[si % nstreams])
+
+    def run_steps(first, n, nstreams):
+        for i in range(n):
+            st = sets[(first + i) % R].step
+            st.route_and_dispatch()
+            st.combine()
+
+    def timed(first, n, nstreams):
+        torch.cuda.synchronize()
+        for strm in streams[1:nstreams]:
+            strm.wait_stream(main)
+        t0 = time.perf_counter()
+        run_steps(first, n, nstreams)
+        for strm in streams[1:nstreams]:
+            main.wait_stream(strm)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / n
+
+    # headline: K steps with nothing but the steps in the stream(s)
+    bind(S)
+    run_steps(0, Wm, S)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(main)
+    ms = timed(Wm, K, S)
+    e1.record(main)
+    torch.cuda.synchronize()
+    event_ms = e0.elapsed_time(e1) / K     # includes the trailing sync gap; reported only
+    gbps = nbytes["total"] / (ms * 1e-3) / 1e9
+
+    # kernel timing pass (after the headline region, one stream): HIP events
+    # recorded on the launch stream around every call.  Where moe_route_dispatch
+    # launches the same kernels as moe_route_topk + moe_dispatch (E > 8, or
+    # grouped routing), the two calls are made and timed separately.
+    bind(1)
+    split = w.E > 8 or route_groups is not None or args.separate_route
+    n = min(K, 200)
+    marks = [tuple(hip_events.create() for _ in range(4)) for _ in range(n)]
+    torch.cuda.synchronize()
+    for i, (a, b, c, d) in enumerate(marks):
+        st = sets[(Wm + K + i) % R].step
+        hip_events.record(a, main)
+        if split:
+            st.route()
+            hip_events.record(b, main)
+            st.dispatch()
+        else:
+            st.route_and_dispatch()
+        hip_events.record(c, main)
+        st.combine()
+        hip_events.record(d, main)
+    torch.cuda.synchronize()
+    comb = [hip_events.elapsed_ms(c, d) for _, _, c, d in marks]
+    kernels = {}
+    if split:
+        route = [hip_events.elapsed_ms(a, b) for a, b, _, _ in marks]
+        disp = [hip_events.elapsed_ms(b, c) for _, b, c, _ in marks]
+        kernels["route"] = {"call": "moe_route_topk" + ("_grouped" if route_groups else ""),
+                            "bytes": nbytes["route"], **_stats_us(route)}
+        kernels["dispatch"] = {"call": "moe_dispatch" + ("_packed" if packed else "") + " (count + pack launches)",
+                               "bytes": nbytes["count_scan_slot"] + nbytes["pack"], **_stats_us(disp)}
+    else:
+        rd = [hip_events.elapsed_ms(a, c) for a, _, c, _ in marks]
+        kernels["route_dispatch"] = {"call": "moe_route_dispatch" + ("_packed" if packed else ""),
+                                     "bytes": nbytes["route"] + nbytes["count_scan_slot"] + nbytes["pack"],
+                                     **_stats_us(rd)}
+    kernels["combine"] = {"call": {None: "moe_combine", "rmsnorm": "moe_combine_residual_rmsnorm",
+                                   "rmsnorm-fp8": "moe_combine_residual_rmsnorm_fp8"}[epilogue],
+                          "bytes": nbytes["combine"], **_stats_us(comb)}
+    for kv in kernels.values():
+        kv["gbps"] = kv["bytes"] / (kv["mean_us"] * 1e-6) / 1e9
+        kv["frac"] = kv["gbps"] / HBM_PEAK_GBPS
+    for trio in marks:
+        for e in trio:
+            hip_events.destroy(e)
+
+    # copy floors: plain kernels moving pack's and combine's exact bytes
+    floor = None
+    if not args.no_floor and not epilogue:
+        lib = floor_lib()
+        fl_events = [tuple(hip_events.create() for _ in range(4)) for _ in range(n)]
+        s0 = main.cuda_stream
+
+        def floor_pair(st, ev=None):
+            bf = st.bufs
+            if ev:
+                hip_events.record(ev[0], main)
+            rc = lib.floor_scatter_rows(st.x.data_ptr(), w.T, w.H, int(w.fp8), bf.token_slot.data_ptr(), w.k,
+                                        bf.recv_x.data_ptr(), bf.recv_scales.data_ptr() if w.fp8 else None, s0)
+            if ev:
+                hip_events.record(ev[1], main)
+                hip_events.record(ev[2], main)
+            rc |= lib.floor_gather_rows(st.y.data_ptr(), st.y.numel() // w.H, w.H, bf.token_slot.data_ptr(),
+                                        st.wt.data_ptr(), w.T, w.k, st.out.data_ptr(), s0)
+            if ev:
+                hip_events.record(ev[3], main)
+            if rc:
+                raise RuntimeError(f"copy-floor launch failed ({rc})")
+
+        floor_pair(sets[0])          # untimed: the first launch also loads the kernels' code
+        torch.cuda.synchronize()
+        for i, ev in enumerate(fl_events):
+            floor_pair(sets[(Wm + K + n + i) % R], ev)
+        torch.cuda.synchronize()
+        sc = _stats_us([hip_events.elapsed_ms(a, b) for a, b, _, _ in fl_events])
+        ga = _stats_us([hip_events.elapsed_ms(c, d) for _, _, c, d in fl_events])
+        for e4 in fl_events:
+            for e in e4:
+                hip_events.destroy(e)
+        pack_bytes = nbytes["pack"]
+        floor = {
+            "pack_shaped_copy": {"kernel": "floor_scatter_rows (bench_floor.hip)", "bytes": pack_bytes, **sc,
+                                 "gbps": pack_bytes / (sc["mean_us"] * 1e-6) / 1e9},
+            "combine_shaped_copy": {"kernel": "floor_gather_rows (bench_floor.hip)", "bytes": nbytes["combine"],
+                                    **ga, "gbps": nbytes["combine"] / (ga["mean_us"] * 1e-6) / 1e9},
+            "note": "plain copies of the same rows at the same addresses (no slot work, no quantisation, no "
+                    "arithmetic); their bytes are pack's and combine's algorithmic bytes",
+        }
+        for v in floor.values():
+            if isinstance(v, dict):
+                v["frac"] = v["gbps"] / HBM_PEAK_GBPS
+
+    res = {
+        "workload": w.name, "tokens": w.T, "hidden": w.H, "experts": w.E, "top_k": w.k, "capacity": w.C,
+        "row_dtype": "fp8-e4m3+fp32/128" if w.fp8 else "bf16", "routing": w.routing,
+        "steps": K, "warmup": Wm, "ms_per_step": ms, "tokens_per_s": w.T / (ms * 1e-3),
+        "algorithmic_bytes_per_step": nbytes["total"], "effective_hbm_gbps": gbps, "hbm_frac": gbps / HBM_PEAK_GBPS,
+        "buffer_copies_cycled": R, "streams": S, "ms_per_step_events": event_ms,
+        "kernels": kernels, "floor": floor,
+    }
+
+    if primary:
+        # the same steps replayed from HIP graphs (one captured step per buffer
+        # set): no host launch cost, so small batches show their GPU time
+        if not args.no_graph and S == 1:
+            cap = torch.cuda.Stream()
+            torch.cuda.synchronize()
+            for st in sets:
+                st.step = st.prepare(w, moe, stream=cap)
+            graphs = []
+            for st in sets:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cap):
+                    st.step.route_and_dispatch()
+                    st.step.combine()
+                graphs.append(g)
+            for i in range(Wm):
+                graphs[i % R].replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(K):
+                graphs[(Wm + i) % R].replay()
+            torch.cuda.synchronize()
+            g_ms = (time.perf_counter() - t0) * 1e3 / K
+            res["graph_replay"] = {"ms_per_step": g_ms, "tokens_per_s": w.T / (g_ms * 1e-3),
+                                   "hbm_frac": nbytes["total"] / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+            del graphs
+        # two independent batches in flight (steps alternate over two streams)
+        if not args.no_overlap and S == 1 and R >= 2:
+            bind(2)
+            run_steps(0, Wm, 2)
+            ov_ms = timed(Wm, K, 2)
+            res["two_batches_in_flight"] = {"streams": 2, "ms_per_step": ov_ms, "tokens_per_s": w.T / (ov_ms * 1e-3),
+                                            "hbm_frac": nbytes["total"] / (ov_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+        res.update({
+            "route_groups": ({"groups": route_groups[0], "kept": route_groups[1]} if route_groups else None),
+            "layout": "packed count-sized rows" if packed else "fixed slots per expert",
+            "route_dispatch_call": (("moe_route_dispatch_packed" if packed else "moe_route_dispatch") if fuse_route
+                                    else "separate"),
+            "combine_epilogue": {None: None, "rmsnorm": "residual add + RMSNorm (fused)",
+                                 "rmsnorm-fp8": "residual add + RMSNorm, output as E4M3 + fp32/128 (fused)"}[epilogue],
+        })
+        res["_traffic"] = None if (packed or epilogue) else measured_traffic(w)
+
+    del sets
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=0,
                     help="timed steps (default 200 for batches of at most 4096 tokens, else 50)")
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="mixtral_prefill", choices=W.ORDER)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=W.ORDER)
+    ap.add_argument("--also", default="auto",
+                    help="comma-separated workloads measured after the headline one and reported in "
+                         "config.other_workloads; 'auto' = the other prefill workloads when the headline is the "
+                         "default one; 'none' = no others")
     ap.add_argument("--rotate", type=int, default=0,
                     help="buffer copies cycled through (0: enough that 2 GiB of step traffic separates reuses)")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=8.0, help="seconds per CPU baseline leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--streams", type=int, default=1,
                     help="HIP streams the timed steps alternate over (2: two independent batches in flight)")
-    ap.add_argument("--timing", choices=["ext", "marker"], default="ext",
-                    help="combine launch timing: events attached to the launch (ext) or recorded around it")
     ap.add_argument("--no-overlap", action="store_true",
                     help="skip the extra two-batches-in-flight measurement")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the extra HIP-graph-replay measurement")
+    ap.add_argument("--no-floor", action="store_true",
+                    help="skip the copy floors (plain copies of pack's and combine's bytes)")
     ap.add_argument("--layout", choices=["fixed", "packed"], default="fixed",
                     help="dispatch layout: fixed slots per expert (moe_dispatch) or packed count-sized rows "
                          "(moe_dispatch_packed)")
@@ -237,163 +578,23 @@ def main() -> int:
     moe.load()
     dev = torch.device("cuda:0")
     w = W.WORKLOADS[args.workload]
-    if args.steps <= 0:
-        args.steps = 200 if w.T <= 4096 else 50
     epilogue = None if args.epilogue == "none" else args.epilogue
-    if epilogue:
-        args.timing = "marker"       # the fused kernel has no launch-attached timing entry point
-    nbytes = algorithmic_bytes(w, epilogue)
-    R = args.rotate or max(1, min(32, math.ceil(2 * 2 ** 30 / nbytes["total"])))
+    if args.also == "auto":
+        others = [n for n in SECONDARY if n != w.name] if w.name == DEFAULT_WORKLOAD else []
+    elif args.also == "none":
+        others = []
+    else:
+        others = [n for n in args.also.split(",") if n]
 
-    logits_cpu = W.make_logits(w)
-    x_cpu = W.make_x(w)
-    route_groups = tuple(int(v) for v in args.route_groups.split(":")) if args.route_groups else None
-    packed = args.layout == "packed"
-    fuse_route = not args.separate_route and route_groups is None
-    sets = [BufferSet(w, logits_cpu, x_cpu, dev, moe, torch, route_groups, packed, epilogue, fuse_route)
-            for _ in range(R)]
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(w.seed * 16 + 3)
-    for s in sets:
-        s.step.route_and_dispatch()
-        s.fill_expert_outputs(w, torch, gen)
-    torch.cuda.synchronize()
-
-    K, Wm = args.steps, args.warmup
-    S = max(1, args.streams)
-    main = torch.cuda.current_stream()
-    streams = [main] + [torch.cuda.Stream() for _ in range(max(S, 2) - 1)]
-    hip_events = moe.HipEvents()
-
-    def bind(nstreams):
-        """Bind buffer set i to stream i % nstreams (a set never changes stream
-        while steps are queued)."""
-        torch.cuda.synchronize()
-        for si, st in enumerate(sets):
-            st.step = st.prepare(w, moe, stream=streams[si % nstreams])
-
-    def run_steps(first, n, nstreams, ev=None):
-        """n steps over buffer sets first, first+1, ...; when `ev` maps step
-        index -> (start, stop) raw events, those steps' combine launches are
-        timed."""
-        for i in range(n):
-            si = (first + i) % R
-            st = sets[si].step
-            st.route_and_dispatch()
-            pair = ev.get(i) if ev else None
-            if pair is None:
-                st.combine()
-            elif args.timing == "ext":
-                st.combine_timed(*pair)
-            else:
-                hip_events.record(pair[0], streams[si % nstreams])
-                st.combine()
-                hip_events.record(pair[1], streams[si % nstreams])
-
-    def timed(first, n, nstreams, ev=None):
-        torch.cuda.synchronize()
-        for strm in streams[1:nstreams]:
-            strm.wait_stream(main)
-        t0 = time.perf_counter()
-        run_steps(first, n, nstreams, ev)
-        for strm in streams[1:nstreams]:
-            main.wait_stream(strm)
-        torch.cuda.synchronize()
-        return (time.perf_counter() - t0) * 1e3 / n
-
-    # headline: S stream(s), combine timed per launch by its own kernel timestamps
-    if R % S:
-        R -= R % S
-    bind(S)
-    run_steps(0, Wm, S)
-    # every event pair is a pair of barrier packets in the stream (~3.5 us of
-    # lost pipelining each on this runtime), so only ~8 launches spread over
-    # the K timed steps carry them
-    every = max(1, K // 8)
-    ev = {i: (hip_events.create(), hip_events.create()) for i in range(every // 2, K, every)}
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(main)
-    wall_ms = timed(Wm, K, S, ev)
-    e1.record(main)
-    torch.cuda.synchronize()
-    event_ms = e0.elapsed_time(e1) / K     # includes the trailing sync gap; reported only
-    ms = wall_ms
-    combine_times = [hip_events.elapsed_ms(a, b) for a, b in ev.values()]
-    combine_ms = sum(combine_times) / len(combine_times)
-    for a, b in ev.values():
-        hip_events.destroy(a)
-        hip_events.destroy(b)
-
-    # the same steps without timing events, for comparison
-    plain_ms = timed(Wm + K, K, S)
-
-    # each call alone: events recorded around route + dispatch and around
-    # combine for ~K/4 steps, a pass of its own outside the timed region
-    per_call = None
-    if S == 1:
-        n = max(8, K // 4)
-        marks = [(hip_events.create(), hip_events.create(), hip_events.create()) for _ in range(n)]
-        torch.cuda.synchronize()
-        for i, (a, b, c) in enumerate(marks):
-            st = sets[(Wm + 2 * K + i) % R].step
-            hip_events.record(a, main)
-            st.route_and_dispatch()
-            hip_events.record(b, main)
-            st.combine()
-            hip_events.record(c, main)
-        torch.cuda.synchronize()
-
-        def stats(v):
-            v = sorted(x * 1e3 for x in v)
-            return {"median": v[len(v) // 2], "min": v[0], "max": v[-1]}
-        per_call = {"steps": n,
-                    "route_dispatch_us": stats([hip_events.elapsed_ms(a, b) for a, b, _ in marks]),
-                    "combine_us": stats([hip_events.elapsed_ms(b, c) for _, b, c in marks]),
-                    "timing": "device-release HIP events recorded around each call, one step at a time"}
-        for trio in marks:
-            for e in trio:
-                hip_events.destroy(e)
-
-    # the same steps replayed from HIP graphs (one captured step per buffer
-    # set): no host launch cost, so small batches show their GPU time
-    graph = None
-    if not args.no_graph and S == 1:
-        cap = torch.cuda.Stream()
-        torch.cuda.synchronize()
-        for st in sets:
-            st.step = st.prepare(w, moe, stream=cap)
-        graphs = []
-        for st in sets:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=cap):
-                st.step.route_and_dispatch()
-                st.step.combine()
-            graphs.append(g)
-        for i in range(Wm):
-            graphs[i % R].replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(K):
-            graphs[(Wm + i) % R].replay()
-        torch.cuda.synchronize()
-        g_ms = (time.perf_counter() - t0) * 1e3 / K
-        graph = {"ms_per_step": g_ms, "tokens_per_s": w.T / (g_ms * 1e-3),
-                 "hbm_frac": nbytes["total"] / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
-        del graphs
-        bind(S)
-
-    # two independent batches in flight (steps alternate over two streams)
-    overlap = None
-    if not args.no_overlap and S == 1 and R >= 2:
-        bind(2)
-        run_steps(0, Wm, 2)
-        ov_ms = timed(Wm, K, 2)
-        overlap = {"streams": 2, "ms_per_step": ov_ms, "tokens_per_s": w.T / (ov_ms * 1e-3),
-                   "hbm_frac": nbytes["total"] / (ov_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
-    gbps = nbytes["total"] / (ms * 1e-3) / 1e9
-    comb_gbps = nbytes["combine"] / (combine_ms * 1e-3) / 1e9
+    head = run_workload(w, args, moe, torch, dev, primary=True)
+    print(f"# {w.name}: {head['ms_per_step'] * 1e3:.1f} us/step, {head['hbm_frac']:.3f} of 8 TB/s",
+          file=sys.stderr, flush=True)
+    other = []
+    for name in others:
+        r = run_workload(W.WORKLOADS[name], args, moe, torch, dev, primary=False)
+        print(f"# {name}: {r['ms_per_step'] * 1e3:.1f} us/step, {r['hbm_frac']:.3f} of 8 TB/s", file=sys.stderr,
+              flush=True)
+        other.append(r)
 
     if args.copy_mib:
         n = args.copy_mib * 2 ** 20
@@ -403,59 +604,45 @@ def main() -> int:
         for _ in range(3):
             b.copy_(a)
         torch.cuda.synchronize()
+        del a, b
 
+    ms = head["ms_per_step"]
+    comb = head["kernels"]["combine"]
+    traffic = head.pop("_traffic", None)
+    config = {k: v for k, v in head.items() if k not in ("steps", "warmup", "ms_per_step")}
+    config["parallelism"] = "none (1 GPU)"
+    config["other_workloads"] = other
     result = {
         "metric": METRIC,
         "value": w.T / (ms * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": K,
-        "warmup": Wm,
+        "steps": head["steps"],
+        "warmup": head["warmup"],
         "ms_per_step": ms,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {
-            "workload": w.name, "tokens": w.T, "hidden": w.H, "experts": w.E, "top_k": w.k, "capacity": w.C,
-            "row_dtype": "fp8-e4m3+fp32/128" if w.fp8 else "bf16", "routing": w.routing,
-            "route_groups": ({"groups": route_groups[0], "kept": route_groups[1]} if route_groups else None),
-            "layout": "packed count-sized rows" if packed else "fixed slots per expert",
-            "route_dispatch_call": (("moe_route_dispatch_packed" if packed else "moe_route_dispatch") if fuse_route
-                                    else "separate"),
-            "combine_epilogue": {None: None, "rmsnorm": "residual add + RMSNorm (fused)",
-                                 "rmsnorm-fp8": "residual add + RMSNorm, output as E4M3 + fp32/128 (fused)"}[epilogue],
-            "parallelism": "none (1 GPU)",
-            "algorithmic_bytes_per_step": nbytes["total"],
-            "effective_hbm_gbps": gbps,
-            "hbm_frac": gbps / HBM_PEAK_GBPS,
-            "buffer_copies_cycled": R,
-            "streams": S,
-            "ms_per_step_events": event_ms,
-            "ms_per_step_without_timing_events": plain_ms,
-            "two_batches_in_flight": overlap,
-            "graph_replay": graph,
-            "per_call": per_call,
-        },
+        "config": config,
         "roofline": {
-            "kernel": (f"combine_rmsnorm_kernel (k={w.k}{', fp8 out' if epilogue == 'rmsnorm-fp8' else ''})"
-                       if epilogue else f"moe_combine (k={w.k}); profiles/{w.name}_kernel_trace.md names the kernel"),
+            "kernel": (f"{comb['call']} (k={w.k}); profiles/{w.name}_kernel_trace.md names the kernel instance"),
             "bound": "hbm",
-            "achieved": comb_gbps,
+            "achieved": comb["gbps"],
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
-            "frac": comb_gbps / HBM_PEAK_GBPS,
-            "traffic": None if (packed or epilogue) else measured_traffic(w),
+            "frac": comb["frac"],
+            "traffic": traffic,
             "traffic_source": f"profiles/{w.name}_hbm_traffic.md (bytes per launch)",
-            "algorithmic_bytes_per_launch": nbytes["combine"],
-            "mean_launch_us": combine_ms * 1e3,
-            "median_launch_us": sorted(combine_times)[len(combine_times) // 2] * 1e3,
-            "timed_launches": len(combine_times),
-            "min_launch_us": min(combine_times) * 1e3,
-            "max_launch_us": max(combine_times) * 1e3,
-            "timing": ("device-release HIP events attached to each timed combine launch (moe_combine_timed)"
-                       if args.timing == "ext" else "device-release HIP events recorded around each timed combine"),
+            "algorithmic_bytes_per_launch": comb["bytes"],
+            "mean_launch_us": comb["mean_us"],
+            "median_launch_us": comb["median_us"],
+            "min_launch_us": comb["min_us"],
+            "max_launch_us": comb["max_us"],
+            "timed_launches": comb["launches"],
+            "timing": "HIP events recorded on the launch stream around every combine call of a timing pass run "
+                      "after the (event-free) headline region",
         },
     }
     if not args.no_cpu_baseline:

@@ -70,8 +70,6 @@ def load() -> ctypes.CDLL:
     lib.moe_combine_residual_rmsnorm_fp8.argtypes = [P, i32, i32, i32, P, P, i64, i32, P, P, ctypes.c_float, P, P,
                                                      P, P, P]
     lib.moe_combine_residual_rmsnorm_fp8.restype = ctypes.c_int
-    lib.moe_combine_timed.argtypes = [P, i32, i32, i32, P, P, i64, i32, P, P, P, P]
-    lib.moe_combine_timed.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -82,7 +80,7 @@ def moe_status_string(status: int) -> str:
 
 class HipEvents:
     """Raw hipEvent_t handles from the HIP runtime this process already uses
-    (the one torch loaded), for moe_combine_timed."""
+    (the one torch loaded), recorded on the stream a call is launched on."""
 
     def __init__(self):
         lib = None
@@ -373,11 +371,10 @@ def moe_route_dispatch_packed(logits: torch.Tensor, x: torch.Tensor, k: int, fp8
 
 
 def moe_combine(y: torch.Tensor, token_slot: torch.Tensor, topk_w: torch.Tensor, out: torch.Tensor | None = None,
-                stream=None, events: tuple[int, int] | None = None) -> torch.Tensor:
+                stream=None) -> torch.Tensor:
     """out[t] = bf16(sum_j w[t,j] * y[token_slot[t,j]]), fp32 FMA in top-k order.
     y is [E, C, H] (fixed slots) or [rows, H] (packed layout: one expert
-    with `rows` slots).  `events` = (start, stop) raw hipEvent_t handles
-    selects moe_combine_timed."""
+    with `rows` slots)."""
     if y.dim() == 2:
         y = y.view(1, max(1, y.shape[0]), y.shape[1]) if y.shape[0] else y.new_empty(1, 1, y.shape[1])
     E, C, H = y.shape
@@ -388,13 +385,9 @@ def moe_combine(y: torch.Tensor, token_slot: torch.Tensor, topk_w: torch.Tensor,
     if out is None:
         out = torch.empty(T, H, dtype=torch.bfloat16, device=y.device)
     _need(out, torch.bfloat16, (T, H), "out")
-    args = (_ptr(y), E, C, H, _ptr(token_slot), _ptr(topk_w), T, k, _ptr(out), _stream(stream))
-    if events is None:
-        rc = load().moe_combine(*args)
-    else:
-        rc = load().moe_combine_timed(*args, events[0], events[1])
+    rc = load().moe_combine(_ptr(y), E, C, H, _ptr(token_slot), _ptr(topk_w), T, k, _ptr(out), _stream(stream))
     if rc != MOE_OK:
-        raise MoeError("moe_combine" if events is None else "moe_combine_timed", rc)
+        raise MoeError("moe_combine", rc)
     return out
 
 
@@ -587,10 +580,3 @@ class PreparedStep:
         if rc != MOE_OK:
             raise MoeError("moe_combine", rc)
 
-    def combine_timed(self, start_event: int, stop_event: int):
-        """combine, with raw hipEvent_t handles recording its kernel's start and end."""
-        if self._epilogue_args is not None:
-            raise MoeError("moe_combine_timed", MOE_ERR_INVALID)
-        rc = self._lib.moe_combine_timed(*self.combine_args, start_event, stop_event)
-        if rc != MOE_OK:
-            raise MoeError("moe_combine_timed", rc)

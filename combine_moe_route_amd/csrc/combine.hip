@@ -21,8 +21,6 @@
 // result identical on every run.  Expert rows and the output are streamed
 // with non-temporal loads/stores.  Slots outside [0, E*C) are skipped, which
 // is also how dropped (over-capacity) pairs are handled.
-#include <hip/hip_ext.h>
-
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -181,48 +179,40 @@ Shape choose_shape(int64_t T, int nvec, int k)
 
 template <int K, int VPL>
 hipError_t launch_vpl(const uint16_t *y, int64_t nrows, int nvec, const int32_t *token_slot, const float *w,
-                      int64_t T, uint16_t *out, hipStream_t s, hipEvent_t start, hipEvent_t stop)
+                      int64_t T, uint16_t *out, hipStream_t s)
 {
     const int segs = (nvec + VPL * kWave - 1) / (VPL * kWave);
     const int64_t blocks = (T * segs + kWavesPerBlock - 1) / kWavesPerBlock;
     if (!grid_fits(blocks, kBlock))
         return hipErrorInvalidConfiguration;
-    if (start || stop)
-        hipExtLaunchKernelGGL((combine_kernel<K, VPL>), dim3((unsigned)blocks), dim3(kBlock), 0, s, start, stop, 0,
-                              (const u32x4 *)y, nrows, nvec, token_slot, w, T, segs, (u32x4 *)out);
-    else
-        hipLaunchKernelGGL((combine_kernel<K, VPL>), dim3((unsigned)blocks), dim3(kBlock), 0, s, (const u32x4 *)y,
-                           nrows, nvec, token_slot, w, T, segs, (u32x4 *)out);
+    hipLaunchKernelGGL((combine_kernel<K, VPL>), dim3((unsigned)blocks), dim3(kBlock), 0, s, (const u32x4 *)y,
+                       nrows, nvec, token_slot, w, T, segs, (u32x4 *)out);
     return hipGetLastError();
 }
 
 template <int K>
 hipError_t launch_row(const uint16_t *y, int64_t nrows, int nvec, const int32_t *token_slot, const float *w,
-                      int64_t T, int bs, uint16_t *out, hipStream_t s, hipEvent_t start, hipEvent_t stop)
+                      int64_t T, int bs, uint16_t *out, hipStream_t s)
 {
     if (bs < nvec || bs > 1024 || !grid_fits(T, bs))
         return hipErrorInvalidConfiguration;
-    if (start || stop)
-        hipExtLaunchKernelGGL((combine_row_kernel<K>), dim3((unsigned)T), dim3(bs), 0, s, start, stop, 0,
-                              (const u32x4 *)y, nrows, nvec, token_slot, w, (u32x4 *)out);
-    else
-        hipLaunchKernelGGL((combine_row_kernel<K>), dim3((unsigned)T), dim3(bs), 0, s, (const u32x4 *)y, nrows,
-                           nvec, token_slot, w, (u32x4 *)out);
+    hipLaunchKernelGGL((combine_row_kernel<K>), dim3((unsigned)T), dim3(bs), 0, s, (const u32x4 *)y, nrows, nvec,
+                       token_slot, w, (u32x4 *)out);
     return hipGetLastError();
 }
 
 template <int K>
 hipError_t launch(const uint16_t *y, int64_t nrows, int H, const int32_t *token_slot, const float *w, int64_t T,
-                  uint16_t *out, hipStream_t s, hipEvent_t start, hipEvent_t stop)
+                  uint16_t *out, hipStream_t s)
 {
     constexpr int V = vpl_for(K);
     const int nvec = H / 8;
     const Shape sh = choose_shape(T, nvec, K);
     if (sh.vpl == 0)
-        return launch_row<K>(y, nrows, nvec, token_slot, w, T, sh.bs, out, s, start, stop);
+        return launch_row<K>(y, nrows, nvec, token_slot, w, T, sh.bs, out, s);
     if (sh.vpl == 1)
-        return launch_vpl<K, 1>(y, nrows, nvec, token_slot, w, T, out, s, start, stop);
-    return launch_vpl<K, V>(y, nrows, nvec, token_slot, w, T, out, s, start, stop);
+        return launch_vpl<K, 1>(y, nrows, nvec, token_slot, w, T, out, s);
+    return launch_vpl<K, V>(y, nrows, nvec, token_slot, w, T, out, s);
 }
 
 }  // namespace
@@ -238,11 +228,11 @@ bool combine_grid_fits(int64_t T, int H, int k)
 }
 
 hipError_t launch_combine(const uint16_t *y, int64_t nrows, int H, const int32_t *token_slot, const float *w,
-                          int64_t T, int k, uint16_t *out, hipStream_t s, hipEvent_t start, hipEvent_t stop)
+                          int64_t T, int k, uint16_t *out, hipStream_t s)
 {
     switch (k) {
 #define MOE_COMBINE_K(K) \
-    case K: return launch<K>(y, nrows, H, token_slot, w, T, out, s, start, stop);
+    case K: return launch<K>(y, nrows, H, token_slot, w, T, out, s);
     MOE_COMBINE_K(1) MOE_COMBINE_K(2) MOE_COMBINE_K(3) MOE_COMBINE_K(4)
     MOE_COMBINE_K(5) MOE_COMBINE_K(6) MOE_COMBINE_K(7) MOE_COMBINE_K(8)
     MOE_COMBINE_K(9) MOE_COMBINE_K(10) MOE_COMBINE_K(11) MOE_COMBINE_K(12)

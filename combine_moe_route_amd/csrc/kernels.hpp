@@ -41,11 +41,8 @@ hipError_t launch_dispatch(const uint16_t *x, int64_t T, int H, const int32_t *t
                            int32_t *expert_counts, int32_t *expert_offsets, int32_t *token_slot, void *workspace,
                            hipStream_t s);
 
-// start/stop: optional events recorded at the kernel's start and end
-// (hipExtLaunchKernel); both NULL for an ordinary launch.
 hipError_t launch_combine(const uint16_t *y, int64_t nrows, int H, const int32_t *token_slot, const float *w,
-                          int64_t T, int k, uint16_t *out, hipStream_t s, hipEvent_t start = nullptr,
-                          hipEvent_t stop = nullptr);
+                          int64_t T, int k, uint16_t *out, hipStream_t s);
 
 // combine + residual add + RMSNorm; residual_out may be residual (in place).
 // normed_q != NULL adds the E4M3 codes [T][H] and per-128 scales [T][H/128]

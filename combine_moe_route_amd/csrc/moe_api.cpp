@@ -297,8 +297,7 @@ MOE_API int moe_dispatch_packed(const uint16_t *x, int64_t T, int32_t H, const i
 namespace {
 
 int combine_checked(const uint16_t *y, int32_t E, int32_t capacity, int32_t H, const int32_t *token_slot,
-                    const float *topk_w, int64_t T, int32_t k, uint16_t *out, hipStream_t stream, hipEvent_t start,
-                    hipEvent_t stop)
+                    const float *topk_w, int64_t T, int32_t k, uint16_t *out, hipStream_t stream)
 {
     if (T < 0 || H < 1 || capacity < 1 || E < 1 || k < 1)
         return MOE_ERR_INVALID;
@@ -322,7 +321,7 @@ int combine_checked(const uint16_t *y, int32_t E, int32_t capacity, int32_t H, c
         return MOE_ERR_UNSUPPORTED;
     (void)hipGetLastError();
     return from_hip(
-        moe::launch_combine(y, (int64_t)E * capacity, H, token_slot, topk_w, T, k, out, stream, start, stop));
+        moe::launch_combine(y, (int64_t)E * capacity, H, token_slot, topk_w, T, k, out, stream));
 }
 
 }  // namespace
@@ -330,14 +329,7 @@ int combine_checked(const uint16_t *y, int32_t E, int32_t capacity, int32_t H, c
 MOE_API int moe_combine(const uint16_t *y, int32_t E, int32_t capacity, int32_t H, const int32_t *token_slot,
                         const float *topk_w, int64_t T, int32_t k, uint16_t *out, hipStream_t stream)
 {
-    return combine_checked(y, E, capacity, H, token_slot, topk_w, T, k, out, stream, nullptr, nullptr);
-}
-
-MOE_API int moe_combine_timed(const uint16_t *y, int32_t E, int32_t capacity, int32_t H,
-                              const int32_t *token_slot, const float *topk_w, int64_t T, int32_t k, uint16_t *out,
-                              hipStream_t stream, hipEvent_t start, hipEvent_t stop)
-{
-    return combine_checked(y, E, capacity, H, token_slot, topk_w, T, k, out, stream, start, stop);
+    return combine_checked(y, E, capacity, H, token_slot, topk_w, T, k, out, stream);
 }
 
 }  // extern "C"

@@ -304,21 +304,6 @@ MOE_API int moe_combine(const uint16_t *y, int32_t E, int32_t capacity, int32_t 
                         uint16_t *out, hipStream_t stream);
 
 /*
- * moe_combine_timed -- moe_combine, plus device timestamps of its kernel.
- *
- * For callers that time the combine kernel on its own (benchmarks,
- * launch-shape tuning) without adding marker packets to the stream: the
- * kernel is launched so that `start` and `stop` (created beforehand with
- * hipEventCreate; either may be NULL) record the start and end of its
- * execution; hipEventElapsedTime(start, stop) is then the kernel's run time.
- * Arguments, results and errors are otherwise those of moe_combine; with
- * T = 0 nothing is launched and the events are left untouched.
- */
-MOE_API int moe_combine_timed(const uint16_t *y, int32_t E, int32_t capacity, int32_t H,
-                              const int32_t *token_slot, const float *topk_w, int64_t T, int32_t k,
-                              uint16_t *out, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
-
-/*
  * moe_combine_residual_rmsnorm -- moe_combine with its epilogue fused: the
  * residual add and the next module's RMSNorm.
  *

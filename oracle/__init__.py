@@ -273,6 +273,84 @@ def fixed_slot_bytes(experts: int, slots_per_expert: int, H: int, dtype: int, he
     return int(_load().oracle_fixed_slot_bytes(experts, slots_per_expert, H, dtype, header_bytes))
 
 
+# ---------------------------------------------------------------------------
+# Range forms for the benchmark's host-cores baseline: the same C functions,
+# called on disjoint token (or expert) ranges of preallocated arrays so that
+# several threads can run them at once (ctypes releases the GIL for the
+# duration of each call).  Marshalling only: no arithmetic here.
+# ---------------------------------------------------------------------------
+
+def route_topk_range(logits: np.ndarray, k: int, idx: np.ndarray, w: np.ndarray, t0: int, t1: int):
+    """route_topk of tokens t0 .. t1-1, written into rows t0 .. t1-1 of idx and w."""
+    T, E = logits.shape
+    assert logits.dtype == np.float32 and logits.flags.c_contiguous and 0 <= t0 <= t1 <= T
+    assert idx.shape == (T, k) and w.shape == (T, k) and idx.flags.c_contiguous and w.flags.c_contiguous
+    _check(_load().oracle_route_topk(_ptr(logits) + t0 * E * 4, t1 - t0, E, k, _ptr(idx) + t0 * k * 4,
+                                     _ptr(w) + t0 * k * 4), "route_topk")
+
+
+def pack_range(x_bits: np.ndarray, dtype: int, recv_src: np.ndarray, counts: np.ndarray, capacity: int,
+               rows: np.ndarray, scales: np.ndarray | None, slot_of_row: np.ndarray, e0: int, e1: int, p0: int):
+    """pack() of experts e0 .. e1-1 only, written from row p0 of the dense
+    outputs (p0 = the filled rows of experts below e0).  slot_of_row holds
+    slots relative to expert e0 (add e0 * capacity for the absolute slot)."""
+    T, H = x_bits.shape
+    E = counts.shape[0]
+    assert 0 <= e0 <= e1 <= E and x_bits.flags.c_contiguous
+    if e1 == e0:
+        return
+    row_bytes = H * (2 if dtype == BF16 else 1)
+    _check(_load().oracle_pack(_ptr(x_bits), T, H, dtype, _ptr(recv_src) + e0 * capacity * 4, _ptr(counts) + e0 * 4,
+                               e1 - e0, capacity, _ptr(rows) + p0 * row_bytes,
+                               None if scales is None else _ptr(scales) + p0 * (H // 128) * 4,
+                               _ptr(slot_of_row) + p0 * 4), "pack")
+
+
+def combine_range(y_pairs_bits: np.ndarray, token_slot: np.ndarray, w: np.ndarray, out: np.ndarray, t0: int,
+                  t1: int):
+    """combine() of tokens t0 .. t1-1, written into rows t0 .. t1-1 of out."""
+    T, k = token_slot.shape
+    H = out.shape[1]
+    assert 0 <= t0 <= t1 <= T and y_pairs_bits.shape == (T * k, H) and out.shape == (T, H)
+    for a in (y_pairs_bits, token_slot, w, out):
+        assert a.flags.c_contiguous
+    if t1 == t0:
+        return
+    _check(_load().oracle_combine(_ptr(y_pairs_bits) + t0 * k * H * 2, _ptr(token_slot) + t0 * k * 4,
+                                  _ptr(w) + t0 * k * 4, t1 - t0, k, H, _ptr(out) + t0 * H * 2, None), "combine")
+
+
+def combine_residual_rmsnorm_range(y_pairs_bits: np.ndarray, token_slot: np.ndarray, w: np.ndarray,
+                                   residual_bits: np.ndarray, gamma_bits: np.ndarray, eps: float,
+                                   residual_out: np.ndarray, normed_out: np.ndarray, t0: int, t1: int):
+    """combine_residual_rmsnorm() of tokens t0 .. t1-1, written into those
+    rows of residual_out and normed_out."""
+    T, k = token_slot.shape
+    H = normed_out.shape[1]
+    assert 0 <= t0 <= t1 <= T and y_pairs_bits.shape == (T * k, H) and residual_bits.shape == (T, H)
+    for a in (y_pairs_bits, token_slot, w, residual_bits, gamma_bits, residual_out, normed_out):
+        assert a.flags.c_contiguous
+    if t1 == t0:
+        return
+    _check(_load().oracle_combine_residual_rmsnorm(
+        _ptr(y_pairs_bits) + t0 * k * H * 2, _ptr(token_slot) + t0 * k * 4, _ptr(w) + t0 * k * 4, t1 - t0, k, H,
+        _ptr(residual_bits) + t0 * H * 2, _ptr(gamma_bits), float(eps), _ptr(residual_out) + t0 * H * 2,
+        _ptr(normed_out) + t0 * H * 2), "combine_residual_rmsnorm")
+
+
+def quantize_rows_fp8_range(x_bits: np.ndarray, codes: np.ndarray, scales: np.ndarray, r0: int, r1: int):
+    """quantize_rows_fp8() of rows r0 .. r1-1, written into those rows of
+    codes and scales."""
+    n, H = x_bits.shape
+    assert 0 <= r0 <= r1 <= n and codes.shape == (n, H) and scales.shape == (n, H // 128)
+    for a in (x_bits, codes, scales):
+        assert a.flags.c_contiguous
+    if r1 == r0:
+        return
+    _check(_load().oracle_quantize_rows_fp8(_ptr(x_bits) + r0 * H * 2, r1 - r0, H, _ptr(codes) + r0 * H,
+                                            _ptr(scales) + r0 * (H // 128) * 4), "quantize_rows_fp8")
+
+
 def run_pipeline(logits: np.ndarray, x_bits: np.ndarray, k: int, capacity: int, dtype: int,
                  y_pairs_bits: np.ndarray | None = None):
     """Route, assign slots, pack and (if y_pairs given) combine, all on the CPU."""

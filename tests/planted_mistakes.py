@@ -4,6 +4,8 @@ Run by hand (not collected by pytest; a few minutes on 4 cores):
 
     python tests/planted_mistakes.py
 
+(The output of its last run is kept in tests/planted_mistakes_result.txt.)
+
 For every mistake below, a copy of oracle/ with that one change in
 moe_oracle.c is built in a temporary directory and the oracle's pin tests
 (-m "not gpu") are run against it.  A mistake "survives" when every pin test
@@ -53,6 +55,8 @@ CORE = {
   'packed_inclusive_offsets': ('        offsets[e] = (int32_t)run;\n        run += count[e];', '        run += count[e];\n        offsets[e] = (int32_t)run;'),
   'fp8_scale_reciprocal_mul': ('amax / 448.0f;', 'amax * (1.0f / 448.0f);'),
   'fp8_zero_block_scale_0': ('(amax == 0.0f) ? 1.0f :', '(amax == 0.0f) ? 0.0f :'),
+  'fp8_rows_scale_stride': ('codes + r * H, scales + r * (H / 128));', 'codes + r * H, scales + r);'),
+  'fp8_rows_code_stride': ('codes + r * H, scales + r * (H / 128));', 'codes + r * 128, scales + r * (H / 128));'),
   'fp8_amax_signed': ('float a = fabsf(bf16_bits_to_float(x[b * 128 + i]));', 'float a = bf16_bits_to_float(x[b * 128 + i]);'),
   'e4m3_no_saturation': ('    if (a > 448.0)\n        return (uint8_t)(sign | 0x7E);', '    if (a > 464.0)\n        return (uint8_t)(sign | 0x7F);'),
   'e4m3_ties_away': ('double m = rint(ldexp(a, 3 - e));', 'double m = floor(ldexp(a, 3 - e) + 0.5);'),

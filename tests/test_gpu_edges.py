@@ -267,27 +267,6 @@ def test_api_rejects_bad_arguments(dev):
     torch.cuda.synchronize()
 
 
-def test_combine_timed_matches_combine(dev):
-    rng = np.random.default_rng(31)
-    T, H, E, k, C = 300, 512, 16, 4, 300
-    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
-    counts, slot, src = oracle.assign_slots(idx, E, C)
-    w = rng.uniform(0, 1, (T, k)).astype(np.float32)
-    y = torch.randn(E, C, H, device=dev).to(torch.bfloat16)
-    ts, wt = torch.from_numpy(slot).to(dev), torch.from_numpy(w).to(dev)
-    ref = moe.moe_combine(y, ts, wt)
-    ev = moe.HipEvents()
-    a, b = ev.create(), ev.create()
-    got = moe.moe_combine(y, ts, wt, events=(a, b))
-    ms = ev.elapsed_ms(a, b)
-    ev.destroy(a)
-    ev.destroy(b)
-    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
-    assert 0.0 < ms < 1000.0
-    want = oracle.combine(dev_bits(y.view(E * C, H))[slot.reshape(-1)], slot, w)
-    assert bf16_ulp_distance(dev_bits(got), want).max() <= 1
-
-
 @pytest.mark.parametrize("T,H,k", [
     (4096, 2056, 3),    # one work-group per token, 320 threads for a ragged 257-vector row
     (2048, 8192, 2),    # one work-group per token, 1024 threads

@@ -160,3 +160,81 @@ def test_pack_fp8_rows_are_quantised_sources(name):
         t = recv_src[s]
         np.testing.assert_array_equal(rows[p], per_token[t][0])
         np.testing.assert_array_equal(scales[p], per_token[t][1])
+
+
+def _rows_with_edge_blocks(n: int, H: int, seed: int) -> np.ndarray:
+    """Seeded bf16 rows [n, H] of widely spread magnitudes, with an all-zero
+    block, a block holding the largest finite bf16 magnitude and a block of
+    tiny (subnormal-code) values in some rows."""
+    rng = np.random.default_rng(seed)
+    mag = 10.0 ** rng.uniform(-4, 4, (n, H))
+    x = torch.from_numpy((rng.standard_normal((n, H)) * mag).astype(np.float32)).to(torch.bfloat16)
+    xb = W.bits(x).reshape(n, H).copy()
+    nblk = H // 128
+    for r in range(n):
+        b = r % nblk
+        if r % 3 == 0:
+            xb[r, b * 128:(b + 1) * 128] = 0                       # all-zero block: scale 1
+        elif r % 3 == 1:
+            xb[r, b * 128 + (r % 128)] = 0x7F7F                    # largest finite bf16
+            xb[r, b * 128 + ((r + 1) % 128)] = 0xFF7F              # and its negative
+        else:
+            xb[r, b * 128:(b + 1) * 128] = 0x0001                  # smallest bf16 subnormal
+    return xb
+
+
+@pytest.mark.parametrize("n,H", [(0, 128), (1, 128), (3, 6144), (257, 128), (5, 7168), (4, 6144)])
+def test_quantize_rows_equals_row_by_row(n, H):
+    """The batch form must give, row for row, what the per-row encoding
+    (pinned above by the E4M3 table, torch's conversion and the error bound)
+    gives: one scale per 128 elements of the same row, codes at the same
+    positions.  A wrong code or scale stride, or a row offset, shows here."""
+    xb = _rows_with_edge_blocks(n, H, seed=n * 31 + H)
+    codes, scales = oracle.quantize_rows_fp8(xb)
+    assert codes.shape == (n, H) and scales.shape == (n, H // 128)
+    for r in range(n):
+        c1, s1 = oracle.quantize_row_fp8(xb[r])
+        np.testing.assert_array_equal(codes[r], c1, err_msg=f"row {r} codes")
+        np.testing.assert_array_equal(scales[r], s1, err_msg=f"row {r} scales")
+
+
+def test_quantize_rows_edge_blocks_decode_within_bound():
+    """Independent of the per-row function: every block of the batch form
+    dequantises to its own source block within the E4M3 error bound, the
+    zero blocks get scale 1, and the largest finite bf16 magnitude maps onto
+    448 exactly (the block's amax code)."""
+    n, H = 6, 384
+    xb = _rows_with_edge_blocks(n, H, seed=7)
+    codes, scales = oracle.quantize_rows_fp8(xb)
+    xf = (xb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    deq = _dequant(codes.reshape(-1), scales.reshape(-1)).reshape(n, H)
+    sc = np.repeat(scales.astype(np.float64), 128, axis=1)
+    ratio = np.abs(xf) / sc
+    normal = ratio >= 2.0 ** -6
+    err = np.abs(xf - deq)
+    assert np.all(err[normal] <= 2.0 ** -4 * (1 + 2.0 ** -20) * np.abs(xf[normal]))
+    assert np.all(err[~normal] <= 2.0 ** -10 * (1 + 2.0 ** -20) * sc[~normal])
+    for r in range(n):
+        b = r % (H // 128)
+        blk = slice(b * 128, (b + 1) * 128)
+        if r % 3 == 0:
+            assert scales[r, b] == 1.0 and (codes[r, blk] == 0).all()
+        elif r % 3 == 1:
+            assert codes[r, b * 128 + (r % 128)] == 0x7E
+            assert codes[r, b * 128 + ((r + 1) % 128)] == 0xFE
+            np.testing.assert_allclose(scales[r, b] * 448.0, float(np.float32(xf[r, b * 128 + (r % 128)])),
+                                       rtol=2.0 ** -23)
+
+
+def test_quantize_rows_agrees_with_pack_on_decode_workload():
+    """The rows the GPU tests take their expected codes from must be those
+    oracle.pack writes into the slots (same workload, same sources)."""
+    w = W.WORKLOADS["dsr1_decode"]
+    idx, _ = oracle.route_topk(W.make_logits(w).numpy(), w.k)
+    counts, _, recv_src = oracle.assign_slots(idx, w.E, w.C)
+    x = W.bits(W.make_x(w))
+    rows, scales, slot_of_row = oracle.pack(x, oracle.FP8_E4M3, recv_src, counts, w.C)
+    codes, blk_scales = oracle.quantize_rows_fp8(x)
+    src = recv_src[slot_of_row]
+    np.testing.assert_array_equal(rows, codes[src])
+    np.testing.assert_array_equal(scales, blk_scales[src])

@@ -3,8 +3,9 @@
 by the sum of its two best expert scores, only the best nodes stay eligible,
 and the top experts are picked among them).
 
-Independent checks: the handbook's printed worked example (4096 seeded tokens
-over 8 nodes of 32 experts), a brute force that characterises the kept groups
+Independent checks: the figures the handbook prints for its worked example
+(4096 seeded tokens over 8 nodes of 32 experts; the measures are recomputed
+here from their definitions), a brute force that characterises the kept groups
 and the chosen experts by pairwise dominance instead of repeated selection,
 and special cases that reduce to the plain router (pinned on its own) or to
 closed forms.
@@ -22,37 +23,63 @@ import workloads as W
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "node_limited_routing.json")
 
 
-def _page_example_stats(idx, spec):
-    """Per-token means of the handbook's traffic measures for a source GPU on
-    node 0: nodes touched (including node 0), chosen experts on other nodes,
-    distinct GPUs on other nodes, distinct other nodes."""
-    per_gpu = spec["experts"] // (spec["nodes"] * spec["gpus_per_node"])
-    gpu = idx // per_gpu
-    node = gpu // spec["gpus_per_node"]
-    touched = np.mean([len(set(r)) for r in node])
-    per_expert = np.mean((node != 0).sum(axis=1))
-    per_gpu_copies = np.mean([len({g for g in r if g // spec["gpus_per_node"] != 0}) for r in gpu])
-    per_node = np.mean([len(set(r) - {0}) for r in node])
-    ms = lambda c: spec["tokens"] * c * spec["token_bytes"] / spec["nic_bytes_per_s"] * 1e3
-    return {"nodes_touched": touched, "copies_per_expert": per_expert, "copies_per_gpu": per_gpu_copies,
-            "copies_per_node": per_node, "ms_per_expert": ms(per_expert), "ms_per_gpu": ms(per_gpu_copies),
-            "ms_per_node": ms(per_node)}
+def _membership(unit_of_choice: np.ndarray, n_units: int) -> np.ndarray:
+    """Boolean [T, n_units]: True where at least one of the token's chosen
+    experts lies in that unit (an expert, a GPU or a node)."""
+    T = unit_of_choice.shape[0]
+    m = np.zeros((T, n_units), dtype=bool)
+    m[np.repeat(np.arange(T), unit_of_choice.shape[1]), unit_of_choice.reshape(-1)] = True
+    return m
+
+
+def _traffic_measures(idx: np.ndarray, spec: dict) -> dict:
+    """The worked example's per-token means, for a source GPU on node 0.  A
+    copy leaves the node once per distinct destination at the level that
+    deduplicates: per chosen expert, per GPU or per node.  Units are numbered
+    so that node 0 holds the first ones at every level; the source node's own
+    units send nothing over the network."""
+    T = idx.shape[0]
+    n_gpus = spec["nodes"] * spec["gpus_per_node"]
+    experts_per_gpu = spec["experts"] // n_gpus
+    levels = {"expert": (1, spec["experts"]), "gpu": (experts_per_gpu, n_gpus),
+              "node": (experts_per_gpu * spec["gpus_per_node"], spec["nodes"])}
+    local = {"expert": experts_per_gpu * spec["gpus_per_node"], "gpu": spec["gpus_per_node"], "node": 1}
+    out = {}
+    for level, (experts_per_unit, n_units) in levels.items():
+        hit = _membership(idx // experts_per_unit, n_units)
+        if level == "node":
+            out["nodes_touched"] = hit.sum(axis=1).mean()
+        copies = hit[:, local[level]:].sum(axis=1).mean()
+        out[f"copies_per_{level}"] = copies
+        # NIC time of the batch: bytes sent over the network / NIC bandwidth
+        out[f"ms_per_{level}"] = T * copies * spec["token_bytes"] / spec["nic_bytes_per_s"] * 1e3
+    return out
+
+
+def _page_scores(spec: dict) -> np.ndarray:
+    """The seeded router scores of the worked example, from the draw the
+    golden file records (float64 draws, then float32 for the routers)."""
+    d = spec["draw"]
+    assert d["generator"] == "numpy.random.default_rng"
+    stream = np.random.default_rng(d["seed"])
+    per_pair = stream.random(spec["tokens"] * spec["experts"]).reshape(spec["tokens"], spec["experts"])
+    per_expert = stream.random(spec["experts"])
+    return (per_pair + d["expert_offset_scale"] * per_expert[None, :]).astype(np.float32)
 
 
 def test_page_worked_example():
     spec = json.load(open(GOLDEN))
-    rng = np.random.default_rng(0)
-    scores = rng.random((spec["tokens"], spec["experts"])) + rng.random(spec["experts"]) * 0.5
-    logits = scores.astype(np.float32)
+    logits = _page_scores(spec)
     k, G, M = spec["topk"], spec["nodes"], spec["max_nodes"]
     free_idx, _ = oracle.route_topk(logits, k)
     lim_idx, _ = oracle.route_topk_grouped(logits, k, G, M)
     for name, idx in (("unlimited", free_idx), ("limited", lim_idx)):
-        got = _page_example_stats(idx, spec)
+        got = _traffic_measures(idx, spec)
         for key, printed in spec["printed"][name].items():
             assert round(got[key], 2) == pytest.approx(printed, abs=1e-9), (name, key, got[key], printed)
     # every token stays within M nodes under the limit
-    assert max(len(set(r)) for r in lim_idx // 32) <= M
+    experts_per_node = spec["experts"] // G
+    assert _membership(lim_idx // experts_per_node, G).sum(axis=1).max() <= M
 
 
 def _scores(row, G):
