@@ -9,6 +9,7 @@ from .binding import (  # noqa: F401
     MOE_DTYPE_FP8_E4M3,
     MOE_MAX_EXPERTS,
     MOE_MAX_TOPK,
+    MOE_NOALLOC_SCRATCH_BYTES,
     DispatchBuffers,
     HipEvents,
     MoeError,
@@ -22,6 +23,7 @@ from .binding import (  # noqa: F401
     moe_dispatch_packed,
     moe_dispatch_workspace_bytes,
     moe_route_dispatch,
+    moe_route_dispatch_noalloc,
     moe_route_dispatch_packed,
     moe_route_topk,
     moe_route_topk_grouped,

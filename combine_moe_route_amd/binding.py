@@ -22,10 +22,12 @@ MOE_ERR_INVALID = -1
 MOE_ERR_UNSUPPORTED = -2
 MOE_ERR_WORKSPACE = -3
 MOE_ERR_HIP = -4
+MOE_ERR_SCRATCH = -5
 MOE_DTYPE_BF16 = 0
 MOE_DTYPE_FP8_E4M3 = 1
 MOE_MAX_EXPERTS = 1024
 MOE_MAX_TOPK = 16
+MOE_NOALLOC_SCRATCH_BYTES = 4 << 20
 
 _lib = None
 
@@ -58,6 +60,8 @@ def load() -> ctypes.CDLL:
     lib.moe_route_dispatch.argtypes = [P, i64, i32, i32, P, i32, i32, i32, P, P, P, P, P, P, P, P,
                                        ctypes.c_size_t, P]
     lib.moe_route_dispatch.restype = ctypes.c_int
+    lib.moe_route_dispatch_noalloc.argtypes = [P, i64, i32, i32, P, i32, i32, i32, P, P, P, P, P, P, P, P]
+    lib.moe_route_dispatch_noalloc.restype = ctypes.c_int
     lib.moe_route_dispatch_packed.argtypes = [P, i64, i32, i32, P, i32, i32, P, P, P, P, P, P, P, P,
                                               ctypes.c_size_t, P]
     lib.moe_route_dispatch_packed.restype = ctypes.c_int
@@ -203,14 +207,17 @@ class DispatchBuffers:
     workspace: torch.Tensor       # uint8 scratch
 
     @staticmethod
-    def allocate(T: int, H: int, E: int, k: int, capacity: int, fp8: bool, device) -> "DispatchBuffers":
+    def allocate(T: int, H: int, E: int, k: int, capacity: int, fp8: bool, device,
+                 workspace: bool = True) -> "DispatchBuffers":
+        """workspace=False: a 256-byte placeholder (moe_route_dispatch_noalloc
+        uses the library's own scratch)."""
         if fp8:
             recv_x = torch.empty(E, capacity, H, dtype=torch.uint8, device=device)
             recv_scales = torch.empty(E, capacity, H // 128, dtype=torch.float32, device=device)
         else:
             recv_x = torch.empty(E, capacity, H, dtype=torch.bfloat16, device=device)
             recv_scales = None
-        ws = moe_dispatch_workspace_bytes(T, E, k)
+        ws = moe_dispatch_workspace_bytes(T, E, k) if workspace else 0
         return DispatchBuffers(
             recv_x=recv_x, recv_scales=recv_scales,
             recv_src=torch.empty(E, capacity, dtype=torch.int32, device=device),
@@ -276,6 +283,38 @@ def moe_route_dispatch(logits: torch.Tensor, x: torch.Tensor, k: int, capacity: 
         _stream(stream))
     if rc != MOE_OK:
         raise MoeError("moe_route_dispatch", rc)
+    return topk_idx, topk_w, bufs
+
+
+def moe_route_dispatch_noalloc(logits: torch.Tensor, x: torch.Tensor, k: int, capacity: int, fp8: bool = False,
+                               bufs: DispatchBuffers | None = None, topk_idx: torch.Tensor | None = None,
+                               topk_w: torch.Tensor | None = None, stream=None):
+    """moe_route_dispatch with the library's static scratch in place of the
+    workspace (bufs.workspace is not used).  Returns (topk_idx, topk_w, bufs)."""
+    T, E = logits.shape
+    H = x.shape[1]
+    _need(logits, torch.float32, (T, E), "logits")
+    _need(x, torch.bfloat16, (T, H), "x")
+    if topk_idx is None:
+        topk_idx = torch.empty(T, k, dtype=torch.int32, device=x.device)
+    if topk_w is None:
+        topk_w = torch.empty(T, k, dtype=torch.float32, device=x.device)
+    _need(topk_idx, torch.int32, (T, k), "topk_idx")
+    _need(topk_w, torch.float32, (T, k), "topk_w")
+    if bufs is None:
+        bufs = DispatchBuffers.allocate(T, H, E, k, capacity, fp8, x.device, workspace=False)
+    _need(bufs.recv_x, torch.uint8 if fp8 else torch.bfloat16, (E, capacity, H), "recv_x")
+    if fp8:
+        _need(bufs.recv_scales, torch.float32, (E, capacity, H // 128), "recv_scales")
+    _need(bufs.recv_src, torch.int32, (E, capacity), "recv_src")
+    _need(bufs.expert_counts, torch.int32, (E,), "expert_counts")
+    _need(bufs.token_slot, torch.int32, (T, k), "token_slot")
+    rc = load().moe_route_dispatch_noalloc(
+        _ptr(logits), T, E, k, _ptr(x), H, capacity, MOE_DTYPE_FP8_E4M3 if fp8 else MOE_DTYPE_BF16, _ptr(topk_idx),
+        _ptr(topk_w), _ptr(bufs.recv_x), _ptr(bufs.recv_scales) if fp8 else None, _ptr(bufs.recv_src),
+        _ptr(bufs.expert_counts), _ptr(bufs.token_slot), _stream(stream))
+    if rc != MOE_OK:
+        raise MoeError("moe_route_dispatch_noalloc", rc)
     return topk_idx, topk_w, bufs
 
 

@@ -29,6 +29,11 @@ hipError_t launch_route_topk_grouped(const float *logits, int64_t T, int E, int 
 
 size_t dispatch_workspace_bytes(int64_t T, int E, int k);
 
+// Device address of the library's static scratch array on the current
+// device (MOE_NOALLOC_SCRATCH_BYTES bytes, 256 B aligned), looked up on the
+// first call per device.
+hipError_t noalloc_scratch(void **out);
+
 // Whether the pack (dispatch) or combine launch grid for this shape stays
 // within one launch's 2^32 - 1 work-items (host-only, no HIP call).
 bool dispatch_grid_fits(int64_t T, int H, int k, int dtype);

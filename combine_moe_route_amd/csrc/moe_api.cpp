@@ -121,6 +121,7 @@ MOE_API const char *moe_status_string(int status)
     case MOE_ERR_UNSUPPORTED: return "unsupported size";
     case MOE_ERR_WORKSPACE: return "workspace missing or too small";
     case MOE_ERR_HIP: return "HIP launch failed";
+    case MOE_ERR_SCRATCH: return "batch needs more workspace than the static scratch (MOE_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
     }
 }
@@ -207,7 +208,8 @@ namespace {
 int route_dispatch_checked(const float *logits, int64_t T, int32_t E, int32_t k, const uint16_t *x, int32_t H,
                            int32_t capacity, int32_t out_dtype, int32_t *topk_idx, float *topk_w, void *recv_x,
                            float *recv_scales, int32_t *recv_src, int32_t *expert_counts, int32_t *expert_offsets,
-                           int32_t *token_slot, void *workspace, size_t workspace_bytes, hipStream_t stream)
+                           int32_t *token_slot, void *workspace, size_t workspace_bytes, hipStream_t stream,
+                           bool noalloc = false)
 {
     if (T < 0 || H < 1 || capacity < 1)
         return MOE_ERR_INVALID;
@@ -235,6 +237,13 @@ int route_dispatch_checked(const float *logits, int64_t T, int32_t E, int32_t k,
     if (out_dtype == MOE_DTYPE_BF16 && recv_scales)
         return MOE_ERR_INVALID;
     const size_t need = moe::dispatch_workspace_bytes(T, E, k);
+    if (noalloc) {   // the library's static array stands in for the workspace
+        if (need > (size_t)MOE_NOALLOC_SCRATCH_BYTES)
+            return MOE_ERR_SCRATCH;
+        if (moe::noalloc_scratch(&workspace) != hipSuccess)
+            return MOE_ERR_HIP;
+        workspace_bytes = MOE_NOALLOC_SCRATCH_BYTES;
+    }
     if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
         return MOE_ERR_WORKSPACE;
     if (T > 0) {
@@ -271,6 +280,15 @@ MOE_API int moe_route_dispatch(const float *logits, int64_t T, int32_t E, int32_
 {
     return route_dispatch_checked(logits, T, E, k, x, H, capacity, out_dtype, topk_idx, topk_w, recv_x, recv_scales,
                                   recv_src, expert_counts, nullptr, token_slot, workspace, workspace_bytes, stream);
+}
+
+MOE_API int moe_route_dispatch_noalloc(const float *logits, int64_t T, int32_t E, int32_t k, const uint16_t *x,
+                                       int32_t H, int32_t capacity, int32_t out_dtype, int32_t *topk_idx,
+                                       float *topk_w, void *recv_x, float *recv_scales, int32_t *recv_src,
+                                       int32_t *expert_counts, int32_t *token_slot, hipStream_t stream)
+{
+    return route_dispatch_checked(logits, T, E, k, x, H, capacity, out_dtype, topk_idx, topk_w, recv_x, recv_scales,
+                                  recv_src, expert_counts, nullptr, token_slot, nullptr, 0, stream, true);
 }
 
 MOE_API int moe_route_dispatch_packed(const float *logits, int64_t T, int32_t E, int32_t k, const uint16_t *x,

@@ -22,7 +22,8 @@
  * Conventions for every entry point
  *   - Pointers marked (device) are HIP device pointers; the caller allocates
  *     and owns every buffer.  The library allocates nothing on these paths
- *     and keeps no state between calls.
+ *     and keeps no state between calls, except moe_route_dispatch_noalloc's
+ *     static per-GPU scratch array (documented there).
  *   - All work is enqueued on `stream` (NULL = the default stream) and the
  *     call returns without waiting: no device synchronisation and no
  *     device-to-host copy, so calls can be captured in a HIP graph.
@@ -58,6 +59,8 @@ extern "C" {
 #define MOE_ERR_UNSUPPORTED (-2)  /* a size this library does not handle (limits below) */
 #define MOE_ERR_WORKSPACE (-3)    /* workspace missing or smaller than moe_dispatch_workspace_bytes() */
 #define MOE_ERR_HIP (-4)          /* a HIP launch failed */
+#define MOE_ERR_SCRATCH (-5)      /* moe_route_dispatch_noalloc: the batch needs more workspace than
+                                     MOE_NOALLOC_SCRATCH_BYTES */
 
 /* Dispatch row formats. */
 #define MOE_DTYPE_BF16 0          /* rows copied bit for bit, 2*H bytes */
@@ -69,6 +72,7 @@ extern "C" {
 #define MOE_MAX_GROUPS 64         /* expert groups of moe_route_topk_grouped */
 #define MOE_MAX_NORM_HIDDEN 16384 /* H of moe_combine_residual_rmsnorm */
 #define MOE_MAX_TOKENS (1 << 24)  /* T above this is MOE_ERR_UNSUPPORTED */
+#define MOE_NOALLOC_SCRATCH_BYTES (4 << 20)  /* static device scratch of moe_route_dispatch_noalloc */
 /* Also MOE_ERR_UNSUPPORTED: a dispatch or combine shape whose single kernel
  * launch would need more than 2^32 - 1 work-items.  Each lane moves at least
  * 128 bytes of row data per copy, so only rows wider than 32768 elements at
@@ -210,6 +214,34 @@ MOE_API int moe_route_dispatch(const float *logits, int64_t T, int32_t E, int32_
                                float *topk_w, void *recv_x, float *recv_scales, int32_t *recv_src,
                                int32_t *expert_counts, int32_t *token_slot, void *workspace,
                                size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_route_dispatch_noalloc -- moe_route_dispatch with no workspace
+ * argument, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * The call allocates nothing (no hipMalloc, no allocating library routine).
+ * Its per-chunk histograms, in-chunk ranks and router membership words live
+ * in a static array of MOE_NOALLOC_SCRATCH_BYTES (4 MiB) in each GPU's
+ * memory, which the library holds from the first call on that device until
+ * the process ends.  The first call on a device (with it current) looks up
+ * that array's device address; later calls reuse it.
+ *
+ *   Arguments, outputs and results: exactly those of moe_route_dispatch,
+ *   minus workspace and workspace_bytes.
+ *   Limit: moe_dispatch_workspace_bytes(T, E, k) <= MOE_NOALLOC_SCRATCH_BYTES
+ *   (for example T * k up to about a million pairs), else MOE_ERR_SCRATCH
+ *   and nothing is enqueued.  MOE_ERR_HIP if the address lookup fails.
+ *   Every call on one GPU shares that GPU's array, and nothing in it needs
+ *   to start at zero (each call writes what it reads).  Calls that overlap
+ *   in time on one GPU (different streams, or different host threads
+ *   without ordering) race on the array and give undefined results; calls
+ *   on one stream, or ordered by events, do not.
+ */
+MOE_API int moe_route_dispatch_noalloc(const float *logits, int64_t T, int32_t E, int32_t k, const uint16_t *x,
+                                       int32_t H, int32_t capacity, int32_t out_dtype, int32_t *topk_idx,
+                                       float *topk_w, void *recv_x, float *recv_scales, int32_t *recv_src,
+                                       int32_t *expert_counts, int32_t *token_slot, hipStream_t stream);
 
 /*
  * moe_dispatch_packed -- per-expert counts, packed count-sized layout and

@@ -232,3 +232,31 @@ def test_overlapping_buffers_are_rejected(lib):
     y, out = rx, x
     assert c(y, E, T, H, slot, tw, T, k, out, None) == -4                # control
     assert c(y, E, T, H, slot, tw, T, k, slot, None) == -1               # out over the slots
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="passes fake device addresses; host-only check")
+def test_noalloc_checks_before_any_hip_call(lib):
+    """moe_route_dispatch_noalloc checks its arguments, then the batch's
+    workspace need against its static scratch (MOE_ERR_SCRATCH), all on the
+    host before the scratch address is looked up or anything is enqueued."""
+    na = lib.moe_route_dispatch_noalloc
+    P = None
+    assert na(P, 4, 8, 2, P, 64, 4, 0, P, P, P, P, P, P, P, P) == -1       # null pointers
+    assert na(P, 4, 8, 9, P, 64, 4, 0, P, P, P, P, P, P, P, P) == -1       # k > E
+    assert na(P, 4, 8, 2, P, 64, 0, 0, P, P, P, P, P, P, P, P) == -1       # capacity 0
+    assert na(P, 4, 8, 2, P, 100, 4, 0, P, P, P, P, P, P, P, P) == -2      # H % 8
+    assert na(P, 4, 4096, 2, P, 64, 4, 0, P, P, P, P, P, P, P, P) == -2    # E above the limit
+
+    def call(T, E, k, H=128):
+        lg, x, idx, tw, rx, src, cnt, slot = _fake_layout(T * E * 4, T * H * 2, T * k * 4, T * k * 4,
+                                                          E * T * 2 * H, E * T * 4, E * 4, T * k * 4)
+        return na(lg, T, E, k, x, H, T, 0, idx, tw, rx, None, src, cnt, slot, None)
+
+    limit = moe.MOE_NOALLOC_SCRATCH_BYTES
+    assert moe.moe_dispatch_workspace_bytes(200_000, 16, 8) > limit
+    assert call(200_000, 16, 8) == moe.binding.MOE_ERR_SCRATCH
+    assert "scratch" in moe.moe_status_string(moe.binding.MOE_ERR_SCRATCH)
+    # a batch within the limit passes every host check and fails only at the
+    # scratch lookup (no GPU here): MOE_ERR_HIP
+    assert moe.moe_dispatch_workspace_bytes(4096, 16, 8) <= limit
+    assert call(4096, 16, 8) == -4
