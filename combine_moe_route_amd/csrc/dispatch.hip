@@ -54,8 +54,14 @@ namespace {
 
 constexpr int kChunk = 256;          // tokens per count work-group (one mask bit each)
 constexpr int kMaskWords = kChunk / 32;
+// LDS membership masks are laid out [E][stride] with an odd stride (one word
+// of padding): with a power-of-two stride, the lanes of one instruction that
+// read or OR word w of different experts all hit a few LDS banks; an odd
+// stride spreads them over every bank.
+constexpr int kMaskStride = kMaskWords + 1;
 constexpr int kMaskChunk = 32;       // tokens per router membership word
 constexpr int kLocalTokens = 2 * kChunk;   // pack counts the batch itself up to this many tokens
+constexpr int kMaxK = 16;                  // the largest k the library accepts (MOE_MAX_TOPK)
 
 // Membership words per expert kept in LDS by the pack modes that count the
 // batch themselves: one 256-token chunk's 8, or ceil(T/32) for larger batches.
@@ -63,6 +69,7 @@ __host__ __device__ constexpr int local_words(int64_t T)
 {
     return T <= kChunk ? kMaskWords : (int)((T + 31) / 32);
 }
+__host__ __device__ constexpr int local_stride(int nw) { return nw | 1; }
 
 // Exclusive scan of the work-group's n <= 4*256 values in LDS (thread i owns
 // values 4i .. 4i+3): out[i] = sum of in[0 .. i-1] for i < n, out[n] = total.
@@ -102,46 +109,81 @@ __device__ __forceinline__ void block_exclusive_scan(const int32_t *in, int n, i
     }
 }
 
+// The count kernel's LDS row per expert: the chunk's 8 membership words,
+// then the exclusive prefix of their popcounts as 8 bytes in 2 words (each
+// at most 7 * 32 = 224), then one word of padding so the stride is odd.
+constexpr int kCountPrefix = kMaskWords;            // word offset of the prefix bytes
+constexpr int kCountStride = kMaskWords + 2 + 1;    // 11
+
 __global__ __launch_bounds__(kBlock) void dispatch_count_kernel(const int32_t *__restrict__ topk_idx, int64_t T,
                                                                 int E, int k, int nchunks,
                                                                 int32_t *__restrict__ chunk_counts,
                                                                 int32_t *__restrict__ local_rank)
 {
-    extern __shared__ uint32_t mask[];  // [E][kMaskWords]
+    extern __shared__ uint32_t mask[];  // [E][kCountStride]
     const int tid = threadIdx.x;
     const int c = blockIdx.x;
-    for (int i = tid; i < E * kMaskWords; i += kBlock)
+    for (int i = tid; i < E * kCountStride; i += kBlock)
         mask[i] = 0u;
     __syncthreads();
 
     const int64_t t = (int64_t)c * kChunk + tid;
     const int word = tid >> 5;
     const uint32_t bit = 1u << (tid & 31);
+    // The token's ids, loaded once.  Lanes walk their k choices starting at
+    // different positions (j0 = lane mod k): with skewed routing a hot expert
+    // tends to sit at the same position j for many tokens, and lanes of one
+    // 32-token word ORing into the same LDS word in one instruction
+    // serialise; rotated, such lanes mostly land in different instructions.
+    int ids[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j)
+        ids[j] = (t < T && j < k) ? topk_idx[t * k + j] : -1;
+    const int j0 = tid % k;
     if (t < T) {
-        for (int j = 0; j < k; ++j) {
-            const int e = topk_idx[t * k + j];
+#pragma unroll
+        for (int jj = 0; jj < kMaxK; ++jj) {
+            if (jj >= k)
+                break;
+            int j = j0 + jj;
+            j = j >= k ? j - k : j;
+            int e = -1;
+#pragma unroll
+            for (int q = 0; q < kMaxK; ++q)
+                e = q == j ? ids[q] : e;
             if ((unsigned)e < (unsigned)E)
-                atomicOr(&mask[e * kMaskWords + word], bit);
+                atomicOr(&mask[e * kCountStride + word], bit);
         }
     }
     __syncthreads();
 
+    // per expert: the chunk's count, and the prefix of each word's popcount
     for (int e = tid; e < E; e += kBlock) {
+        uint32_t *row = mask + e * kCountStride;
+        uint32_t pre[2] = {0u, 0u};
         int n = 0;
 #pragma unroll
-        for (int w = 0; w < kMaskWords; ++w)
-            n += __popc(mask[e * kMaskWords + w]);
+        for (int w = 0; w < kMaskWords; ++w) {
+            pre[w >> 2] |= (uint32_t)n << (8 * (w & 3));
+            n += __popc(row[w]);
+        }
+        row[kCountPrefix] = pre[0];
+        row[kCountPrefix + 1] = pre[1];
         chunk_counts[(int64_t)e * nchunks + c] = n;
     }
+    __syncthreads();
 
+    // rank of (t, j) in the chunk: earlier words' total + earlier bits of its own word
     if (t < T) {
-        for (int j = 0; j < k; ++j) {
-            const int e = topk_idx[t * k + j];
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j) {
+            if (j >= k)
+                break;
+            const int e = ids[j];
             int r = -1;
             if ((unsigned)e < (unsigned)E) {
-                r = __popc(mask[e * kMaskWords + word] & (bit - 1u));
-                for (int w = 0; w < word; ++w)
-                    r += __popc(mask[e * kMaskWords + w]);
+                const uint32_t *row = mask + e * kCountStride;
+                r = __popc(row[word] & (bit - 1u)) + (int)((row[kCountPrefix + (word >> 2)] >> (8 * (word & 3))) & 0xFFu);
             }
             local_rank[t * k + j] = r;
         }
@@ -289,7 +331,7 @@ __device__ __forceinline__ void store_stream(float *p, float v) { __builtin_nont
 // from L2), so no count launch is needed; up to 512 tokens are counted the
 // same way, with ceil(T/32) words per expert (local_words).  The ids are requested before the
 // row loads (local_ids_load): vector loads retire in order, so waiting for
-// ids issued after the rows would wait for the rows too.  lds: [E][nw] mask
+// ids issued after the rows would wait for the rows too.  lds: [E][nw | 1] mask
 // words, then for the packed layout [E+1] offsets (the exclusive scan of the
 // popcounts).  Work-group 0 publishes the totals (or offsets).  All threads
 // must call both.
@@ -312,7 +354,7 @@ __device__ __forceinline__ void local_ids_load(const int32_t *__restrict__ topk_
 // The chunk's per-expert totals from its complete LDS masks: work-group 0
 // writes them (fixed slots), or every work-group scans them into loffs and
 // work-group 0 writes the offsets (packed layout).  All threads call it.
-__device__ __forceinline__ void local_totals(int E, int nw, bool packed, const uint32_t *lmask, int32_t *loffs,
+__device__ __forceinline__ void local_totals(int E, int nw, int ns, bool packed, const uint32_t *lmask, int32_t *loffs,
                                              int32_t *wave_sums, int32_t *__restrict__ expert_counts,
                                              int32_t *__restrict__ expert_offsets)
 {
@@ -321,7 +363,7 @@ __device__ __forceinline__ void local_totals(int E, int nw, bool packed, const u
         int n = 0;
 #pragma unroll
         for (int w = 0; w < nw; ++w)
-            n += __popc(lmask[e * nw + w]);
+            n += __popc(lmask[e * ns + w]);
         if (packed)
             loffs[e] = n;
         else if (blockIdx.x == 0)
@@ -337,13 +379,14 @@ __device__ __forceinline__ void local_totals(int E, int nw, bool packed, const u
     }
 }
 
-__device__ __forceinline__ void local_chunk_counts(const int (&ids)[kLocalIds], int E, int k, int nw, bool packed,
+__device__ __forceinline__ void local_chunk_counts(const int (&ids)[kLocalIds], int E, int k, int nw, int ns,
+                                                   bool packed,
                                                    uint32_t *lmask, int32_t *loffs, int32_t *wave_sums,
                                                    int32_t *__restrict__ expert_counts,
                                                    int32_t *__restrict__ expert_offsets)
 {
     const int tid = threadIdx.x;
-    for (int i = tid; i < E * nw; i += kBlock)
+    for (int i = tid; i < E * ns; i += kBlock)
         lmask[i] = 0u;
     __syncthreads();
 #pragma unroll
@@ -351,11 +394,11 @@ __device__ __forceinline__ void local_chunk_counts(const int (&ids)[kLocalIds], 
         const int e = ids[q];   // pair p = tid + q*256 of token p / k; -1 past the end
         if ((unsigned)e < (unsigned)E) {
             const int tok = (tid + q * kBlock) / k;
-            atomicOr(&lmask[e * nw + (tok >> 5)], 1u << (tok & 31));
+            atomicOr(&lmask[e * ns + (tok >> 5)], 1u << (tok & 31));
         }
     }
     __syncthreads();
-    local_totals(E, nw, packed, lmask, loffs, wave_sums, expert_counts, expert_offsets);
+    local_totals(E, nw, ns, packed, lmask, loffs, wave_sums, expert_counts, expert_offsets);
 }
 
 // Route + dispatch of a batch of at most 256 tokens with E <= 8 in one
@@ -473,7 +516,7 @@ __device__ __forceinline__ void route_local_counts(const float (&v)[kRoutePasses
 {
     const int tid = threadIdx.x;
     const int gl = lane_id() % 8;
-    for (int i = tid; i < E * kMaskWords; i += kBlock)
+    for (int i = tid; i < E * kMaskStride; i += kBlock)
         lmask[i] = 0u;
     __syncthreads();
     const bool store = blockIdx.x == 0;
@@ -489,11 +532,11 @@ __device__ __forceinline__ void route_local_counts(const float (&v)[kRoutePasses
                                                          store ? out_w : nullptr);
         if (active && gl < k) {
             lids[tt * k + gl] = e;
-            atomicOr(&lmask[e * kMaskWords + ((int)tt >> 5)], 1u << ((int)tt & 31));
+            atomicOr(&lmask[e * kMaskStride + ((int)tt >> 5)], 1u << ((int)tt & 31));
         }
     }
     __syncthreads();
-    local_totals(E, kMaskWords, packed, lmask, loffs, wave_sums, expert_counts, expert_offsets);
+    local_totals(E, kMaskWords, kMaskStride, packed, lmask, loffs, wave_sums, expert_counts, expert_offsets);
 }
 
 // The expert id (and for 256-token chunks the in-chunk rank) of pair
@@ -540,7 +583,7 @@ __device__ __forceinline__ int wave_slot(PairIds pre, const int32_t *__restrict_
                                          const int32_t *__restrict__ local_rank,
                                          const int32_t *__restrict__ chunk_counts, const uint32_t *__restrict__ masks,
                                          const int32_t *__restrict__ offs, const uint32_t *lmask, const int32_t *loffs,
-                                         int64_t t, int E, int k, int C, int nchunks, int lanes_per_pair, int nw)
+                                         int64_t t, int E, int k, int C, int nchunks, int lanes_per_pair, int ns)
 {
     const int lane = lane_id();
     const int j = lane / lanes_per_pair;
@@ -554,9 +597,9 @@ __device__ __forceinline__ int wave_slot(PairIds pre, const int32_t *__restrict_
                 base = loffs ? loffs[e] : offs[e];
             if (lmask) {
                 const int word = (int)t >> 5;
-                r = __popc(lmask[e * nw + word] & ((1u << ((int)t & 31)) - 1u));
+                r = __popc(lmask[e * ns + word] & ((1u << ((int)t & 31)) - 1u));
                 for (int w = 0; w < word; ++w)
-                    r += __popc(lmask[e * nw + w]);
+                    r += __popc(lmask[e * ns + w]);
             } else if (masks) {
                 const uint32_t *row = masks + (int64_t)e * nchunks;
                 r = __popc(row[c] & ((1u << (int)(t % kMaskChunk)) - 1u));
@@ -660,7 +703,8 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_bf16_kernel(
     __shared__ int32_t wave_sums[kWavesPerBlock];
     uint32_t *lmask = LOCAL ? lds_words : nullptr;
     const int nw = local_words(T);   // LDS membership words per expert (local modes)
-    int32_t *loffs = LOCAL && offs ? (int32_t *)(lds_words + E * nw)
+    const int ns = local_stride(nw); // and the row stride of the masks
+    int32_t *loffs = LOCAL && offs ? (int32_t *)(lds_words + E * ns)
                      : MODE == kPackMaskOffsets ? (int32_t *)(lds_words + E) : nullptr;
     const int lane = lane_id();
     const int64_t task = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
@@ -698,13 +742,13 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_bf16_kernel(
     if (MODE == kPackMaskOffsets)
         mask_words_count(mw);
     // (local counting overlaps the row loads; every thread takes part)
-    int32_t *lroute = (int32_t *)(lds_words + E * nw + E + 1);   // routed ids [T][k]
+    int32_t *lroute = (int32_t *)(lds_words + E * ns + E + 1);   // routed ids [T][k]
     if (MODE == kPackLocalIds)
-        local_chunk_counts(lids, E, k, nw, offs != nullptr, lds_words, (int32_t *)(lds_words + E * nw),
+        local_chunk_counts(lids, E, k, nw, ns, offs != nullptr, lds_words, (int32_t *)(lds_words + E * ns),
                            wave_sums, expert_counts, offs);
     if (MODE == kPackLocalRoute) {
         route_local_counts(rv, rkey, T, E, k, offs != nullptr, route_idx, route_w, lds_words, lroute,
-                           (int32_t *)(lds_words + E * nw), wave_sums, expert_counts, offs);
+                           (int32_t *)(lds_words + E * ns), wave_sums, expert_counts, offs);
         const int j = lane / lanes_per_pair;
         ids.e = active && j < k ? lroute[t * k + j] : -1;
     }
@@ -715,7 +759,7 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_bf16_kernel(
 
     const int slot = wave_slot<LOCAL, MODE == kPackScanned>(ids, topk_idx, local_rank, chunk_counts, masks, offs,
                                                              lmask, loffs, t, E, k, C, nchunks, lanes_per_pair,
-                                                             nw);
+                                                             ns);
     if (seg == 0)
         record_slot(slot, t, k, lanes_per_pair, token_slot, recv_src);
     if (task < E && expert_counts && !LOCAL && MODE != kPackScanned)
@@ -763,7 +807,8 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_fp8_kernel(
     __shared__ int32_t wave_sums[kWavesPerBlock];
     uint32_t *lmask = LOCAL ? lds_words : nullptr;
     const int nw = local_words(T);   // LDS membership words per expert (local modes)
-    int32_t *loffs = LOCAL && offs ? (int32_t *)(lds_words + E * nw)
+    const int ns = local_stride(nw); // and the row stride of the masks
+    int32_t *loffs = LOCAL && offs ? (int32_t *)(lds_words + E * ns)
                      : MODE == kPackMaskOffsets ? (int32_t *)(lds_words + E) : nullptr;
     const int lane = lane_id();
     const int64_t task = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
@@ -805,13 +850,13 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_fp8_kernel(
     if (MODE == kPackMaskOffsets)
         mask_words_count(mw);
     // (local counting overlaps the row loads; every thread takes part)
-    int32_t *lroute = (int32_t *)(lds_words + E * nw + E + 1);   // routed ids [T][k]
+    int32_t *lroute = (int32_t *)(lds_words + E * ns + E + 1);   // routed ids [T][k]
     if (MODE == kPackLocalIds)
-        local_chunk_counts(lids, E, k, nw, offs != nullptr, lds_words, (int32_t *)(lds_words + E * nw),
+        local_chunk_counts(lids, E, k, nw, ns, offs != nullptr, lds_words, (int32_t *)(lds_words + E * ns),
                            wave_sums, expert_counts, offs);
     if (MODE == kPackLocalRoute) {
         route_local_counts(rv, rkey, T, E, k, offs != nullptr, route_idx, route_w, lds_words, lroute,
-                           (int32_t *)(lds_words + E * nw), wave_sums, expert_counts, offs);
+                           (int32_t *)(lds_words + E * ns), wave_sums, expert_counts, offs);
         const int j = lane / lanes_per_pair;
         ids.e = active && j < k ? lroute[t * k + j] : -1;
     }
@@ -822,7 +867,7 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_fp8_kernel(
 
     const int slot = wave_slot<LOCAL, MODE == kPackScanned>(ids, topk_idx, local_rank, chunk_counts, masks, offs,
                                                              lmask, loffs, t, E, k, C, nchunks, lanes_per_pair,
-                                                             nw);
+                                                             ns);
     if (seg == 0)
         record_slot(slot, t, k, lanes_per_pair, token_slot, recv_src);
     if (task < E && expert_counts && !LOCAL && MODE != kPackScanned)
@@ -926,11 +971,11 @@ hipError_t launch_pack(const uint16_t *x, int64_t T, int H, const int32_t *topk_
                        int32_t *expert_counts, int32_t *token_slot, hipStream_t s, int mode = kPackChunks,
                        const float *logits = nullptr, int32_t *route_idx = nullptr, float *route_w = nullptr)
 {
-    // single chunk: masks [E][8] and offsets [E+1] in LDS (+ routed ids [T][k]);
+    // single chunk: masks [E][9] (or [E][nw | 1]) and offsets [E+1] in LDS (+ routed ids [T][k]);
     // totals from membership words: totals [E] and offsets [E+1]
     const size_t lds = mode == kPackChunks || mode == kPackScanned ? 0
                      : mode == kPackMaskOffsets ? (size_t)(2 * E + 1) * 4
-                     : (size_t)(E * local_words(T) + E + 1 + (mode == kPackLocalRoute ? T * k : 0)) * 4;
+                     : (size_t)(E * local_stride(local_words(T)) + E + 1 + (mode == kPackLocalRoute ? T * k : 0)) * 4;
     const int lpp = pair_lanes(k);
     int vpl, segs;
     if (!pack_split(T, H, k, dtype, &vpl, &segs))
@@ -1038,7 +1083,7 @@ hipError_t launch_dispatch(const uint16_t *x, int64_t T, int H, const int32_t *t
         (int32_t *)((char *)workspace + ((int64_t)E * nchunks * 4 + 255) / 256 * 256);
 
     // packed layout: one more work-group totals the chunks and scans
-    hipLaunchKernelGGL(dispatch_count_kernel, dim3(nchunks), dim3(kBlock), (size_t)E * kMaskWords * 4, s, topk_idx,
+    hipLaunchKernelGGL(dispatch_count_kernel, dim3(nchunks), dim3(kBlock), (size_t)E * kCountStride * 4, s, topk_idx,
                        T, E, k, nchunks, chunk_counts, local_rank);
     if (expert_offsets)
         hipLaunchKernelGGL(dispatch_offsets_kernel<false>, dim3(1), dim3(kScanBlock), 0, s, chunk_counts, E,
