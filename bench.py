@@ -279,9 +279,12 @@ class BufferSet:
         self.out = torch.empty(w.T, w.H, dtype=torch.bfloat16, device=dev)
         self.epilogue = None
         if epilogue:
-            # residual stream (the activations stand in for it) and RMSNorm weight
+            # residual stream (a copy of the activations, in its own memory: were
+            # it x itself, the next step's pack would find x in the last-level
+            # cache, freshly read by this combine) and RMSNorm weight
+            residual = self.x.clone()
             gamma = torch.linspace(0.5, 1.5, w.H, device=dev).to(torch.bfloat16)
-            self.epilogue = (self.x, gamma, 1e-6, torch.empty(w.T, w.H, dtype=torch.bfloat16, device=dev))
+            self.epilogue = (residual, gamma, 1e-6, torch.empty(w.T, w.H, dtype=torch.bfloat16, device=dev))
             if epilogue == "rmsnorm-fp8":
                 self.epilogue += (torch.empty(w.T, w.H, dtype=torch.uint8, device=dev),
                                   torch.empty(w.T, w.H // 128, dtype=torch.float32, device=dev))
