@@ -165,6 +165,8 @@ def test_empty_combine_and_route(dev):
     (500, 256, 256, 8, 500, False, "normal"),     # 256 experts x 16 words: the largest local mask
     (500, 256, 512, 8, 500, False, "normal"),     # 512 experts x 16 words: count launch
     (400, 128, 1024, 8, 400, False, "zeros"),     # 1024 experts: count launch
+    (1100, 64, 1024, 16, 1100, False, "normal"),  # the largest E and k together through the count launch
+    (2000, 64, 1024, 16, 700, False, "ties"),     # and with ties and capacity overflow
     (512, 64, 32, 16, 512, False, "normal"),      # 8192 ids: count launch
     (257, 64, 16, 16, 257, False, "normal"),      # 4112 ids: count launch
     (480, 136, 20, 3, 37, False, "normal"),       # counted inside pack, with capacity overflow

@@ -76,7 +76,7 @@ def test_workloads(dev, name):
     _check(name, o.logits, o.x, w.k, w.C, w.fp8, fused, separate)
 
 
-@pytest.mark.parametrize("T", [1, 31, 32, 33, 255, 256, 257, 1000, 65536, 65537])
+@pytest.mark.parametrize("T", [1, 31, 32, 33, 255, 256, 257, 1000, 4096, 4097, 65536, 65537])
 def test_token_counts(dev, T):
     rng = np.random.default_rng(T)
     E, k, H = 8, 2, 64
