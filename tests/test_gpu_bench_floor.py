@@ -1,0 +1,77 @@
+"""The benchmark's copy floors (bench_floor.hip) move the bytes they are
+compared against: floor_scatter_rows writes every filled slot's row (the
+whole bf16 row, or H code bytes plus one 4-byte word per 128 elements) and
+nothing else; floor_gather_rows reads each token's k slotted rows and writes
+one row per token.  Checked on small dispatches through the library, so the
+slot maps are the real ones."""
+import numpy as np
+import pytest
+import torch
+
+import bench
+import combine_moe_route_amd as moe
+from gpu_common import require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+SENT = 0x5A
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return require_gpu()
+
+
+@pytest.mark.parametrize("T,H,E,k,fp8", [(300, 256, 16, 4, False), (300, 512, 16, 4, True), (1000, 1024, 8, 2, False),
+                                         (200, 384, 64, 8, True)])
+def test_floor_kernels_touch_exactly_the_slotted_rows(dev, T, H, E, k, fp8):
+    say(f"[floor] T={T} H={H} E={E} k={k} fp8={fp8}")
+    lib = bench.floor_lib()
+    g = torch.Generator(device="cpu")
+    g.manual_seed(T + H + E)
+    logits = torch.randn(T, E, generator=g).to(dev)
+    x = torch.randn(T, H, generator=g).to(torch.bfloat16).to(dev)
+    C = T
+    idx, wt, bufs = moe.moe_route_dispatch(logits, x, k, C, fp8=fp8)
+    slots = bufs.token_slot.cpu().numpy()
+    # scatter into fresh, sentinel-filled rows
+    rows = torch.full((E * C, H * (1 if fp8 else 2)), SENT, dtype=torch.uint8, device=dev)
+    scales = torch.full((E * C, H // 128 * 4), SENT, dtype=torch.uint8, device=dev) if fp8 else None
+    s = torch.cuda.current_stream().cuda_stream
+    rc = lib.floor_scatter_rows(x.data_ptr(), T, H, int(fp8), bufs.token_slot.data_ptr(), k, rows.data_ptr(),
+                                scales.data_ptr() if fp8 else None, s)
+    assert rc == 0
+    torch.cuda.synchronize()
+    filled = np.zeros(E * C, bool)
+    filled[slots[slots >= 0]] = True
+    r = rows.cpu().numpy()
+    xb = x.view(torch.uint8).cpu().numpy().reshape(T, 2 * H)
+    assert (r[~filled] == SENT).all(), "a row outside the slots was written"
+    for t in range(T):
+        for j in range(k):
+            sl = slots[t, j]
+            if not fp8:
+                np.testing.assert_array_equal(r[sl], xb[t])          # the row itself
+            else:
+                lo_hi = xb[t].reshape(-1, 2, 16)                     # per 16-element group: two 16 B halves
+                np.testing.assert_array_equal(r[sl], np.bitwise_xor(lo_hi[:, 0], lo_hi[:, 1]).reshape(-1))
+    if fp8:
+        sc = scales.cpu().numpy()
+        assert (sc[~filled] == SENT).all()
+        assert (sc[filled] != SENT).any()
+    # gather: every token's row written, from the rows its slots name
+    y = torch.randint(0, 256, (E * C, 2 * H), dtype=torch.uint8, device=dev)
+    out = torch.full((T, 2 * H), SENT, dtype=torch.uint8, device=dev)
+    rc = lib.floor_gather_rows(y.data_ptr(), E * C, H, bufs.token_slot.data_ptr(), wt.data_ptr(), T, k,
+                               out.data_ptr(), s)
+    assert rc == 0
+    torch.cuda.synchronize()
+    yh = y.cpu().numpy().view(np.uint32).reshape(E * C, -1, 4)
+    oh = out.cpu().numpy().view(np.uint32).reshape(T, -1, 4)
+    wb = wt.cpu().numpy().view(np.uint32)
+    for t in range(T):
+        want = np.zeros_like(oh[t])
+        want[:, 0] = np.bitwise_xor.reduce(wb[t])
+        for j in range(k):
+            want ^= yh[slots[t, j]]
+        np.testing.assert_array_equal(oh[t], want)
