@@ -116,3 +116,52 @@ def test_noalloc_refuses_batches_beyond_its_scratch(dev):
     assert err.value.status == moe.binding.MOE_ERR_SCRATCH
     torch.cuda.synchronize()
     assert int((bufs.token_slot != -7).sum()) == 0, "a refused call must enqueue nothing"
+
+
+@pytest.mark.parametrize("T,H,E,k,fp8", [(2048, 512, 8, 2, False), (1000, 256, 64, 8, True)])
+def test_noalloc_graph_replays(dev, T, H, E, k, fp8):
+    """The case the entry point exists for: route + dispatch captured in a
+    HIP graph with no workspace to allocate, replayed several times.  Between
+    replays an eager call on a different batch overwrites the library's
+    scratch; every replay must still reproduce the eager outputs bit for bit
+    (nothing in the scratch is carried from one call to the next)."""
+    say(f"[noalloc graph] T={T} H={H} E={E} k={k} fp8={fp8}")
+    logits, x = _inputs(T, H, E, 21, dev)
+    other_l, other_x = _inputs(3000, 128, 16, 22, dev)
+    C = T
+    bufs = moe.DispatchBuffers.allocate(T, H, E, k, C, fp8, dev, workspace=False)
+    idx = torch.empty(T, k, dtype=torch.int32, device=dev)
+    wt = torch.empty(T, k, dtype=torch.float32, device=dev)
+    side = torch.cuda.Stream()
+    outs = (idx, wt, bufs.expert_counts, bufs.token_slot, bufs.recv_src)
+
+    def clear():
+        for t in outs:
+            t.zero_()
+
+    clear()
+    torch.cuda.synchronize()
+    moe.moe_route_dispatch_noalloc(logits, x, k, C, fp8=fp8, bufs=bufs, topk_idx=idx, topk_w=wt, stream=side)
+    side.synchronize()
+    ref = [t.clone() for t in outs]
+    rows = _filled_rows(bufs, bufs.expert_counts.cpu(), C, H)
+    ref_rows = bufs.recv_x.view(E * C, -1).index_select(0, rows).clone()
+    r_idx, r_w, r_bufs = moe.moe_route_dispatch(logits, x, k, C, fp8=fp8)
+    torch.cuda.synchronize()
+    _same(ref[0], r_idx, "topk_idx")
+    _same(ref[3], r_bufs.token_slot, "token_slot")
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        moe.moe_route_dispatch_noalloc(logits, x, k, C, fp8=fp8, bufs=bufs, topk_idx=idx, topk_w=wt, stream=side)
+    for rep in range(4):
+        clear()
+        bufs.recv_x.view(torch.uint8)[0].fill_(0)
+        moe.moe_route_dispatch_noalloc(other_l, other_x, 4, 3000)      # eager, different batch: scratch reused
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(ref, outs):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {rep} differs"
+        got_rows = bufs.recv_x.view(E * C, -1).index_select(0, rows)
+        assert torch.equal(got_rows.view(torch.uint8), ref_rows.view(torch.uint8)), f"replay {rep} rows differ"
