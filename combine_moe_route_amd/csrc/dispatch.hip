@@ -71,6 +71,53 @@ __host__ __device__ constexpr int local_words(int64_t T)
 }
 __host__ __device__ constexpr int local_stride(int nw) { return nw | 1; }
 
+// Sum of v over aligned groups of g lanes (g a power of two, 1 .. 64), in
+// every lane of the group; every lane of the wave must be active.  Up to 16
+// lanes the partial sums move by DPP inside a 16-lane row (lane xor 1,
+// xor 2, then the half-row mirror i <- 7 - i and the row mirror
+// i <- 15 - i, which pair each lane with one of the other half); wider
+// groups add cross-row shuffles.  Integer sums are exact in any order.
+template <int CTRL>
+__device__ __forceinline__ int dpp_int(int v)
+{
+    return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ int group_sum(int v, int g)
+{
+    if (g > 1)
+        v += dpp_int<0xB1>(v);    // quad_perm [1,0,3,2]
+    if (g > 2)
+        v += dpp_int<0x4E>(v);    // quad_perm [2,3,0,1]
+    if (g > 4)
+        v += dpp_int<0x141>(v);   // row_half_mirror
+    if (g > 8)
+        v += dpp_int<0x140>(v);   // row_mirror
+    if (g > 16)
+        v += __shfl_xor(v, 16);
+    if (g > 32)
+        v += __shfl_xor(v, 32);
+    return v;
+}
+
+// p / k for 0 <= p < 4096 and 1 <= k <= 16 as (p * ceil(2^16 / k)) >> 16:
+// the multiplier overshoots 2^16 / k by less than 1, which adds less than
+// p / 2^16 < 1/16 to p / k, and the fraction of p / k is at most
+// (k - 1) / k, so the floor is unchanged while 4095 (k - 1) < 2^16.
+__host__ __device__ constexpr uint32_t small_div_mul(int k) { return (65536u + (uint32_t)k - 1u) / (uint32_t)k; }
+__host__ __device__ constexpr int small_div(int p, uint32_t mul) { return (int)(((uint32_t)p * mul) >> 16); }
+constexpr bool small_div_exact(int k)
+{
+    for (int p = 0; p < 4096; ++p)
+        if (small_div(p, small_div_mul(k)) != p / k)
+            return false;
+    return true;
+}
+static_assert(small_div_exact(1) && small_div_exact(2) && small_div_exact(3) && small_div_exact(4) &&
+              small_div_exact(5) && small_div_exact(6) && small_div_exact(7) && small_div_exact(8) &&
+              small_div_exact(9) && small_div_exact(10) && small_div_exact(11) && small_div_exact(12) &&
+              small_div_exact(13) && small_div_exact(14) && small_div_exact(15) && small_div_exact(16),
+              "multiply-shift division is exact for every pair index of a local batch");
+
 // Exclusive scan of the work-group's n <= 4*256 values in LDS (thread i owns
 // values 4i .. 4i+3): out[i] = sum of in[0 .. i-1] for i < n, out[n] = total.
 // out may be in: a thread reads its own values before the barrier and
@@ -333,8 +380,9 @@ __device__ __forceinline__ void store_stream(float *p, float v) { __builtin_nont
 // row loads (local_ids_load): vector loads retire in order, so waiting for
 // ids issued after the rows would wait for the rows too.  lds: [E][nw | 1] mask
 // words, then for the packed layout [E+1] offsets (the exclusive scan of the
-// popcounts).  Work-group 0 publishes the totals (or offsets).  All threads
-// must call both.
+// popcounts).  The totals are published by the work-groups in turn (expert e
+// by work-group e mod gridDim.x); work-group 0 publishes the offsets.  All
+// threads must call both.
 constexpr int kLocalIds = kChunk * 16 / kBlock;   // ids per thread: T*k <= 256 * MOE_MAX_TOPK
 
 // The single-chunk loads are issued unconditionally, from a clamped
@@ -351,25 +399,33 @@ __device__ __forceinline__ void local_ids_load(const int32_t *__restrict__ topk_
     }
 }
 
-// The chunk's per-expert totals from its complete LDS masks: work-group 0
-// writes them (fixed slots), or every work-group scans them into loffs and
-// work-group 0 writes the offsets (packed layout).  All threads call it.
+// The chunk's per-expert totals from its complete LDS masks: each work-group
+// writes those of the experts e with e mod gridDim.x == blockIdx.x (fixed
+// slots; no work-group pays for all E), or every work-group scans them into
+// loffs and work-group 0 writes the offsets (packed layout).  All threads
+// call it.
 __device__ __forceinline__ void local_totals(int E, int nw, int ns, bool packed, const uint32_t *lmask, int32_t *loffs,
                                              int32_t *wave_sums, int32_t *__restrict__ expert_counts,
                                              int32_t *__restrict__ expert_offsets)
 {
     const int tid = threadIdx.x;
+    if (!packed) {   // expert e's total is written by work-group e mod gridDim.x
+        for (int e = (int)blockIdx.x + tid * (int)gridDim.x; e < E; e += kBlock * (int)gridDim.x) {
+            int n = 0;
+            for (int w = 0; w < nw; ++w)
+                n += __popc(lmask[e * ns + w]);
+            expert_counts[e] = n;
+        }
+        return;
+    }
     for (int e = tid; e < E; e += kBlock) {
         int n = 0;
 #pragma unroll
         for (int w = 0; w < nw; ++w)
             n += __popc(lmask[e * ns + w]);
-        if (packed)
-            loffs[e] = n;
-        else if (blockIdx.x == 0)
-            expert_counts[e] = n;
+        loffs[e] = n;
     }
-    if (packed) {
+    {
         __syncthreads();
         block_exclusive_scan(loffs, E, loffs, wave_sums);   // in place: each thread rewrites only what it read
         __syncthreads();
@@ -386,6 +442,7 @@ __device__ __forceinline__ void local_chunk_counts(const int (&ids)[kLocalIds], 
                                                    int32_t *__restrict__ expert_offsets)
 {
     const int tid = threadIdx.x;
+    const uint32_t kmul = small_div_mul(k);
     for (int i = tid; i < E * ns; i += kBlock)
         lmask[i] = 0u;
     __syncthreads();
@@ -393,7 +450,7 @@ __device__ __forceinline__ void local_chunk_counts(const int (&ids)[kLocalIds], 
     for (int q = 0; q < kLocalIds; ++q) {
         const int e = ids[q];   // pair p = tid + q*256 of token p / k; -1 past the end
         if ((unsigned)e < (unsigned)E) {
-            const int tok = (tid + q * kBlock) / k;
+            const int tok = small_div(tid + q * kBlock, kmul);
             atomicOr(&lmask[e * ns + (tok >> 5)], 1u << (tok & 31));
         }
     }
@@ -406,7 +463,7 @@ __device__ __forceinline__ void local_chunk_counts(const int (&ids)[kLocalIds], 
 // groups, 32 tokens per pass, the router's own selection and softmax code,
 // so the choices and weights are those of moe_route_topk bit for bit --
 // keeping the choices in LDS (ids and membership masks); work-group 0 also
-// stores ids, weights and totals.  A lane's logits for all passes are
+// stores ids and weights, and the totals are spread as in local_totals.  A lane's logits for all passes are
 // requested before the row loads, for the reason given at local_ids_load.
 constexpr int kRoutePasses = kChunk / kMaskChunk;   // 8 passes of 32 tokens
 
@@ -595,11 +652,12 @@ __device__ __forceinline__ int wave_slot(PairIds pre, const int32_t *__restrict_
         if ((unsigned)e < (unsigned)E) {
             if (offs)
                 base = loffs ? loffs[e] : offs[e];
-            if (lmask) {
+            if (lmask) {   // the earlier words' popcounts, spread over the pair's lanes
                 const int word = (int)t >> 5;
-                r = __popc(lmask[e * ns + word] & ((1u << ((int)t & 31)) - 1u));
-                for (int w = 0; w < word; ++w)
-                    r += __popc(lmask[e * ns + w]);
+                const uint32_t *row = lmask + e * ns;
+                r = __popc(row[word] & ((1u << ((int)t & 31)) - 1u));
+                for (int w = sub; w < word; w += lanes_per_pair)
+                    sum += __popc(row[w]);
             } else if (masks) {
                 const uint32_t *row = masks + (int64_t)e * nchunks;
                 r = __popc(row[c] & ((1u << (int)(t % kMaskChunk)) - 1u));
@@ -636,8 +694,7 @@ __device__ __forceinline__ int wave_slot(PairIds pre, const int32_t *__restrict_
             }
         }
     }
-    for (int o = lanes_per_pair / 2; o > 0; o >>= 1)
-        sum += __shfl_xor(sum, o);
+    sum = group_sum(sum, lanes_per_pair);
     int slot = -1;
     if (j < k && (unsigned)e < (unsigned)E && r >= 0) {
         if (offs)
