@@ -36,12 +36,14 @@ __device__ __forceinline__ float lane_value(float v, int l)
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
 
-// Two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+// Two floats -> packed bf16 pair (lo in the low half), round to nearest
+// even: one v_cvt_pk_bf16_f32 with both operands (two scalar casts compile
+// to two conversions plus a shift and an OR).
+typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
-    __bf16 a = (__bf16)lo;
-    __bf16 b = (__bf16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((float2_t){lo, hi}, bf16x2_t));
 }
 
 }  // namespace moe

@@ -98,6 +98,27 @@ def test_every_k(dev, E, T):
         _check(f"E={E} k={k}", logits, x, k, T, k % 2 == 1, fused, separate)
 
 
+@pytest.mark.parametrize("T", [200, 480, 3000])
+def test_every_k_counted_in_pack_and_by_chunks(dev, T):
+    """E > 8, every k from 1 to 16: the lanes owning one pair (64, 32, 16, 8
+    or 4 of them) sum the pair's earlier counts together.  T = 200: the batch
+    is counted inside pack; T = 480: inside pack up to k = 8 (T*k <= 4096
+    ids), by the count launch beyond; T = 3000: by 256-token chunks.  Odd k
+    overflow the capacity.  The packed layout is checked on the same
+    inputs."""
+    E, H = 24, 128
+    rng = np.random.default_rng(7000 + T)
+    x = W.bits(torch.from_numpy(rng.standard_normal((T, H)).astype(np.float32)).to(torch.bfloat16))
+    for k in range(1, 17):
+        logits = rng.integers(-2, 3, (T, E)).astype(np.float32)     # ties everywhere
+        C = T if k % 2 == 0 else max(1, T * k // E // 2)
+        fp8 = k % 4 == 1
+        fused, separate = _run_both(dev, logits, x, k, C, fp8)
+        _check(f"k={k}", logits, x, k, C, fp8, fused, separate)
+        fused, separate = _run_both_packed(dev, logits, x, k, fp8)
+        _check_packed(f"k={k}", logits, x, k, fp8, fused, separate)
+
+
 @pytest.mark.parametrize("T,C", [(3000, 300), (200, 20)])
 def test_capacity_overflow(dev, T, C):
     rng = np.random.default_rng(9 + T)
