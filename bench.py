@@ -27,6 +27,8 @@ Prints one JSON line (stdout):
   roofline  the dominant kernel (combine): algorithmic bytes per launch over
             its mean launch time, from HIP events recorded on the launch
             stream around every combine call of the timing pass
+  roofline_dispatch  the same for the dispatch call (count + pack launches,
+            or route + pack for the one-call path)
   cpu_baseline  the CPU oracle on a bounded sample of the same workload, on
             the host's cores (threads over tokens for route, pack and
             combine; slot assignment serial) and on one thread
@@ -647,6 +649,15 @@ def main() -> int:
             "timing": "HIP events recorded on the launch stream around every combine call of a timing pass run "
                       "after the (event-free) headline region",
         },
+    }
+    # the other HBM-bound call of the step, timed the same way
+    dname = "dispatch" if "dispatch" in head["kernels"] else "route_dispatch"
+    disp = head["kernels"][dname]
+    result["roofline_dispatch"] = {
+        "kernel": f"{disp['call']}; profiles/{w.name}_kernel_trace.md names the kernel instances",
+        "bound": "hbm", "achieved": disp["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": disp["frac"],
+        "algorithmic_bytes_per_launch": disp["bytes"], "mean_launch_us": disp["mean_us"],
+        "median_launch_us": disp["median_us"], "timed_launches": disp["launches"],
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, epilogue)
