@@ -385,6 +385,21 @@ __device__ __forceinline__ void store_stream(float *p, float v) { __builtin_nont
 // threads must call both.
 constexpr int kLocalIds = kChunk * 16 / kBlock;   // ids per thread: T*k <= 256 * MOE_MAX_TOPK
 
+// Whether pack counts the batch itself: one chunk, or up to 512 tokens whose
+// ids fit kLocalIds per thread and whose masks are at most 4096 words (every
+// work-group clears, fills and popcounts the masks, which past that costs
+// more than the count launch it saves).
+__host__ __device__ constexpr bool local_count(int64_t T, int E, int k)
+{
+    return T <= kChunk ||
+           (T <= kLocalTokens && T * k <= (int64_t)kLocalIds * kBlock && (int64_t)E * local_words(T) <= 4096);
+}
+
+// For E > 8, the router's membership words replace the count launch while a
+// pair's prefix (the popcounts of the earlier words of its expert) takes at
+// most this many L2 loads per lane.
+constexpr int kHalfMaskLoads = 32;
+
 // The single-chunk loads are issued unconditionally, from a clamped
 // (in-bounds) index, and unwanted values discarded afterwards: a load under a
 // branch makes the compiler wait for every outstanding load before the first
@@ -1127,12 +1142,8 @@ hipError_t launch_dispatch(const uint16_t *x, int64_t T, int H, const int32_t *t
     if (!dispatch_grid_fits(T, H, k, dtype))   // before anything is enqueued
         return hipErrorInvalidConfiguration;
     const int nchunks = (int)((T + kChunk - 1) / kChunk);
-    // one chunk, or up to 512 tokens whose ids fit kLocalIds per thread and
-    // whose masks are at most 4096 words: pack counts the whole batch itself,
-    // no count launch (every work-group clears, fills and popcounts the
-    // masks, which past that costs more than the launch it saves)
-    if (T <= kChunk ||
-        (T <= kLocalTokens && T * k <= (int64_t)kLocalIds * kBlock && (int64_t)E * local_words(T) <= 4096))
+    // pack counts the whole batch itself, no count launch
+    if (local_count(T, E, k))
         return launch_pack(x, T, H, topk_idx, nullptr, nullptr, nullptr, expert_offsets, E, k, C, 1, dtype, recv_x,
                            recv_scales, recv_src, expert_counts, token_slot, s, kPackLocalIds);
     int32_t *chunk_counts = (int32_t *)workspace;
@@ -1200,6 +1211,19 @@ hipError_t launch_route_dispatch(const float *logits, int64_t T, int E, int k, c
         return launch_pack(x, T, H, topk_idx, nullptr, nullptr, masks, expert_offsets, E, k, C, (int)nmask, dtype,
                            recv_x, recv_scales, recv_src, expert_offsets ? nullptr : expert_counts, token_slot, s,
                            own_offsets ? kPackMaskOffsets : kPackChunks);
+    }
+    // E > 8, fixed slots, a batch past the in-pack count with few enough
+    // membership words: the router writes the words a 16-token half per
+    // work-group and pack derives the slots from them, as for E <= 8 (two
+    // launches instead of three).
+    if (E > 8 && !expert_offsets && !local_count(T, E, k) && nmask <= kHalfMaskLoads * (int64_t)lpp &&
+        (size_t)E * nmask * 4 <= dispatch_workspace_bytes(T, E, k)) {
+        uint32_t *masks = (uint32_t *)workspace;
+        hipError_t e = launch_route_topk_half_masks(logits, T, E, k, topk_idx, topk_w, masks, s);
+        if (e != hipSuccess)
+            return e;
+        return launch_pack(x, T, H, topk_idx, nullptr, nullptr, masks, nullptr, E, k, C, (int)nmask, dtype, recv_x,
+                           recv_scales, recv_src, expert_counts, token_slot, s, kPackChunks);
     }
     hipError_t e = launch_route_topk(logits, T, E, k, topk_idx, topk_w, s);
     if (e != hipSuccess)

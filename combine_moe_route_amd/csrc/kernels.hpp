@@ -16,6 +16,12 @@ hipError_t launch_route_topk(const float *logits, int64_t T, int E, int k, int32
 hipError_t launch_route_topk_masks(const float *logits, int64_t T, int E, int k, int32_t *idx, float *w,
                                    uint32_t *masks, hipStream_t s);
 
+// Router top-k for E > 8 that also writes the same 32-token membership
+// words, a 16-token half per work-group (weights identical to
+// launch_route_topk's).
+hipError_t launch_route_topk_half_masks(const float *logits, int64_t T, int E, int k, int32_t *idx, float *w,
+                                        uint32_t *masks, hipStream_t s);
+
 // Route + dispatch in one call; the workspace is dispatch_workspace_bytes(T,
 // E, k).  expert_offsets != NULL selects the packed layout (C and
 // expert_counts unused), otherwise fixed slots of C rows per expert.

@@ -83,6 +83,47 @@ __global__ __launch_bounds__(kBlock) void route_topk_mask_kernel(const float *__
         masks[(int64_t)threadIdx.x * nchunks + blockIdx.x] = smask[threadIdx.x];
 }
 
+// Router top-k for E > 8 with the dispatch count step folded in, as above:
+// a work-group routes 16 tokens with the plain router's lane layout for this
+// E and T (so the weights are the same bits) and writes, for every expert,
+// the 16-bit half of the 32-token membership word that covers its tokens
+// (bit b of word c: token 32c + b chose e).  Each half is written by exactly
+// one work-group, and when the halves are odd in number the last
+// work-group also clears the unused upper half of the final word, so the
+// words need no clearing beforehand and no global atomics.
+constexpr int kHalfTokens = 16;
+
+template <int G, int VPL, bool VEC>
+__global__ __launch_bounds__(kHalfTokens * kWave) void route_topk_half_mask_kernel(
+    const float *__restrict__ logits, int64_t T, int E, int k, int32_t *__restrict__ topk_idx,
+    float *__restrict__ topk_w, uint16_t *__restrict__ half_masks, int nwords)
+{
+    extern __shared__ uint32_t hmask[];   // [E]
+    for (int e = threadIdx.x; e < E; e += blockDim.x)
+        hmask[e] = 0u;
+    __syncthreads();
+    const int lane = lane_id();
+    const int tl = (int)threadIdx.x / G;   // the work-group's token, 0 .. 15
+    const int64_t t = (int64_t)blockIdx.x * kHalfTokens + tl;
+    const bool active = t < T;
+    float v[VPL];
+    uint32_t key[VPL];
+    load_logits<VPL, VEC>(logits, t, active, E, lane % G, v, key);
+    const int my_e = select_and_store<G, VPL>(v, key, active, t, E, k, topk_idx, topk_w);
+    if (active && lane % G < k && (unsigned)my_e < (unsigned)E)
+        atomicOr(&hmask[my_e], 1u << tl);
+    __syncthreads();
+    const int64_t word = blockIdx.x >> 1;
+    const int half = (int)(blockIdx.x & 1);
+    const bool clear_upper = half == 0 && blockIdx.x == gridDim.x - 1;
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        uint16_t *p = half_masks + ((int64_t)e * nwords + word) * 2;
+        p[half] = (uint16_t)hmask[e];
+        if (clear_upper)
+            p[1] = 0;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Group-limited ("node-limited") selection.  Handbook "NVSHMEM and DeepEP",
 // "High-throughput mode": each node (here: a group of E/n_groups consecutive
@@ -333,26 +374,76 @@ hipError_t launch_route_topk_masks(const float *logits, int64_t T, int E, int k,
     return hipGetLastError();
 }
 
+namespace {
+
+// The router's lane layout for E experts and T tokens: G lanes per token,
+// VPL logits per lane.  Every router launch takes it from here, so a token's
+// weights (whose softmax sum runs over that layout) are the same bits
+// whichever router kernel routes it.  Above 32 experts: four tokens per wave
+// (16-lane groups) when there are enough tokens to fill the chip that way,
+// else one token per wave (measured on MI355X at E = 256: 16-lane groups win
+// from ~6000 tokens, 10.7 vs 14.1 us at 16384; one wave per token wins
+// below, 3.5 vs 5.6 us at 128).
+template <class F>
+hipError_t with_router_shape(int64_t T, int E, F &&f)
+{
+    if (E <= 1) return f.template run<1, 1>();
+    if (E <= 2) return f.template run<2, 1>();
+    if (E <= 4) return f.template run<4, 1>();
+    if (E <= 8) return f.template run<8, 1>();
+    if (E <= 16) return f.template run<16, 1>();
+    if (E <= 32) return f.template run<32, 1>();
+    const bool wide = T >= 6144;
+    if (E <= 64) return wide ? f.template run<16, 4>() : f.template run<64, 1>();
+    if (E <= 128) return wide ? f.template run<16, 8>() : f.template run<64, 2>();
+    if (E <= 256) return wide ? f.template run<16, 16>() : f.template run<64, 4>();
+    if (E <= 512) return f.template run<64, 8>();
+    return f.template run<64, 16>();
+}
+
+struct PlainRouter {
+    const float *logits; int64_t T; int E, k; int32_t *idx; float *w; hipStream_t s;
+    template <int G, int VPL>
+    hipError_t run() { return launch<G, VPL>(logits, T, E, k, idx, w, s); }
+};
+
+struct HalfMaskRouter {
+    const float *logits; int64_t T; int E, k; int32_t *idx; float *w; uint16_t *half_masks; hipStream_t s;
+    template <int G, int VPL>
+    hipError_t run()
+    {
+        if (G < 16)   // E <= 8 has its own word-per-work-group kernel
+            return hipErrorInvalidValue;
+        const int64_t blocks = (T + kHalfTokens - 1) / kHalfTokens;
+        const int nwords = (int)((T + kMaskChunk - 1) / kMaskChunk);
+        const bool vec = VPL > 1 && E % VPL == 0 && (VPL == 2 ? ((uintptr_t)logits % 8 == 0)
+                                                               : (E % 4 == 0 && (uintptr_t)logits % 16 == 0));
+        const dim3 grid((unsigned)blocks), block(kHalfTokens * G);
+        const size_t lds = (size_t)E * 4;
+        if (vec)
+            hipLaunchKernelGGL((route_topk_half_mask_kernel<G, VPL, true>), grid, block, lds, s, logits, T, E, k,
+                               idx, w, half_masks, nwords);
+        else
+            hipLaunchKernelGGL((route_topk_half_mask_kernel<G, VPL, false>), grid, block, lds, s, logits, T, E, k,
+                               idx, w, half_masks, nwords);
+        return hipGetLastError();
+    }
+};
+
+}  // namespace
+
 hipError_t launch_route_topk(const float *logits, int64_t T, int E, int k, int32_t *idx, float *w,
                              hipStream_t s)
 {
-    if (E <= 1) return launch<1, 1>(logits, T, E, k, idx, w, s);
-    if (E <= 2) return launch<2, 1>(logits, T, E, k, idx, w, s);
-    if (E <= 4) return launch<4, 1>(logits, T, E, k, idx, w, s);
-    if (E <= 8) return launch<8, 1>(logits, T, E, k, idx, w, s);
-    if (E <= 16) return launch<16, 1>(logits, T, E, k, idx, w, s);
-    if (E <= 32) return launch<32, 1>(logits, T, E, k, idx, w, s);
-    // above 32 experts: four tokens per wave (16-lane groups) when there are
-    // enough tokens to fill the chip that way, else one token per wave
-    // (measured on MI355X at E = 256: 16-lane groups win from ~6000 tokens,
-    // 10.7 vs 14.1 us at 16384; one wave per token wins below, 3.5 vs 5.6 us
-    // at 128)
-    const bool wide = T >= 6144;
-    if (E <= 64) return wide ? launch<16, 4>(logits, T, E, k, idx, w, s) : launch<64, 1>(logits, T, E, k, idx, w, s);
-    if (E <= 128) return wide ? launch<16, 8>(logits, T, E, k, idx, w, s) : launch<64, 2>(logits, T, E, k, idx, w, s);
-    if (E <= 256) return wide ? launch<16, 16>(logits, T, E, k, idx, w, s) : launch<64, 4>(logits, T, E, k, idx, w, s);
-    if (E <= 512) return launch<64, 8>(logits, T, E, k, idx, w, s);
-    return launch<64, 16>(logits, T, E, k, idx, w, s);
+    return with_router_shape(T, E, PlainRouter{logits, T, E, k, idx, w, s});
+}
+
+hipError_t launch_route_topk_half_masks(const float *logits, int64_t T, int E, int k, int32_t *idx, float *w,
+                                        uint32_t *masks, hipStream_t s)
+{
+    if (E <= 8)
+        return hipErrorInvalidValue;
+    return with_router_shape(T, E, HalfMaskRouter{logits, T, E, k, idx, w, (uint16_t *)masks, s});
 }
 
 }  // namespace moe

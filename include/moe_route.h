@@ -199,9 +199,14 @@ MOE_API int moe_dispatch(const uint16_t *x, int64_t T, int32_t H, const int32_t 
  * pack derives counts, prefixes and ranks from those words, so the call is
  * two kernel launches instead of three.  With E <= 8 and at most 256 tokens
  * it is one launch: every pack work-group routes the whole batch itself with
- * the router's own code.  Larger E, or more than 2048 * (64 / p) tokens
- * (p = k rounded up to a power of two), use route, count and pack, with a
- * scan of the per-chunk counts before the pack past 65536 tokens.
+ * the router's own code.  E <= 8 with more than 2048 * (64 / p) tokens
+ * (p = k rounded up to a power of two) uses route, count and pack.  For
+ * E > 8, batches the pack cannot count itself (above 256 or 512 tokens) but
+ * of at most 1024 * (64 / p) tokens take the same two-launch path, a
+ * work-group of the router writing a 16-token half of each word, when the
+ * words (E * ceil(T/32) * 4 bytes) fit the workspace; otherwise route, count
+ * and pack, with a scan of the per-chunk counts before the pack past 65536
+ * tokens.
  *
  *   logits, T, E, k, topk_idx, topk_w: as for moe_route_topk
  *   x, H, capacity, out_dtype, recv_x, recv_scales, recv_src, expert_counts,

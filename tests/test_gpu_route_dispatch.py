@@ -1,11 +1,14 @@
 """GPU parity of moe_route_dispatch (router top-k and fixed-slot dispatch in
-one call; for E <= 8 the count step is folded into the router kernel as
-32-token membership words), through the C ABI.
+one call; for E <= 8, and for E > 8 at moderate batch sizes, the count step
+is folded into the router kernel as 32-token membership words), through the
+C ABI.
 
 Every output must equal the CPU oracle (ids, counts, slots, sources, rows
 bit for bit; weights within the router tolerance) and must be bit-identical
 to the separate moe_route_topk + moe_dispatch calls.  Cases: the five
 workloads (E = 8 on the fused path, E = 128 and 256 on the three-step path),
+E > 8 on the router-words path (every router lane layout, the 16-token
+halves, the load limit on both sides),
 token counts around the 32-token word and 256-token chunk boundaries, every
 E <= 8 with every k, capacity overflow, fp8 rows, and token counts past the
 fused path's limit; batches of at most 256 tokens with E <= 8 take a single
@@ -96,6 +99,32 @@ def test_every_k(dev, E, T):
         logits = rng.integers(-2, 3, (T, E)).astype(np.float32)     # ties everywhere
         fused, separate = _run_both(dev, logits, x, k, T, k % 2 == 1 and H % 128 == 0)
         _check(f"E={E} k={k}", logits, x, k, T, k % 2 == 1, fused, separate)
+
+
+@pytest.mark.parametrize("T,E,k,fp8,C", [
+    (513, 9, 1, False, 513),      # 16-lane groups, 9 of 16 lanes real; 33 halves (the last word's upper half cleared)
+    (1000, 16, 2, True, 1000),    # 16-lane groups; 63 halves
+    (1007, 24, 3, False, 90),     # 32-lane groups; 63 halves; capacity overflow
+    (1040, 64, 8, False, 1040),   # one token per wave, one logit per lane; 65 halves
+    (2049, 100, 6, True, 2049),   # one token per wave, two logits per lane; 129 halves
+    (3000, 256, 8, False, 3000),  # one token per wave, four logits per lane
+    (700, 300, 10, False, 700),   # eight logits per lane, E not a multiple of them (scalar loads)
+    (6145, 64, 2, False, 150),    # four tokens per wave (16-lane groups, four logits per lane); 385 halves; overflow
+    (8192, 256, 8, True, 8192),   # the last size whose prefix stays within 32 loads per lane
+    (8193, 256, 8, False, 8193),  # one token more: route, count and pack
+])
+def test_router_words_for_more_than_8_experts(dev, T, E, k, fp8, C):
+    """E > 8 past the in-pack count: the router writes each expert's 32-token
+    membership words a 16-token half per work-group, in the plain router's
+    lane layout for that E and T, and pack takes counts, prefixes and ranks
+    from them.  Outputs must equal the oracle and the separate calls bit for
+    bit (the weights too, since both calls route with the same layout)."""
+    rng = np.random.default_rng(9000 + T + E + k)
+    H = 256
+    logits = rng.integers(-3, 4, (T, E)).astype(np.float32) + rng.standard_normal((T, E)).astype(np.float32) * 0.25
+    x = W.bits(torch.from_numpy(rng.standard_normal((T, H)).astype(np.float32)).to(torch.bfloat16))
+    fused, separate = _run_both(dev, logits, x, k, C, fp8)
+    _check(f"E={E} k={k}", logits, x, k, C, fp8, fused, separate)
 
 
 @pytest.mark.parametrize("T", [200, 480, 3000])
