@@ -412,8 +412,15 @@ struct HalfMaskRouter {
     template <int G, int VPL>
     hipError_t run()
     {
-        if (G < 16)   // E <= 8 has its own word-per-work-group kernel
+        if constexpr (G < 16) {   // E <= 8 has its own word-per-work-group kernel
             return hipErrorInvalidValue;
+        } else {
+            return launch_half<G, VPL>();
+        }
+    }
+    template <int G, int VPL>
+    hipError_t launch_half()
+    {
         const int64_t blocks = (T + kHalfTokens - 1) / kHalfTokens;
         const int nwords = (int)((T + kMaskChunk - 1) / kMaskChunk);
         const bool vec = VPL > 1 && E % VPL == 0 && (VPL == 2 ? ((uintptr_t)logits % 8 == 0)
