@@ -382,8 +382,11 @@ def run_workload(w: W.Workload, args, moe, torch, dev, primary: bool) -> dict:
 
     # kernel timing pass (after the headline region, one stream): HIP events
     # recorded on the launch stream around every call.  Where moe_route_dispatch
-    # launches the same kernels as moe_route_topk + moe_dispatch (E > 8, or
-    # grouped routing), the two calls are made and timed separately.
+    # launches the same kernels as moe_route_topk + moe_dispatch, the two calls
+    # are made and timed separately: grouped routing, and E > 8 at the
+    # benchmark's sizes (decode is counted inside pack, and the prefill
+    # batches are past the size up to which the fused call's router writes
+    # membership words instead).
     bind(1)
     split = w.E > 8 or route_groups is not None or args.separate_route
     n = min(K, 200)
