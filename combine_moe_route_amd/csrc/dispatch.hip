@@ -30,7 +30,7 @@
 //           the prefix with one load.
 // A batch of at most 256 tokens is a single chunk: then there is no count
 // launch, and every pack work-group rebuilds the chunk's masks in LDS from
-// ids it requests before the rows.  Up to 512 tokens whose ids fit 16 per
+// ids it requests before the rows.  Up to 1024 tokens whose ids fit 16 per
 // thread (and whose masks are at most 4096 words) are counted the same way.
 // Route + dispatch in one call with E <= 8: the router already wrote one
 // membership word per expert and 32-token chunk, and pack takes prefixes and
@@ -60,7 +60,7 @@ constexpr int kMaskWords = kChunk / 32;
 // stride spreads them over every bank.
 constexpr int kMaskStride = kMaskWords + 1;
 constexpr int kMaskChunk = 32;       // tokens per router membership word
-constexpr int kLocalTokens = 2 * kChunk;   // pack counts the batch itself up to this many tokens
+constexpr int kLocalTokens = 4 * kChunk;   // pack counts the batch itself up to this many tokens
 constexpr int kMaxK = 16;                  // the largest k the library accepts (MOE_MAX_TOPK)
 
 // Membership words per expert kept in LDS by the pack modes that count the
@@ -375,7 +375,7 @@ __device__ __forceinline__ void store_stream(float *p, float v) { __builtin_nont
 
 // A batch of at most 256 tokens is one chunk: every pack work-group then
 // rebuilds that chunk's membership masks from the ids itself (T*k ids, read
-// from L2), so no count launch is needed; up to 512 tokens are counted the
+// from L2), so no count launch is needed; up to 1024 tokens are counted the
 // same way, with ceil(T/32) words per expert (local_words).  The ids are requested before the
 // row loads (local_ids_load): vector loads retire in order, so waiting for
 // ids issued after the rows would wait for the rows too.  lds: [E][nw | 1] mask
@@ -385,7 +385,7 @@ __device__ __forceinline__ void store_stream(float *p, float v) { __builtin_nont
 // threads must call both.
 constexpr int kLocalIds = kChunk * 16 / kBlock;   // ids per thread: T*k <= 256 * MOE_MAX_TOPK
 
-// Whether pack counts the batch itself: one chunk, or up to 512 tokens whose
+// Whether pack counts the batch itself: one chunk, or up to 1024 tokens whose
 // ids fit kLocalIds per thread and whose masks are at most 4096 words (every
 // work-group clears, fills and popcounts the masks, which past that costs
 // more than the count launch it saves).

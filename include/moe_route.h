@@ -201,7 +201,7 @@ MOE_API int moe_dispatch(const uint16_t *x, int64_t T, int32_t H, const int32_t 
  * it is one launch: every pack work-group routes the whole batch itself with
  * the router's own code.  E <= 8 with more than 2048 * (64 / p) tokens
  * (p = k rounded up to a power of two) uses route, count and pack.  For
- * E > 8, batches the pack cannot count itself (above 256 or 512 tokens) but
+ * E > 8, batches the pack cannot count itself (above 256 or 1024 tokens) but
  * of at most 1024 * (64 / p) tokens take the same two-launch path, a
  * work-group of the router writing a 16-token half of each word, when the
  * words (E * ceil(T/32) * 4 bytes) fit the workspace; otherwise route, count

@@ -102,9 +102,9 @@ def test_every_k(dev, E, T):
 
 
 @pytest.mark.parametrize("T,E,k,fp8,C", [
-    (513, 9, 1, False, 513),      # 16-lane groups, 9 of 16 lanes real; 33 halves (the last word's upper half cleared)
-    (1000, 16, 2, True, 1000),    # 16-lane groups; 63 halves
-    (1007, 24, 3, False, 90),     # 32-lane groups; 63 halves; capacity overflow
+    (1025, 9, 1, False, 1025),    # 16-lane groups, 9 of 16 lanes real; 65 halves (the last word's upper half cleared)
+    (1031, 16, 2, True, 1031),    # 16-lane groups; 65 halves
+    (1007, 24, 5, False, 90),     # 32-lane groups; 63 halves; 5035 ids, too many to count inside pack; overflow
     (1040, 64, 8, False, 1040),   # one token per wave, one logit per lane; 65 halves
     (2049, 100, 6, True, 2049),   # one token per wave, two logits per lane; 129 halves
     (3000, 256, 8, False, 3000),  # one token per wave, four logits per lane
@@ -114,7 +114,8 @@ def test_every_k(dev, E, T):
     (8193, 256, 8, False, 8193),  # one token more: route, count and pack
 ])
 def test_router_words_for_more_than_8_experts(dev, T, E, k, fp8, C):
-    """E > 8 past the in-pack count: the router writes each expert's 32-token
+    """E > 8 past the in-pack count (more than 1024 tokens, or more than 4096
+    ids): the router writes each expert's 32-token
     membership words a 16-token half per work-group, in the plain router's
     lane layout for that E and T, and pack takes counts, prefixes and ranks
     from them.  Outputs must equal the oracle and the separate calls bit for
@@ -132,7 +133,8 @@ def test_every_k_counted_in_pack_and_by_chunks(dev, T):
     """E > 8, every k from 1 to 16: the lanes owning one pair (64, 32, 16, 8
     or 4 of them) sum the pair's earlier counts together.  T = 200: the batch
     is counted inside pack; T = 480: inside pack up to k = 8 (T*k <= 4096
-    ids), by the count launch beyond; T = 3000: by 256-token chunks.  Odd k
+    ids); beyond, and at T = 3000, the separate call counts with its own
+    launch (256-token chunks) and the fused call from the router's words.  Odd k
     overflow the capacity.  The packed layout is checked on the same
     inputs."""
     E, H = 24, 128
