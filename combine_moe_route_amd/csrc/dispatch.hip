@@ -395,10 +395,14 @@ __host__ __device__ constexpr bool local_count(int64_t T, int E, int k)
            (T <= kLocalTokens && T * k <= (int64_t)kLocalIds * kBlock && (int64_t)E * local_words(T) <= 4096);
 }
 
-// For E > 8, the router's membership words replace the count launch while a
-// pair's prefix (the popcounts of the earlier words of its expert) takes at
-// most this many L2 loads per lane.
-constexpr int kHalfMaskLoads = 32;
+// The router's membership words replace the count launch while a pair's
+// prefix (the popcounts of the earlier words of its expert) takes at most
+// this many L2 loads per lane: for E > 8, and for E <= 8 with k > 4 (eight
+// lanes or fewer per pair), 32; for E <= 8 with k <= 4, 64.  Measured in one
+// process against route + count + pack: at 8 experts, top-8, the words win
+// by 6% at 32 loads per lane and lose by 7-9% at 48 and 64; at top-2 they
+// still win by 1-3% at 48 and 64 loads.
+__host__ __device__ constexpr int mask_prefix_loads(int E, int k) { return E <= 8 && k <= 4 ? 64 : 32; }
 
 // The single-chunk loads are issued unconditionally, from a clamped
 // (in-bounds) index, and unwanted values discarded afterwards: a load under a
@@ -1187,16 +1191,16 @@ hipError_t launch_route_dispatch(const float *logits, int64_t T, int E, int k, c
     // pack derives the slots from them (two launches; for the packed layout
     // every pack work-group also totals the words into the offsets, or for
     // more than 2048 words one added work-group does it first).
-    // Otherwise, or when the prefix over those words would exceed 64 loads
-    // per lane: route, count (+ offsets), pack -- or for a single chunk route
-    // and a pack that counts in LDS.
+    // Otherwise, or when the prefix over those words would exceed
+    // mask_prefix_loads per lane: route, count (+ offsets), pack -- or for a
+    // batch pack can count, route and a pack that counts in LDS.
     if (E <= 8 && T <= kChunk)
         return launch_pack(x, T, H, nullptr, nullptr, nullptr, nullptr, expert_offsets, E, k, C, 1, dtype, recv_x,
                            recv_scales, recv_src, expert_offsets ? nullptr : expert_counts, token_slot, s,
                            kPackLocalRoute, logits, topk_idx, topk_w);
     const int64_t nmask = (T + kMaskChunk - 1) / kMaskChunk;
     const int lpp = pair_lanes(k);
-    if (E <= 8 && nmask <= 64 * (int64_t)lpp &&
+    if (E <= 8 && nmask <= mask_prefix_loads(E, k) * (int64_t)lpp &&
         (size_t)E * nmask * 4 <= dispatch_workspace_bytes(T, E, k)) {
         uint32_t *masks = (uint32_t *)workspace;
         hipError_t e = launch_route_topk_masks(logits, T, E, k, topk_idx, topk_w, masks, s);
@@ -1216,7 +1220,7 @@ hipError_t launch_route_dispatch(const float *logits, int64_t T, int E, int k, c
     // membership words: the router writes the words a 16-token half per
     // work-group and pack derives the slots from them, as for E <= 8 (two
     // launches instead of three).
-    if (E > 8 && !expert_offsets && !local_count(T, E, k) && nmask <= kHalfMaskLoads * (int64_t)lpp &&
+    if (E > 8 && !expert_offsets && !local_count(T, E, k) && nmask <= mask_prefix_loads(E, k) * (int64_t)lpp &&
         (size_t)E * nmask * 4 <= dispatch_workspace_bytes(T, E, k)) {
         uint32_t *masks = (uint32_t *)workspace;
         hipError_t e = launch_route_topk_half_masks(logits, T, E, k, topk_idx, topk_w, masks, s);

@@ -200,7 +200,8 @@ MOE_API int moe_dispatch(const uint16_t *x, int64_t T, int32_t H, const int32_t 
  * two kernel launches instead of three.  With E <= 8 and at most 256 tokens
  * it is one launch: every pack work-group routes the whole batch itself with
  * the router's own code.  E <= 8 with more than 2048 * (64 / p) tokens
- * (p = k rounded up to a power of two) uses route, count and pack.  For
+ * (p = k rounded up to a power of two; 1024 * (64 / p) for k > 4) uses
+ * route, count and pack.  For
  * E > 8, batches the pack cannot count itself (above 256 or 1024 tokens) but
  * of at most 1024 * (64 / p) tokens take the same two-launch path, a
  * work-group of the router writing a 16-token half of each word, when the

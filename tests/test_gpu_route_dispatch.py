@@ -150,6 +150,23 @@ def test_every_k_counted_in_pack_and_by_chunks(dev, T):
         _check_packed(f"k={k}", logits, x, k, fp8, fused, separate)
 
 
+@pytest.mark.parametrize("T,E,k", [(8192, 8, 8), (8193, 8, 8), (8192, 6, 5), (8193, 6, 5), (32768, 4, 4),
+                                   (32769, 4, 4)])
+def test_router_word_limit_by_k(dev, T, E, k):
+    """E <= 8: the router's words serve while a pair's prefix takes at most 32
+    L2 loads per lane for k > 4 (8192 tokens at eight lanes per pair) and 64
+    for k <= 4 (32768 tokens at 16 lanes): both sides of each limit, fixed
+    slots and packed layout."""
+    rng = np.random.default_rng(T + 10 * E + k)
+    H = 64
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    x = W.bits(torch.from_numpy(rng.standard_normal((T, H)).astype(np.float32)).to(torch.bfloat16))
+    fused, separate = _run_both(dev, logits, x, k, T, False)
+    _check(f"E={E} k={k}", logits, x, k, T, False, fused, separate)
+    fused, separate = _run_both_packed(dev, logits, x, k, False)
+    _check_packed(f"E={E} k={k}", logits, x, k, False, fused, separate)
+
+
 @pytest.mark.parametrize("T,C", [(3000, 300), (200, 20)])
 def test_capacity_overflow(dev, T, C):
     rng = np.random.default_rng(9 + T)
