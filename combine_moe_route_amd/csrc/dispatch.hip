@@ -31,7 +31,7 @@
 // A batch of at most 256 tokens is a single chunk: then there is no count
 // launch, and every pack work-group rebuilds the chunk's masks in LDS from
 // ids it requests before the rows.  Up to 1024 tokens whose ids fit 16 per
-// thread (and whose masks are at most 4096 words) are counted the same way.
+// thread (and whose masks are at most 8192 words) are counted the same way.
 // Route + dispatch in one call with E <= 8: the router already wrote one
 // membership word per expert and 32-token chunk, and pack takes prefixes and
 // ranks from their popcounts (no count launch either).
@@ -386,13 +386,13 @@ __device__ __forceinline__ void store_stream(float *p, float v) { __builtin_nont
 constexpr int kLocalIds = kChunk * 16 / kBlock;   // ids per thread: T*k <= 256 * MOE_MAX_TOPK
 
 // Whether pack counts the batch itself: one chunk, or up to 1024 tokens whose
-// ids fit kLocalIds per thread and whose masks are at most 4096 words (every
+// ids fit kLocalIds per thread and whose masks are at most 8192 words (every
 // work-group clears, fills and popcounts the masks, which past that costs
 // more than the count launch it saves).
 __host__ __device__ constexpr bool local_count(int64_t T, int E, int k)
 {
     return T <= kChunk ||
-           (T <= kLocalTokens && T * k <= (int64_t)kLocalIds * kBlock && (int64_t)E * local_words(T) <= 4096);
+           (T <= kLocalTokens && T * k <= (int64_t)kLocalIds * kBlock && (int64_t)E * local_words(T) <= 8192);
 }
 
 // The router's membership words replace the count launch while a pair's

@@ -159,16 +159,18 @@ def test_empty_combine_and_route(dev):
     (3000, 2056, 16, 3, 3000, False, "ties"),     # 2, ragged
     (2500, 1024, 64, 4, 2500, False, "normal"),   # 2
     (2300, 1024, 32, 1, 2300, True, "normal"),    # fp8: 2 groups per lane
-    # 257-1024 tokens counted inside pack (ids <= 4096, masks <= 4096 words), and past each limit
+    # 257-1024 tokens counted inside pack (ids <= 4096, masks <= 8192 words), and past each limit
     (300, 7168, 256, 8, 300, True, "normal"),
     (512, 2048, 64, 8, 512, False, "ties"),
     (1024, 256, 64, 4, 1024, False, "ties"),      # 4096 ids, 64 experts x 32 words: the largest local batch
     (800, 512, 128, 2, 800, True, "normal"),      # 128 experts x 25 words
     (1025, 256, 64, 4, 1025, False, "normal"),    # one token past the limit: count launch
-    (1000, 128, 130, 4, 1000, False, "zeros"),    # 130 experts x 32 words: count launch
+    (1000, 128, 130, 4, 1000, False, "zeros"),    # 130 experts x 32 words
+    (1000, 128, 257, 4, 1000, False, "ties"),     # 257 experts x 32 words: count launch
     (1024, 64, 32, 5, 300, False, "normal"),      # 5120 ids: count launch, capacity overflow
-    (500, 256, 256, 8, 500, False, "normal"),     # 256 experts x 16 words: the largest local mask
-    (500, 256, 512, 8, 500, False, "normal"),     # 512 experts x 16 words: count launch
+    (500, 256, 256, 8, 500, False, "normal"),     # 256 experts x 16 words
+    (500, 256, 512, 8, 500, False, "normal"),     # 512 experts x 16 words: the largest local mask
+    (500, 256, 520, 8, 500, False, "normal"),     # 520 experts x 16 words: count launch
     (400, 128, 1024, 8, 400, False, "zeros"),     # 1024 experts: count launch
     (1100, 64, 1024, 16, 1100, False, "normal"),  # the largest E and k together through the count launch
     (2000, 64, 1024, 16, 700, False, "ties"),     # and with ties and capacity overflow
