@@ -30,7 +30,7 @@
 //           the prefix with one load.
 // A batch of at most 256 tokens is a single chunk: then there is no count
 // launch, and every pack work-group rebuilds the chunk's masks in LDS from
-// ids it requests before the rows.  Up to 1024 tokens whose ids fit 16 per
+// ids it requests before the rows.  Up to 1024 tokens whose ids fit 32 per
 // thread (and whose masks are at most 8192 words) are counted the same way.
 // Route + dispatch in one call with E <= 8: the router already wrote one
 // membership word per expert and 32-token chunk, and pack takes prefixes and
@@ -99,15 +99,15 @@ __device__ __forceinline__ int group_sum(int v, int g)
     return v;
 }
 
-// p / k for 0 <= p < 4096 and 1 <= k <= 16 as (p * ceil(2^16 / k)) >> 16:
-// the multiplier overshoots 2^16 / k by less than 1, which adds less than
-// p / 2^16 < 1/16 to p / k, and the fraction of p / k is at most
-// (k - 1) / k, so the floor is unchanged while 4095 (k - 1) < 2^16.
-__host__ __device__ constexpr uint32_t small_div_mul(int k) { return (65536u + (uint32_t)k - 1u) / (uint32_t)k; }
-__host__ __device__ constexpr int small_div(int p, uint32_t mul) { return (int)(((uint32_t)p * mul) >> 16); }
+// p / k for 0 <= p < 8192 and 1 <= k <= 16 as (p * ceil(2^17 / k)) >> 17:
+// the multiplier overshoots 2^17 / k by less than 1, which adds less than
+// p / 2^17 to p / k, and the fraction of p / k is at most (k - 1) / k, so
+// the floor is unchanged while 8191 (k - 1) < 2^17 (p * mul < 2^30).
+__host__ __device__ constexpr uint32_t small_div_mul(int k) { return (131072u + (uint32_t)k - 1u) / (uint32_t)k; }
+__host__ __device__ constexpr int small_div(int p, uint32_t mul) { return (int)(((uint32_t)p * mul) >> 17); }
 constexpr bool small_div_exact(int k)
 {
-    for (int p = 0; p < 4096; ++p)
+    for (int p = 0; p < 8192; ++p)
         if (small_div(p, small_div_mul(k)) != p / k)
             return false;
     return true;
@@ -383,17 +383,20 @@ __device__ __forceinline__ void store_stream(float *p, float v) { __builtin_nont
 // popcounts).  The totals are published by the work-groups in turn (expert e
 // by work-group e mod gridDim.x); work-group 0 publishes the offsets.  All
 // threads must call both.
-constexpr int kLocalIds = kChunk * 16 / kBlock;   // ids per thread: T*k <= 256 * MOE_MAX_TOPK
+constexpr int kLocalIds = kChunk * 16 / kBlock;   // ids per thread: T*k <= 4096
+constexpr int kLocalIdsWide = 2 * kLocalIds;      // the wide mode's: T*k <= 8192
 
 // Whether pack counts the batch itself: one chunk, or up to 1024 tokens whose
-// ids fit kLocalIds per thread and whose masks are at most 8192 words (every
-// work-group clears, fills and popcounts the masks, which past that costs
-// more than the count launch it saves).
+// ids fit kLocalIdsWide per thread and whose masks are at most 8192 words
+// (every work-group clears, fills and popcounts the masks, which past that
+// costs more than the count launch it saves).  Past kLocalIds ids per thread
+// the pack takes its wide mode (32 id registers per thread).
 __host__ __device__ constexpr bool local_count(int64_t T, int E, int k)
 {
     return T <= kChunk ||
-           (T <= kLocalTokens && T * k <= (int64_t)kLocalIds * kBlock && (int64_t)E * local_words(T) <= 8192);
+           (T <= kLocalTokens && T * k <= (int64_t)kLocalIdsWide * kBlock && (int64_t)E * local_words(T) <= 8192);
 }
+__host__ __device__ constexpr bool local_ids_wide(int64_t T, int k) { return T * k > (int64_t)kLocalIds * kBlock; }
 
 // The router's membership words replace the count launch while a pair's
 // prefix (the popcounts of the earlier words of its expert) takes at most
@@ -408,10 +411,11 @@ __host__ __device__ constexpr int mask_prefix_loads(int E, int k) { return E <= 
 // (in-bounds) index, and unwanted values discarded afterwards: a load under a
 // branch makes the compiler wait for every outstanding load before the first
 // use, which would make the counting wait for the rows.
-__device__ __forceinline__ void local_ids_load(const int32_t *__restrict__ topk_idx, int n, int (&ids)[kLocalIds])
+template <int N>
+__device__ __forceinline__ void local_ids_load(const int32_t *__restrict__ topk_idx, int n, int (&ids)[N])
 {
 #pragma unroll
-    for (int q = 0; q < kLocalIds; ++q) {
+    for (int q = 0; q < N; ++q) {
         const int p = (int)threadIdx.x + q * kBlock;
         const int v = topk_idx[p < n ? p : n - 1];
         ids[q] = p < n ? v : -1;
@@ -454,7 +458,8 @@ __device__ __forceinline__ void local_totals(int E, int nw, int ns, bool packed,
     }
 }
 
-__device__ __forceinline__ void local_chunk_counts(const int (&ids)[kLocalIds], int E, int k, int nw, int ns,
+template <int N>
+__device__ __forceinline__ void local_chunk_counts(const int (&ids)[N], int E, int k, int nw, int ns,
                                                    bool packed,
                                                    uint32_t *lmask, int32_t *loffs, int32_t *wave_sums,
                                                    int32_t *__restrict__ expert_counts,
@@ -466,7 +471,7 @@ __device__ __forceinline__ void local_chunk_counts(const int (&ids)[kLocalIds], 
         lmask[i] = 0u;
     __syncthreads();
 #pragma unroll
-    for (int q = 0; q < kLocalIds; ++q) {
+    for (int q = 0; q < N; ++q) {
         const int e = ids[q];   // pair p = tid + q*256 of token p / k; -1 past the end
         if ((unsigned)e < (unsigned)E) {
             const int tok = small_div(tid + q * kBlock, kmul);
@@ -500,6 +505,13 @@ constexpr int kOffWords = 8;   // membership words per thread in that mode: E * 
 // Several chunks whose counts dispatch_chunk_scan_kernel has already turned
 // into per-expert exclusive prefixes: one load per pair instead of a sum.
 constexpr int kPackScanned = 4;
+// A single batch counted in LDS as kPackLocalIds, with kLocalIdsWide ids per
+// thread (4096 < T*k <= 8192).
+constexpr int kPackLocalIdsWide = 5;
+template <int MODE>
+__host__ __device__ constexpr bool local_ids_mode() { return MODE == kPackLocalIds || MODE == kPackLocalIdsWide; }
+template <int MODE>
+__host__ __device__ constexpr int local_ids_count() { return MODE == kPackLocalIdsWide ? kLocalIdsWide : kLocalIds; }
 
 // The membership words [E][nwords] as kOffWords words per thread, requested
 // before the row loads from a clamped index (see local_ids_load); words past
@@ -774,7 +786,8 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_bf16_kernel(
     u32x4 *__restrict__ recv_x, const float *__restrict__ logits, int32_t *__restrict__ route_idx,
     float *__restrict__ route_w)
 {
-    constexpr bool LOCAL = MODE == kPackLocalIds || MODE == kPackLocalRoute;
+    constexpr bool LIDS = local_ids_mode<MODE>();
+    constexpr bool LOCAL = LIDS || MODE == kPackLocalRoute;
     extern __shared__ uint32_t lds_words[];  // local counting only: masks, packed offsets, routed ids
     __shared__ int32_t wave_sums[kWavesPerBlock];
     uint32_t *lmask = LOCAL ? lds_words : nullptr;
@@ -794,10 +807,10 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_bf16_kernel(
     // Otherwise wave_slot loads the ids after the rows are requested (moving
     // them ahead was measured slower there).
     PairIds ids = {-1, -1};
-    int lids[kLocalIds];
+    int lids[local_ids_count<MODE>()];
     float rv[kRoutePasses];
     uint32_t rkey[kRoutePasses];
-    if (MODE == kPackLocalIds) {
+    if (LIDS) {
         ids = load_pair_ids(topk_idx, local_rank, active, t, k, lanes_per_pair);
         local_ids_load(topk_idx, (int)T * k, lids);
     }
@@ -819,7 +832,7 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_bf16_kernel(
         mask_words_count(mw);
     // (local counting overlaps the row loads; every thread takes part)
     int32_t *lroute = (int32_t *)(lds_words + E * ns + E + 1);   // routed ids [T][k]
-    if (MODE == kPackLocalIds)
+    if (LIDS)
         local_chunk_counts(lids, E, k, nw, ns, offs != nullptr, lds_words, (int32_t *)(lds_words + E * ns),
                            wave_sums, expert_counts, offs);
     if (MODE == kPackLocalRoute) {
@@ -874,7 +887,8 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_fp8_kernel(
     u32x4 *__restrict__ recv_x, float *__restrict__ recv_scales, const float *__restrict__ logits,
     int32_t *__restrict__ route_idx, float *__restrict__ route_w)
 {
-    constexpr bool LOCAL = MODE == kPackLocalIds || MODE == kPackLocalRoute;
+    constexpr bool LIDS = local_ids_mode<MODE>();
+    constexpr bool LOCAL = LIDS || MODE == kPackLocalRoute;
     // the wave's block scales, staged so each slot's scale segment is
     // written by one contiguous store instruction
     __shared__ float s_scale[kWavesPerBlock][VPL * 8];
@@ -895,10 +909,10 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_fp8_kernel(
     const int nblk = ngrp / 8;
     const int g0 = seg * VPL * kWave + lane;
     PairIds ids = {-1, -1};   // the same load order as the bf16 kernel
-    int lids[kLocalIds];
+    int lids[local_ids_count<MODE>()];
     float rv[kRoutePasses];
     uint32_t rkey[kRoutePasses];
-    if (MODE == kPackLocalIds) {
+    if (LIDS) {
         ids = load_pair_ids(topk_idx, local_rank, active, t, k, lanes_per_pair);
         local_ids_load(topk_idx, (int)T * k, lids);
     }
@@ -927,7 +941,7 @@ __global__ __launch_bounds__(kBlock) void dispatch_pack_fp8_kernel(
         mask_words_count(mw);
     // (local counting overlaps the row loads; every thread takes part)
     int32_t *lroute = (int32_t *)(lds_words + E * ns + E + 1);   // routed ids [T][k]
-    if (MODE == kPackLocalIds)
+    if (LIDS)
         local_chunk_counts(lids, E, k, nw, ns, offs != nullptr, lds_words, (int32_t *)(lds_words + E * ns),
                            wave_sums, expert_counts, offs);
     if (MODE == kPackLocalRoute) {
@@ -1069,6 +1083,8 @@ hipError_t launch_pack(const uint16_t *x, int64_t T, int H, const int32_t *topk_
             MOE_PACK_BF16_L(V, kPackLocalRoute);                                                                 \
         else if (mode == kPackLocalIds)                                                                          \
             MOE_PACK_BF16_L(V, kPackLocalIds);                                                                   \
+        else if (mode == kPackLocalIdsWide)                                                                      \
+            MOE_PACK_BF16_L(V, kPackLocalIdsWide);                                                               \
         else if (mode == kPackMaskOffsets)                                                                       \
             MOE_PACK_BF16_L(V, kPackMaskOffsets);                                                                \
         else if (mode == kPackScanned)                                                                           \
@@ -1097,6 +1113,8 @@ hipError_t launch_pack(const uint16_t *x, int64_t T, int H, const int32_t *topk_
             MOE_PACK_FP8_L(V, kPackLocalRoute);                                                                  \
         else if (mode == kPackLocalIds)                                                                          \
             MOE_PACK_FP8_L(V, kPackLocalIds);                                                                    \
+        else if (mode == kPackLocalIdsWide)                                                                      \
+            MOE_PACK_FP8_L(V, kPackLocalIdsWide);                                                                \
         else if (mode == kPackMaskOffsets)                                                                       \
             MOE_PACK_FP8_L(V, kPackMaskOffsets);                                                                 \
         else if (mode == kPackScanned)                                                                           \
@@ -1149,7 +1167,8 @@ hipError_t launch_dispatch(const uint16_t *x, int64_t T, int H, const int32_t *t
     // pack counts the whole batch itself, no count launch
     if (local_count(T, E, k))
         return launch_pack(x, T, H, topk_idx, nullptr, nullptr, nullptr, expert_offsets, E, k, C, 1, dtype, recv_x,
-                           recv_scales, recv_src, expert_counts, token_slot, s, kPackLocalIds);
+                           recv_scales, recv_src, expert_counts, token_slot, s,
+                           local_ids_wide(T, k) ? kPackLocalIdsWide : kPackLocalIds);
     int32_t *chunk_counts = (int32_t *)workspace;
     int32_t *local_rank =
         (int32_t *)((char *)workspace + ((int64_t)E * nchunks * 4 + 255) / 256 * 256);

@@ -159,7 +159,8 @@ def test_empty_combine_and_route(dev):
     (3000, 2056, 16, 3, 3000, False, "ties"),     # 2, ragged
     (2500, 1024, 64, 4, 2500, False, "normal"),   # 2
     (2300, 1024, 32, 1, 2300, True, "normal"),    # fp8: 2 groups per lane
-    # 257-1024 tokens counted inside pack (ids <= 4096, masks <= 8192 words), and past each limit
+    # 257-1024 tokens counted inside pack (ids <= 8192, 32 per thread past 4096; masks <= 8192 words), and past
+    # each limit
     (300, 7168, 256, 8, 300, True, "normal"),
     (512, 2048, 64, 8, 512, False, "ties"),
     (1024, 256, 64, 4, 1024, False, "ties"),      # 4096 ids, 64 experts x 32 words: the largest local batch
@@ -174,8 +175,11 @@ def test_empty_combine_and_route(dev):
     (400, 128, 1024, 8, 400, False, "zeros"),     # 1024 experts: count launch
     (1100, 64, 1024, 16, 1100, False, "normal"),  # the largest E and k together through the count launch
     (2000, 64, 1024, 16, 700, False, "ties"),     # and with ties and capacity overflow
-    (512, 64, 32, 16, 512, False, "normal"),      # 8192 ids: count launch
-    (257, 64, 16, 16, 257, False, "normal"),      # 4112 ids: count launch
+    (512, 64, 32, 16, 512, False, "normal"),      # 8192 ids: the most, 32 per thread
+    (257, 64, 16, 16, 257, False, "normal"),      # 4112 ids: 32 per thread
+    (520, 64, 32, 16, 520, False, "ties"),        # 8320 ids: count launch
+    (1024, 256, 256, 8, 1024, False, "ties"),     # 8192 ids and 8192 mask words together
+    (600, 7168, 256, 8, 600, True, "normal"),     # a mid-size batch of the DeepSeek-R1 shape, 4800 ids
     (480, 136, 20, 3, 37, False, "normal"),       # counted inside pack, with capacity overflow
     # more than 256 chunks: the chunk counts are scanned into prefixes first
     (66000, 64, 16, 4, 66000, False, "normal"),

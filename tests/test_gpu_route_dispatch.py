@@ -104,18 +104,18 @@ def test_every_k(dev, E, T):
 @pytest.mark.parametrize("T,E,k,fp8,C", [
     (1025, 9, 1, False, 1025),    # 16-lane groups, 9 of 16 lanes real; 65 halves (the last word's upper half cleared)
     (1031, 16, 2, True, 1031),    # 16-lane groups; 65 halves
-    (1007, 24, 5, False, 90),     # 32-lane groups; 63 halves; 5035 ids, too many to count inside pack; overflow
+    (1040, 24, 5, False, 90),     # 32-lane groups; 65 halves; capacity overflow
     (1040, 64, 8, False, 1040),   # one token per wave, one logit per lane; 65 halves
     (2049, 100, 6, True, 2049),   # one token per wave, two logits per lane; 129 halves
     (3000, 256, 8, False, 3000),  # one token per wave, four logits per lane
-    (700, 300, 10, False, 700),   # eight logits per lane, E not a multiple of them (scalar loads)
+    (1100, 300, 10, False, 1100), # eight logits per lane, E not a multiple of them (scalar loads); 69 halves
     (6145, 64, 2, False, 150),    # four tokens per wave (16-lane groups, four logits per lane); 385 halves; overflow
     (8192, 256, 8, True, 8192),   # the last size whose prefix stays within 32 loads per lane
     (8193, 256, 8, False, 8193),  # one token more: route, count and pack
 ])
 def test_router_words_for_more_than_8_experts(dev, T, E, k, fp8, C):
-    """E > 8 past the in-pack count (more than 1024 tokens, or more than 4096
-    ids): the router writes each expert's 32-token
+    """E > 8 past the in-pack count (more than 1024 tokens, more than 8192
+    ids, or more than 8192 mask words): the router writes each expert's 32-token
     membership words a 16-token half per work-group, in the plain router's
     lane layout for that E and T, and pack takes counts, prefixes and ranks
     from them.  Outputs must equal the oracle and the separate calls bit for
@@ -132,9 +132,9 @@ def test_router_words_for_more_than_8_experts(dev, T, E, k, fp8, C):
 def test_every_k_counted_in_pack_and_by_chunks(dev, T):
     """E > 8, every k from 1 to 16: the lanes owning one pair (64, 32, 16, 8
     or 4 of them) sum the pair's earlier counts together.  T = 200: the batch
-    is counted inside pack; T = 480: inside pack up to k = 8 (T*k <= 4096
-    ids); beyond, and at T = 3000, the separate call counts with its own
-    launch (256-token chunks) and the fused call from the router's words.  Odd k
+    is counted inside pack; T = 480: inside pack for every k (16 ids per
+    thread up to k = 8, 32 beyond); T = 3000: the separate call counts with
+    its own launch (256-token chunks), the fused call from the router's words.  Odd k
     overflow the capacity.  The packed layout is checked on the same
     inputs."""
     E, H = 24, 128
