@@ -19,15 +19,18 @@ constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141;  // lane i <- 7 - i within 8
 constexpr int kDppMirror = 0x140;      // lane i <- 15 - i within 16
 
+// Under these patterns every lane reads a lane of its own row, so the
+// bound_ctrl fill value (0) is never used; with it the compiler folds each
+// move into the max or add that follows (one DPP-modified instruction).
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp(uint32_t v)
 {
-    return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
 }
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v)
 {
-    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xF, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
 __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
