@@ -32,9 +32,11 @@
 // launch, and every pack work-group rebuilds the chunk's masks in LDS from
 // ids it requests before the rows.  Up to 1024 tokens whose ids fit 32 per
 // thread (and whose masks are at most 8192 words) are counted the same way.
-// Route + dispatch in one call with E <= 8: the router already wrote one
-// membership word per expert and 32-token chunk, and pack takes prefixes and
-// ranks from their popcounts (no count launch either).
+// Route + dispatch in one call: the router already wrote one membership
+// word per expert and 32-token chunk (for E > 8 as two 16-token halves, on
+// batches past the in-pack limits while each pair's prefix stays a bounded
+// number of word loads), and pack takes prefixes and ranks from their
+// popcounts (no count launch either).
 // Packed, count-sized layout (handbook "High-throughput mode": count first,
 // then a receive buffer of exactly the needed size): between count and
 // pack, one work-group sums each expert's chunk counts (or the popcounts of
