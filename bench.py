@@ -533,6 +533,70 @@ def run_workload(w: W.Workload, args, moe, torch, dev, primary: bool) -> dict:
     return res
 
 
+def placement_probe(w: W.Workload, n_recv: int, moe, torch, dev) -> dict:
+    """The same dispatch and combine calls on separately allocated buffers, in
+    one process: `n_recv` receive buffers (codes or rows, scales and the small
+    outputs, each its own allocation) and max(1, n_recv // 2) expert-output
+    buffers, each timed over two passes of 10 calls, beside a plain
+    sequential fill of the same buffer; then dispatch into the first receive
+    buffer viewed with other per-expert capacities (strides).  Inputs, ids and
+    weights are shared, so the buffers' memory is the only difference."""
+    logits = W.make_logits(w).to(dev)
+    x = W.make_x(w).to(dev)
+    idx, wt = moe.moe_route_topk(logits, w.k)
+    max_count = int(torch.bincount(idx.view(-1).long(), minlength=w.E).max())
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def per_call_us(fn, n=10):
+        fn()
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(n):
+            fn()
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) * 1e3 / n
+
+    def fill_tbps(t):
+        us = per_call_us(lambda: t.fill_(1), n=3)
+        return t.numel() * t.element_size() / (us * 1e-6) / 1e12
+
+    caps = sorted({w.C, w.C + 1, w.C + 16, w.C + 1024, -(-max_count // 256) * 256})
+    cmax = max(caps)
+    recv = []
+    for i in range(n_recv):
+        b = moe.DispatchBuffers.allocate(w.T, w.H, w.E, w.k, cmax if i == 0 else w.C, w.fp8, dev)
+        recv.append(b)
+
+    def dispatch_into(b, C):
+        rows = w.E * C
+        view = moe.DispatchBuffers(
+            recv_x=b.recv_x.view(-1)[:rows * w.H].view(w.E, C, w.H),
+            recv_scales=(b.recv_scales.view(-1)[:rows * (w.H // 128)].view(w.E, C, w.H // 128) if w.fp8 else None),
+            recv_src=b.recv_src.view(-1)[:rows].view(w.E, C), expert_counts=b.expert_counts,
+            token_slot=b.token_slot, workspace=b.workspace)
+        return lambda: moe.moe_route_dispatch(logits, x, w.k, C, fp8=w.fp8, bufs=view, topk_idx=idx, topk_w=wt)
+
+    res = {"workload": w.name, "call": "moe_route_dispatch", "max_expert_count": max_count, "receive_buffers": []}
+    for i, b in enumerate(recv):
+        C = w.C
+        res["receive_buffers"].append({
+            "capacity": C, "dispatch_us": [round(per_call_us(dispatch_into(b, C)), 1) for _ in range(2)],
+            "sequential_fill_tbps": round(fill_tbps(b.recv_x), 2)})
+    res["capacity_sweep_first_buffer_us"] = {str(C): round(per_call_us(dispatch_into(recv[0], C)), 1) for C in caps}
+    slots = recv[-1].token_slot
+    out = torch.empty(w.T, w.H, dtype=torch.bfloat16, device=dev)
+    res["expert_output_buffers"] = []
+    ys = []   # all kept alive, so that each is a fresh allocation
+    for _ in range(max(1, n_recv // 2)):
+        y = torch.empty(w.E, w.C, w.H, dtype=torch.bfloat16, device=dev)
+        ys.append(y)
+        res["expert_output_buffers"].append({
+            "combine_us": [round(per_call_us(lambda: moe.moe_combine(y, slots, wt, out=out)), 1) for _ in range(2)],
+            "sequential_fill_tbps": round(fill_tbps(y), 2)})
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -566,6 +630,10 @@ def main() -> int:
                     help="call moe_route_topk and moe_dispatch separately instead of moe_route_dispatch")
     ap.add_argument("--route-groups", default="",
                     help="G:M routes with moe_route_topk_grouped (G expert groups, the best M kept)")
+    ap.add_argument("--placement", type=int, default=0,
+                    help="instead of the benchmark: time dispatch and combine on this many separately allocated "
+                         "receive buffers (and half as many expert-output buffers) of the workload, plus a "
+                         "capacity sweep; prints one JSON object")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -586,6 +654,9 @@ def main() -> int:
     moe.load()
     dev = torch.device("cuda:0")
     w = W.WORKLOADS[args.workload]
+    if args.placement:
+        print(json.dumps({"placement": placement_probe(w, args.placement, moe, torch, dev)}), flush=True)
+        return 0
     epilogue = None if args.epilogue == "none" else args.epilogue
     if args.also == "auto":
         others = [n for n in SECONDARY if n != w.name] if w.name == DEFAULT_WORKLOAD else []
