@@ -247,6 +247,8 @@ def floor_lib():
     lib.floor_scatter_rows.restype = ctypes.c_int
     lib.floor_gather_rows.argtypes = [P, i64, i32, P, P, i64, i32, P, P]
     lib.floor_gather_rows.restype = ctypes.c_int
+    lib.floor_scatter_writes.argtypes = [i64, i32, i32, P, i32, P, P, P]
+    lib.floor_scatter_writes.restype = ctypes.c_int
     return lib
 
 
@@ -429,19 +431,21 @@ def run_workload(w: W.Workload, args, moe, torch, dev, primary: bool) -> dict:
         for e in trio:
             hip_events.destroy(e)
 
-    # copy floors: plain kernels moving pack's and combine's exact bytes
+    # copy floors: plain kernels moving pack's and combine's exact bytes, and
+    # pack's stores alone
     floor = None
     if not args.no_floor and not epilogue:
         lib = floor_lib()
-        fl_events = [tuple(hip_events.create() for _ in range(4)) for _ in range(n)]
+        fl_events = [tuple(hip_events.create() for _ in range(6)) for _ in range(n)]
         s0 = main.cuda_stream
 
-        def floor_pair(st, ev=None):
+        def floor_run(st, ev=None):
             bf = st.bufs
+            scales = bf.recv_scales.data_ptr() if w.fp8 else None
             if ev:
                 hip_events.record(ev[0], main)
             rc = lib.floor_scatter_rows(st.x.data_ptr(), w.T, w.H, int(w.fp8), bf.token_slot.data_ptr(), w.k,
-                                        bf.recv_x.data_ptr(), bf.recv_scales.data_ptr() if w.fp8 else None, s0)
+                                        bf.recv_x.data_ptr(), scales, s0)
             if ev:
                 hip_events.record(ev[1], main)
                 hip_events.record(ev[2], main)
@@ -449,27 +453,53 @@ def run_workload(w: W.Workload, args, moe, torch, dev, primary: bool) -> dict:
                                         st.wt.data_ptr(), w.T, w.k, st.out.data_ptr(), s0)
             if ev:
                 hip_events.record(ev[3], main)
+                hip_events.record(ev[4], main)
+            rc |= lib.floor_scatter_writes(w.T, w.H, int(w.fp8), bf.token_slot.data_ptr(), w.k,
+                                           bf.recv_x.data_ptr(), scales, s0)
+            if ev:
+                hip_events.record(ev[5], main)
             if rc:
                 raise RuntimeError(f"copy-floor launch failed ({rc})")
 
-        floor_pair(sets[0])          # untimed: the first launch also loads the kernels' code
+        floor_run(sets[0])           # untimed: the first launch also loads the kernels' code
         torch.cuda.synchronize()
         for i, ev in enumerate(fl_events):
-            floor_pair(sets[(Wm + K + n + i) % R], ev)
+            floor_run(sets[(Wm + K + n + i) % R], ev)
         torch.cuda.synchronize()
-        sc = _stats_us([hip_events.elapsed_ms(a, b) for a, b, _, _ in fl_events])
-        ga = _stats_us([hip_events.elapsed_ms(c, d) for _, _, c, d in fl_events])
-        for e4 in fl_events:
-            for e in e4:
+        sc = _stats_us([hip_events.elapsed_ms(e[0], e[1]) for e in fl_events])
+        ga = _stats_us([hip_events.elapsed_ms(e[2], e[3]) for e in fl_events])
+        wo = _stats_us([hip_events.elapsed_ms(e[4], e[5]) for e in fl_events])
+        for e6 in fl_events:
+            for e in e6:
                 hip_events.destroy(e)
+        # a plain sequential fill of one receive buffer: its bandwidth for
+        # writes that are not scattered
+        rx = sets[0].bufs.recv_x
+        fill_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        rx.fill_(0)
+        torch.cuda.synchronize()
+        fill_ev[0].record(main)
+        for _ in range(3):
+            rx.fill_(0)
+        fill_ev[1].record(main)
+        torch.cuda.synchronize()
+        fill_us = fill_ev[0].elapsed_time(fill_ev[1]) * 1e3 / 3
+        fill_bytes = rx.numel() * rx.element_size()
         pack_bytes = nbytes["pack"]
+        write_bytes = w.T * w.k * ((w.H + w.H // 32) if w.fp8 else 2 * w.H)
         floor = {
             "pack_shaped_copy": {"kernel": "floor_scatter_rows (bench_floor.hip)", "bytes": pack_bytes, **sc,
                                  "gbps": pack_bytes / (sc["mean_us"] * 1e-6) / 1e9},
             "combine_shaped_copy": {"kernel": "floor_gather_rows (bench_floor.hip)", "bytes": nbytes["combine"],
                                     **ga, "gbps": nbytes["combine"] / (ga["mean_us"] * 1e-6) / 1e9},
+            "pack_writes_only": {"kernel": "floor_scatter_writes (bench_floor.hip)", "bytes": write_bytes, **wo,
+                                 "gbps": write_bytes / (wo["mean_us"] * 1e-6) / 1e9},
+            "receive_buffer_fill": {"kernel": "torch fill_ of one receive buffer (sequential writes)",
+                                    "bytes": fill_bytes, "mean_us": fill_us,
+                                    "gbps": fill_bytes / (fill_us * 1e-6) / 1e9},
             "note": "plain copies of the same rows at the same addresses (no slot work, no quantisation, no "
-                    "arithmetic); their bytes are pack's and combine's algorithmic bytes",
+                    "arithmetic); their bytes are pack's and combine's algorithmic bytes. pack_writes_only: the "
+                    "copy's stores without its reads; receive_buffer_fill: the same memory written sequentially",
         }
         for v in floor.values():
             if isinstance(v, dict):

@@ -16,6 +16,10 @@
 //                       to a second array (fp8 codes + per-128 fp32 scales)
 //   floor_gather_rows   combine's pattern: each token's k rows (2H bytes
 //                       each) and k weights read, one row of 2H bytes written
+//   floor_scatter_writes  pack's stores alone: floor_scatter_rows with the
+//                       source reads left out (each vector written is made
+//                       from its token and position), to split pack's time
+//                       between its writes and the reads mixed into them
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -27,7 +31,7 @@ constexpr int kBlock = 256;
 constexpr int kWaves = kBlock / kWave;
 
 // bf16 rows: a lane copies VPL vectors of its segment to each slot.
-template <int VPL>
+template <int VPL, bool READ>
 __global__ __launch_bounds__(kBlock) void scatter_bf16(const u32x4 *__restrict__ src, int64_t T, int nvec,
                                                        const int32_t *__restrict__ slot, int k, int segs,
                                                        u32x4 *__restrict__ dst)
@@ -43,7 +47,10 @@ __global__ __launch_bounds__(kBlock) void scatter_bf16(const u32x4 *__restrict__
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
         const int v = v0 + i * kWave;
-        buf[i] = v < nvec ? src[t * nvec + v] : (u32x4){0, 0, 0, 0};
+        if (READ)
+            buf[i] = v < nvec ? src[t * nvec + v] : (u32x4){0, 0, 0, 0};
+        else
+            buf[i] = (u32x4){(uint32_t)t, (uint32_t)v, ~(uint32_t)t, ~(uint32_t)v};
     }
     int my = lane < k ? slot[t * k + lane] : -1;
     for (int j = 0; j < k; ++j) {
@@ -62,6 +69,7 @@ __global__ __launch_bounds__(kBlock) void scatter_bf16(const u32x4 *__restrict__
 // fp8 rows: a lane reads two 16-element groups (2 x 32 bytes) and writes
 // 16 bytes per group to each slot's code row; the first lane of every 8
 // groups (one 128-element block) also writes 4 bytes to the scale row.
+template <bool READ>
 __global__ __launch_bounds__(kBlock) void scatter_fp8(const u32x4 *__restrict__ src, int64_t T, int ngrp,
                                                       const int32_t *__restrict__ slot, int k, int segs,
                                                       u32x4 *__restrict__ codes, uint32_t *__restrict__ scales)
@@ -78,8 +86,13 @@ __global__ __launch_bounds__(kBlock) void scatter_fp8(const u32x4 *__restrict__ 
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
         const int g = g0 + i * kWave;
-        lo[i] = g < ngrp ? src[(t * ngrp + g) * 2] : (u32x4){0, 0, 0, 0};
-        hi[i] = g < ngrp ? src[(t * ngrp + g) * 2 + 1] : (u32x4){0, 0, 0, 0};
+        if (READ) {
+            lo[i] = g < ngrp ? src[(t * ngrp + g) * 2] : (u32x4){0, 0, 0, 0};
+            hi[i] = g < ngrp ? src[(t * ngrp + g) * 2 + 1] : (u32x4){0, 0, 0, 0};
+        } else {   // lo ^ hi = {t, g, ~t, ~g}; lo[0] = t
+            lo[i] = (u32x4){(uint32_t)t, 0u, 0u, 0u};
+            hi[i] = (u32x4){0u, (uint32_t)g, ~(uint32_t)t, ~(uint32_t)g};
+        }
     }
     int my = lane < k ? slot[t * k + lane] : -1;
     const int nblk = ngrp / 8;
@@ -162,6 +175,33 @@ hipError_t gather_k(const void *y, int64_t nrows, int nvec, const int32_t *slot,
     return hipGetLastError();
 }
 
+template <bool READ>
+int scatter(const void *x, int64_t T, int32_t H, int32_t fp8, const int32_t *token_slot, int32_t k, void *recv_x,
+            void *recv_scales, hipStream_t s)
+{
+    if (fp8) {
+        const int ngrp = H / 16;
+        const int segs = (ngrp + 2 * kWave - 1) / (2 * kWave);
+        hipLaunchKernelGGL(scatter_fp8<READ>, dim3((unsigned)blocks_for(T, segs)), dim3(kBlock), 0, s,
+                           (const u32x4 *)x, T, ngrp, token_slot, k, segs, (u32x4 *)recv_x, (uint32_t *)recv_scales);
+        return (int)hipGetLastError();
+    }
+    const int nvec = H / 8;
+    int vpl = k >= 8 ? 1 : 8 / k;
+    vpl = vpl >= 8 ? 8 : (vpl >= 4 ? 4 : (vpl >= 2 ? 2 : 1));
+    const int segs = (nvec + vpl * kWave - 1) / (vpl * kWave);
+    const dim3 grid((unsigned)blocks_for(T, segs));
+    const u32x4 *src = (const u32x4 *)x;
+    u32x4 *dst = (u32x4 *)recv_x;
+    switch (vpl) {
+    case 1: hipLaunchKernelGGL((scatter_bf16<1, READ>), grid, dim3(kBlock), 0, s, src, T, nvec, token_slot, k, segs, dst); break;
+    case 2: hipLaunchKernelGGL((scatter_bf16<2, READ>), grid, dim3(kBlock), 0, s, src, T, nvec, token_slot, k, segs, dst); break;
+    case 4: hipLaunchKernelGGL((scatter_bf16<4, READ>), grid, dim3(kBlock), 0, s, src, T, nvec, token_slot, k, segs, dst); break;
+    default: hipLaunchKernelGGL((scatter_bf16<8, READ>), grid, dim3(kBlock), 0, s, src, T, nvec, token_slot, k, segs, dst); break;
+    }
+    return (int)hipGetLastError();
+}
+
 }  // namespace
 
 extern "C" {
@@ -174,25 +214,18 @@ __attribute__((visibility("default"))) int floor_scatter_rows(const void *x, int
     if (T < 1 || k < 1 || k > 64 || H % (fp8 ? 128 : 8) != 0 || !x || !token_slot || !recv_x ||
         (fp8 && !recv_scales))
         return -1;
-    if (fp8) {
-        const int ngrp = H / 16;
-        const int segs = (ngrp + 2 * kWave - 1) / (2 * kWave);
-        hipLaunchKernelGGL(scatter_fp8, dim3((unsigned)blocks_for(T, segs)), dim3(kBlock), 0, s, (const u32x4 *)x, T,
-                           ngrp, token_slot, k, segs, (u32x4 *)recv_x, (uint32_t *)recv_scales);
-        return (int)hipGetLastError();
-    }
-    const int nvec = H / 8;
-    int vpl = k >= 8 ? 1 : 8 / k;
-    vpl = vpl >= 8 ? 8 : (vpl >= 4 ? 4 : (vpl >= 2 ? 2 : 1));
-    const int segs = (nvec + vpl * kWave - 1) / (vpl * kWave);
-    const dim3 grid((unsigned)blocks_for(T, segs));
-    switch (vpl) {
-    case 1: hipLaunchKernelGGL(scatter_bf16<1>, grid, dim3(kBlock), 0, s, (const u32x4 *)x, T, nvec, token_slot, k, segs, (u32x4 *)recv_x); break;
-    case 2: hipLaunchKernelGGL(scatter_bf16<2>, grid, dim3(kBlock), 0, s, (const u32x4 *)x, T, nvec, token_slot, k, segs, (u32x4 *)recv_x); break;
-    case 4: hipLaunchKernelGGL(scatter_bf16<4>, grid, dim3(kBlock), 0, s, (const u32x4 *)x, T, nvec, token_slot, k, segs, (u32x4 *)recv_x); break;
-    default: hipLaunchKernelGGL(scatter_bf16<8>, grid, dim3(kBlock), 0, s, (const u32x4 *)x, T, nvec, token_slot, k, segs, (u32x4 *)recv_x); break;
-    }
-    return (int)hipGetLastError();
+    return scatter<true>(x, T, H, fp8, token_slot, k, recv_x, recv_scales, s);
+}
+
+// floor_scatter_rows without the source: the same slots, launch shape and
+// stores, with no loads of x.
+__attribute__((visibility("default"))) int floor_scatter_writes(int64_t T, int32_t H, int32_t fp8,
+                                                                 const int32_t *token_slot, int32_t k, void *recv_x,
+                                                                 void *recv_scales, hipStream_t s)
+{
+    if (T < 1 || k < 1 || k > 64 || H % (fp8 ? 128 : 8) != 0 || !token_slot || !recv_x || (fp8 && !recv_scales))
+        return -1;
+    return scatter<false>(nullptr, T, H, fp8, token_slot, k, recv_x, recv_scales, s);
 }
 
 __attribute__((visibility("default"))) int floor_gather_rows(const void *y, int64_t nrows, int32_t H,

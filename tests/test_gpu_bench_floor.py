@@ -2,8 +2,9 @@
 compared against: floor_scatter_rows writes every filled slot's row (the
 whole bf16 row, or H code bytes plus one 4-byte word per 128 elements) and
 nothing else; floor_gather_rows reads each token's k slotted rows and writes
-one row per token.  Checked on small dispatches through the library, so the
-slot maps are the real ones."""
+one row per token; floor_scatter_writes stores what floor_scatter_rows stores,
+at the same slots, without reading the source.  Checked on small dispatches
+through the library, so the slot maps are the real ones."""
 import numpy as np
 import pytest
 import torch
@@ -75,3 +76,43 @@ def test_floor_kernels_touch_exactly_the_slotted_rows(dev, T, H, E, k, fp8):
         for j in range(k):
             want ^= yh[slots[t, j]]
         np.testing.assert_array_equal(oh[t], want)
+
+
+@pytest.mark.parametrize("T,H,E,k,fp8", [(300, 256, 16, 4, False), (300, 512, 16, 4, True), (1000, 1024, 8, 2, False),
+                                         (200, 384, 64, 8, True)])
+def test_floor_writes_touch_exactly_the_slotted_rows(dev, T, H, E, k, fp8):
+    """floor_scatter_writes stores every filled slot's whole row (and scale
+    words) with the copy's pattern made from (token, vector), and nothing
+    outside the slots."""
+    say(f"[floor writes] T={T} H={H} E={E} k={k} fp8={fp8}")
+    lib = bench.floor_lib()
+    g = torch.Generator(device="cpu")
+    g.manual_seed(T * 3 + H + E)
+    logits = torch.randn(T, E, generator=g).to(dev)
+    x = torch.randn(T, H, generator=g).to(torch.bfloat16).to(dev)
+    C = T
+    _, _, bufs = moe.moe_route_dispatch(logits, x, k, C, fp8=fp8)
+    slots = bufs.token_slot.cpu().numpy()
+    rows = torch.full((E * C, H * (1 if fp8 else 2)), SENT, dtype=torch.uint8, device=dev)
+    scales = torch.full((E * C, H // 128 * 4), SENT, dtype=torch.uint8, device=dev) if fp8 else None
+    rc = lib.floor_scatter_writes(T, H, int(fp8), bufs.token_slot.data_ptr(), k, rows.data_ptr(),
+                                  scales.data_ptr() if fp8 else None, torch.cuda.current_stream().cuda_stream)
+    assert rc == 0
+    torch.cuda.synchronize()
+    filled = np.zeros(E * C, bool)
+    filled[slots[slots >= 0]] = True
+    r = rows.cpu().numpy()
+    assert (r[~filled] == SENT).all(), "a row outside the slots was written"
+    nvec = r.shape[1] // 16
+    v = np.arange(nvec, dtype=np.uint32)
+    for t in range(T):
+        tt = np.full(nvec, t, np.uint32)
+        want = np.stack([tt, v, ~tt, ~v], axis=1).reshape(-1).view(np.uint8)
+        for j in range(k):
+            np.testing.assert_array_equal(r[slots[t, j]], want)
+    if fp8:
+        sc = scales.cpu().numpy().view(np.uint32)
+        assert (scales.cpu().numpy()[~filled] == SENT).all()
+        for t in range(T):
+            for j in range(k):
+                np.testing.assert_array_equal(sc[slots[t, j]], np.full(H // 128, t, np.uint32))
