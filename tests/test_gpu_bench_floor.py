@@ -116,3 +116,23 @@ def test_floor_writes_touch_exactly_the_slotted_rows(dev, T, H, E, k, fp8):
         for t in range(T):
             for j in range(k):
                 np.testing.assert_array_equal(sc[slots[t, j]], np.full(H // 128, t, np.uint32))
+
+
+def test_placement_probe_runs(dev):
+    """bench.py --placement times the same dispatch into separately allocated
+    buffers and prints one JSON object with every figure filled in."""
+    import json
+    import os
+    import subprocess
+    import sys
+    say("[placement probe] tiny, 2 buffers")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--workload", "tiny", "--placement", "2"],
+                       cwd=root, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    p = json.loads([ln for ln in r.stdout.splitlines() if ln.startswith("{")][-1])["placement"]
+    assert p["workload"] == "tiny" and len(p["receive_buffers"]) == 2 and len(p["expert_output_buffers"]) == 1
+    for b in p["receive_buffers"]:
+        assert len(b["dispatch_us"]) == 2 and min(b["dispatch_us"]) > 0 and b["sequential_fill_tbps"] > 0
+    assert all(v > 0 for v in p["capacity_sweep_first_buffer_us"].values())
+    assert min(p["expert_output_buffers"][0]["combine_us"]) > 0
