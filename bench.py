@@ -695,14 +695,20 @@ def main() -> int:
     else:
         others = [n for n in args.also.split(",") if n]
 
+    def summary(r):
+        line = f"# {r['workload']}: {r['ms_per_step'] * 1e3:.1f} us/step, {r['hbm_frac']:.3f} of 8 TB/s"
+        fl = r.get("floor") or {}
+        if "pack_writes_only" in fl:
+            line += (f"; pack's stores alone {fl['pack_writes_only']['gbps'] / 1e3:.2f} TB/s, receive buffer "
+                     f"sequential fill {fl['receive_buffer_fill']['gbps'] / 1e3:.2f} TB/s")
+        print(line, file=sys.stderr, flush=True)
+
     head = run_workload(w, args, moe, torch, dev, primary=True)
-    print(f"# {w.name}: {head['ms_per_step'] * 1e3:.1f} us/step, {head['hbm_frac']:.3f} of 8 TB/s",
-          file=sys.stderr, flush=True)
+    summary(head)
     other = []
     for name in others:
         r = run_workload(W.WORKLOADS[name], args, moe, torch, dev, primary=False)
-        print(f"# {name}: {r['ms_per_step'] * 1e3:.1f} us/step, {r['hbm_frac']:.3f} of 8 TB/s", file=sys.stderr,
-              flush=True)
+        summary(r)
         other.append(r)
 
     if args.copy_mib:
