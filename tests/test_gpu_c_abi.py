@@ -1,8 +1,10 @@
 """The C ABI on its own: tests/c_abi/c_abi_example.c (plain C99, linked
 against libmoe_route.so and the oracle's library, no Python or torch) runs
 route + dispatch in one call and combine with identity experts on a seeded
-batch, and checks ids, weights, counts, slots and the combined rows against
-the oracle.  It runs as a child process of the test."""
+batch, then the group-limited router, the separate dispatch with E4M3 rows
+and the packed dispatch on a second batch, and checks ids, weights, counts,
+slots, offsets, sources, codes, scales, packed rows and the combined rows
+against the oracle.  It runs as a child process of the test."""
 import os
 import subprocess
 
