@@ -1,10 +1,13 @@
 """The C ABI on its own: tests/c_abi/c_abi_example.c (plain C99, linked
 against libmoe_route.so and the oracle's library, no Python or torch) runs
 route + dispatch in one call and combine with identity experts on a seeded
-batch, then the group-limited router, the separate dispatch with E4M3 rows
-and the packed dispatch on a second batch, and checks ids, weights, counts,
-slots, offsets, sources, codes, scales, packed rows and the combined rows
-against the oracle.  It runs as a child process of the test."""
+batch; the group-limited router, the separate dispatch with E4M3 rows and
+the packed dispatch on a second batch; and the plain router, the one-call
+packed and no-alloc dispatches and the fused residual + RMSNorm epilogue
+(bf16 and E4M3 output) on a third.  Every entry point of the library runs.
+It checks ids, weights, counts, slots, offsets, sources, codes, scales,
+rows, the updated residual and the normalised rows against the oracle.  It
+runs as a child process of the test."""
 import os
 import subprocess
 
