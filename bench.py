@@ -661,9 +661,9 @@ def main() -> int:
     ap.add_argument("--route-groups", default="",
                     help="G:M routes with moe_route_topk_grouped (G expert groups, the best M kept)")
     ap.add_argument("--placement", type=int, default=0,
-                    help="instead of the benchmark: time dispatch and combine on this many separately allocated "
-                         "receive buffers (and half as many expert-output buffers) of the workload, plus a "
-                         "capacity sweep; prints one JSON object")
+                    help="instead of the benchmark: time moe_route_dispatch and moe_combine (fixed-slot layout) "
+                         "on this many separately allocated receive buffers (and half as many expert-output "
+                         "buffers) of the workload, plus a capacity sweep; prints one JSON object")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
